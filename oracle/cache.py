@@ -1,0 +1,235 @@
+"""Oracle cache state machine: explicit concatenation, physical left-shift eviction.
+
+Logical order is: sink entries (oldest first), then the rolling window (oldest
+first, newest chunk last).  Every entry keeps its stored key (what the cache
+holds: the rotated key, bf16-rounded for bf16 caches), its value, its time
+index t, its global token index g, its raw key (for the fp64 semantic
+reference) and its token-in-frame index (for h/w positions).
+
+Sources:
+  * capacity fixed at creation: kv_size = frame_seqlen * local_attn_size
+    (LingBot-World 2.0 article, "chunked inference"); memory precomputed by
+    cache_max_len() (rCM length-extrapolation article, intro).
+  * roll rule (LingBot article, "how the window rolls when full"): when
+    new + local_end > kv_size, num_evicted = new + local_end - kv_size; the
+    contents after the sink are shifted left by num_evicted, the sink never
+    moves, the roped K/V of the new block are written at the tail.  The '+'
+    and '>' lost in the page's extraction are restored; the page's own worked
+    numbers (a 4680-token block evicts an equal 4680 from a full 28080 cache)
+    fix that reading.
+  * the sink is the first sink_size frames of the stream (LingBot article,
+    "sink_size attention sink").
+  * the newest block may be written again in place by later denoising steps
+    before the clean commit; rolling only happens for genuinely new content
+    (LingBot article, roll condition; Causal-Forcing article, section 4).
+  * in-place time re-rotation of cached keys (rCM article, Deep Forcing:
+    rope_time_delta_), clamping negative time indices to 0 (rCM article,
+    Infinity-RoPE item 2), KV flush keeping sink + last block (item 3).
+  * Rolling Sink bank of the first K blocks and the sink refilled from it
+    (rCM article, strategy 2; Rolling Sink summary, "method step details").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bf16 import round_to_bf16
+from .rope import band_split, rotate_f32, token_positions
+from .attention import attention_f32, attention_f64
+from .score import attention_mass_scores
+
+
+class OracleError(ValueError):
+    pass
+
+
+class OracleCache:
+    def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
+                 dtype="bf16", bank_frames=0):
+        self.S = frame_seqlen
+        self.H = heads
+        self.D = head_dim
+        self.grid_w = grid_w
+        self.dtype = dtype
+        self.S_tok = sink_frames * frame_seqlen
+        self.W_tok = window_frames * frame_seqlen
+        self.C_tok = self.S_tok + self.W_tok
+        self.bank_tok = bank_frames * frame_seqlen
+        e = np.zeros((0, heads, head_dim), np.float32)
+        self.K, self.V, self.Kraw = e.copy(), e.copy(), e.copy()
+        self.t = np.zeros(0, np.int64)
+        self.g = np.zeros(0, np.int64)
+        self.tok = np.zeros(0, np.int64)          # token index inside its frame
+        self.n_sink = 0
+        self.global_end = 0
+        self.newest = None                        # (g0, n_tokens, frames)
+        self.bank_K = np.zeros((self.bank_tok, heads, head_dim), np.float32)
+        self.bank_V = np.zeros((self.bank_tok, heads, head_dim), np.float32)
+
+    # ------------------------------------------------------------------ helpers
+    @property
+    def n(self) -> int:
+        return int(self.t.shape[0])
+
+    def _store(self, x):
+        return round_to_bf16(x) if self.dtype == "bf16" else np.asarray(x, np.float32)
+
+    def _rotate(self, x, t, tok, bands=(True, True, True)):
+        h = tok // self.grid_w
+        w = tok % self.grid_w
+        return self._store(rotate_f32(x, t, h, w, bands))
+
+    def _take(self, idx):
+        idx = np.asarray(idx, dtype=np.int64)
+        for name in ("K", "V", "Kraw", "t", "g", "tok"):
+            setattr(self, name, getattr(self, name)[idx])
+
+    def _cat(self, parts):
+        for name in ("K", "V", "Kraw", "t", "g", "tok"):
+            setattr(self, name, np.concatenate([p[name] for p in parts], axis=0))
+
+    def _entries(self, lo, hi):
+        return {n: getattr(self, n)[lo:hi] for n in ("K", "V", "Kraw", "t", "g", "tok")}
+
+    # ------------------------------------------------------------------ append
+    def append(self, k, v, frames, t0, replace_newest=False):
+        """Write `frames` new frames at times t0 .. t0+frames-1 (rotating k), FIFO-evicting if full."""
+        N = frames * self.S
+        k = np.asarray(k, np.float32)
+        v = np.asarray(v, np.float32)
+        if k.shape != (N, self.H, self.D) or v.shape != k.shape:
+            raise OracleError("k/v shape")
+        if N > self.W_tok:
+            raise OracleError("chunk larger than the rolling window")
+        t, _, _ = token_positions(N, self.S, self.grid_w, t0)
+        tok = np.arange(N, dtype=np.int64) % self.S
+        Kst = self._rotate(k, t, tok)
+        if replace_newest:
+            if self.newest is None or self.newest[2] != frames:
+                raise OracleError("no newest chunk of that size to replace")
+            g0 = self.newest[0]
+            idx = np.nonzero((self.g >= g0) & (self.g < g0 + N))[0]
+            if idx.shape[0] != N:
+                raise OracleError("newest chunk no longer whole")
+            order = np.argsort(self.g[idx], kind="stable")
+            idx = idx[order]
+            self.K[idx], self.V[idx], self.Kraw[idx], self.t[idx] = Kst, v, k, t
+            self._capture_bank(g0, k, v)
+            return
+        g0 = self.global_end
+        new = {"K": Kst, "V": v.copy(), "Kraw": k.copy(), "t": t, "g": g0 + np.arange(N, dtype=np.int64),
+               "tok": tok}
+        self._cat([self._entries(0, self.n), new])
+        self.n_sink = min(self.S_tok, self.n_sink + N)
+        if self.n > self.C_tok:
+            n_evict = self.n - self.C_tok
+            # physical left shift of everything after the sink: window = window[n_evict:]
+            sink = self._entries(0, self.S_tok)
+            window = self._entries(self.S_tok + n_evict, self.n)
+            self._cat([sink, window])
+        self.newest = (g0, N, frames)
+        self.global_end += N
+        self._capture_bank(g0, k, v)
+
+    def _capture_bank(self, g0, k, v):
+        if self.bank_tok == 0 or g0 >= self.bank_tok:
+            return
+        m = min(self.bank_tok - g0, k.shape[0])
+        self.bank_K[g0:g0 + m] = k[:m]
+        self.bank_V[g0:g0 + m] = v[:m]
+
+    # ------------------------------------------------------------------ retime
+    def retime(self, delta, clamp0, lo=0, hi=None):
+        """Shift times of logical entries [lo, hi) by delta (clamped at 0 if clamp0), re-rotating in place.
+
+        Storage model: the time band of the *stored* key is rotated by the
+        actual change t' - t and rounded again; the other bands are untouched.
+        """
+        hi = self.n if hi is None else hi
+        if not (0 <= lo <= hi <= self.n):
+            raise OracleError("retime range")
+        if hi == lo:
+            return
+        t_old = self.t[lo:hi]
+        t_new = np.maximum(0, t_old + delta) if clamp0 else t_old + delta
+        dlt = t_new - t_old
+        blk = self.K[lo:hi]
+        rot = rotate_f32(blk, dlt, np.zeros_like(dlt), np.zeros_like(dlt), bands=(True, False, False))
+        (ts, tw) = band_split(self.D)[0]
+        out = blk.copy()
+        out[:, :, ts:ts + tw] = self._store(rot[:, :, ts:ts + tw])
+        self.K[lo:hi] = out
+        self.t[lo:hi] = t_new
+
+    # ------------------------------------------------------------------ compact
+    def compact(self, keep_idx):
+        """Keep exactly the logical entries keep_idx (sorted, unique, containing the whole sink)."""
+        keep = np.asarray(keep_idx, dtype=np.int64)
+        if keep.ndim != 1 or keep.shape[0] == 0:
+            raise OracleError("keep_idx empty")
+        if np.any(np.diff(keep) <= 0):
+            raise OracleError("keep_idx not sorted unique")
+        if keep[0] < 0 or keep[-1] >= self.n:
+            raise OracleError("keep_idx out of range")
+        if keep.shape[0] < self.n_sink or np.any(keep[:self.n_sink] != np.arange(self.n_sink)):
+            raise OracleError("keep_idx drops a sink entry")
+        if self.newest is not None:
+            g0, N, _ = self.newest
+            kept_g = self.g[keep]
+            if np.count_nonzero((kept_g >= g0) & (kept_g < g0 + N)) != N:
+                self.newest = None
+        self._take(keep)
+
+    # ------------------------------------------------------------------ sink push
+    def sink_push(self, bank_frame, frames, t0):
+        """Rolling-Sink sink FIFO step: drop the oldest `frames` sink frames, append bank frames
+        [bank_frame, bank_frame+frames) freshly rotated at times t0 .. t0+frames-1."""
+        N = frames * self.S
+        if self.bank_tok == 0 or self.global_end < self.bank_tok:
+            raise OracleError("bank incomplete")
+        if self.n_sink != self.S_tok or N > self.S_tok:
+            raise OracleError("sink not full / block too large")
+        b0 = bank_frame * self.S
+        if b0 < 0 or b0 + N > self.bank_tok:
+            raise OracleError("bank range")
+        raw = self.bank_K[b0:b0 + N]
+        t, _, _ = token_positions(N, self.S, self.grid_w, t0)
+        tok = (b0 + np.arange(N, dtype=np.int64)) % self.S
+        new = {"K": self._rotate(raw, t, tok), "V": self.bank_V[b0:b0 + N].copy(), "Kraw": raw.copy(),
+               "t": t, "g": b0 + np.arange(N, dtype=np.int64), "tok": tok}
+        self._cat([self._entries(N, self.S_tok), new, self._entries(self.S_tok, self.n)])
+
+    # ------------------------------------------------------------------ queries
+    def rotate_queries(self, q, frames, t0):
+        N = frames * self.S
+        q = np.asarray(q, np.float32)
+        if q.shape != (N, self.H, self.D):
+            raise OracleError("q shape")
+        t, _, _ = token_positions(N, self.S, self.grid_w, t0)
+        tok = np.arange(N, dtype=np.int64) % self.S
+        return self._rotate(q, t, tok)
+
+    def newest_time(self):
+        g0 = self.newest[0]
+        return int(self.t[np.nonzero(self.g == g0)[0][0]])
+
+    def attend(self, q, frames, t0=None, rows=None, f64=False):
+        """softmax(q_hat K^T / sqrt(D)) V over every valid entry, no mask; q rotated at t0."""
+        t0 = self.newest_time() if t0 is None else t0
+        qh = self.rotate_queries(q, frames, t0)
+        if rows is not None:
+            qh = qh[np.asarray(rows)]
+        if f64:
+            return attention_f64(qh, self.K, self.V)
+        return attention_f32(qh, self.K, self.V)
+
+    def score(self, q_win, frames, t_frames, f64=False):
+        """Per-entry attention mass of the query window, summed over heads and query rows."""
+        N = frames * self.S
+        t = np.repeat(np.asarray(t_frames, np.int64), self.S)
+        tok = np.arange(N, dtype=np.int64) % self.S
+        qh = self._rotate(np.asarray(q_win, np.float32), t, tok)
+        return attention_mass_scores(qh, self.K, np.float64 if f64 else np.float32)
+
+    def state(self):
+        return {"K": self.K, "V": self.V, "t": self.t, "g": self.g, "n_sink": self.n_sink,
+                "global_end": self.global_end}
