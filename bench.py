@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the bounded video KV cache hot path on one MI355X.
+
+A step is one steady-state chunk of the 14B-shaped sliding-window workload
+(40 heads x 128, 1560-token frames, 6 sink + 12 rolling frames = 28080-token
+cache, 3-frame chunks): kvc_append (fused 3D RoPE + ring write, evicting 4680
+tokens) followed by kvc_attend (4680 queries over all 28080 cached keys).
+Inputs are seeded synthetic N(0,1) bf16 chunks, resident in HBM before timing.
+
+Prints one JSON line.  `value` is attention TFLOP/s over the whole step
+(algorithmic 4*H*Lq*Lk*D flop per chunk / step wall time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_attend_c3.json"))
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard across GPUs "
+              "with no exchange on the attention path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import WORKLOADS, chunk_inputs
+
+    w = WORKLOADS["c3"]
+    S, H, D = w.frame_seqlen, w.heads, w.head_dim
+    F = 3
+    N = F * S
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs: a pool of chunks resident in HBM
+    pool = []
+    for c in range(4):
+        q, k, v = chunk_inputs(w, c)
+        pool.append(tuple(torch.from_numpy(x).to(dev, torch.bfloat16) for x in (q, k, v)))
+    cache = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16)
+    out = torch.empty_like(pool[0][0])
+
+    # fill the cache to capacity (6 chunks = 28080 tokens)
+    t_frame = 0
+    for c in range(6):
+        q, k, v = pool[c % 4]
+        cache.append(k, v, t_frame)
+        t_frame += F
+    torch.cuda.synchronize()
+    Lk = cache.info()["n_valid"]
+    assert Lk == w.capacity == 28080
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    flop = 4.0 * H * N * Lk * D
+
+    def step(i, rec=None):
+        nonlocal t_frame
+        q, k, v = pool[i % 4]
+        if rec:
+            rec[0].record(stream)
+        cache.append(k, v, t_frame)
+        if rec:
+            rec[1].record(stream)
+        cache.attend(q, t_frame, out=out)
+        if rec:
+            rec[2].record(stream)
+        t_frame += F
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    recs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, recs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    app_ms = [a.elapsed_time(b) for a, b, _ in recs]
+    att_ms = [b.elapsed_time(c) for _, b, c in recs]
+    att_avg = float(np.mean(att_ms))
+    app_avg = float(np.mean(app_ms))
+    assert cache.info()["n_valid"] == 28080
+
+    # ---- retime over the whole cache (time band only), MALL flushed between samples
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ret_ms = []
+    for i in range(12):
+        flush.fill_(i & 0xFF)
+        a, b = ev(), ev()
+        a.record(stream)
+        cache.retime(1 if i % 2 == 0 else -1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ret_ms.append(a.elapsed_time(b))
+    ret_avg = float(np.mean(ret_ms))
+    # append with the MALL flushed as well (the step loop above runs warm)
+    app_cold = []
+    for i in range(8):
+        flush.fill_(i & 0xFF)
+        a, b = ev(), ev()
+        q, k, v = pool[i % 4]
+        a.record(stream)
+        cache.append(k, v, t_frame)
+        b.record(stream)
+        t_frame += F
+        torch.cuda.synchronize()
+        if i >= 2:
+            app_cold.append(a.elapsed_time(b))
+    del flush
+
+    dt = D - 4 * (D // 6)
+    app_bytes = 4.0 * N * H * D * 2
+    ret_bytes = 4.0 * Lk * H * dt * 2
+    att_tflops = flop / (att_avg * 1e-3) / 1e12
+    value = flop / (ms_step * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "kvc_attend TFLOP/s (% bf16 MFMA peak) + ms per 3-frame chunk at 28080-token cache",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c3 14B-shaped sliding window + sink: 40 heads x 128, 1560-token frames (30x52), "
+                               "3-frame chunks (4680 queries), 6 sink + 12 rolling frames = 28080-token cache",
+                   "heads": H, "head_dim": D, "cache_tokens": Lk, "chunk_tokens": N, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "kernels": {
+            "attend_ms": round(att_avg, 4),
+            "attend_tflops": round(att_tflops, 2),
+            "append_us_warm": round(app_avg * 1e3, 2),
+            "append_GBps_warm": round(app_bytes / (app_avg * 1e-3) / 1e9, 1),
+            "append_us_cold": round(float(np.mean(app_cold)) * 1e3, 2),
+            "append_GBps_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9, 1),
+            "retime_us_cold": round(ret_avg * 1e3, 2),
+            "retime_GBps_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9, 1),
+            "append_hbm_frac_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "retime_hbm_frac_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_rows, w, cache)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(rows, w, cache):
+    """The oracle, untuned, on this host: fp32 BLAS attention of `rows` query rows (all heads) over a full
+    28080-entry cache, as TFLOP/s; the cache contents are the GPU cache's own export."""
+    import numpy as np
+    import torch
+    from oracle import attention_f32, OracleCache
+    from workloads import chunk_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    st = cache.export()
+    K = st["K"].float().cpu().numpy()
+    V = st["V"].float().cpu().numpy()
+    q, _, _ = chunk_inputs(w, 0)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, "bf16")
+    t0 = time.perf_counter()
+    qh = oc.rotate_queries(q, 3, 0)[:rows]
+    attention_f32(qh, K, V)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * w.heads * rows * K.shape[0] * w.head_dim
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} query rows x {w.heads} heads over {K.shape[0]} keys (one 3-frame chunk's queries, "
+                      f"incl. their RoPE), fp32 numpy BLAS; {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * kvc.h -- C ABI of libkvc: a bounded, ring-indexed KV cache for chunk-wise
+ * causal video attention on AMD Instinct MI355X (gfx950).
+ *
+ * What the cache is (sources, by page and section):
+ *  - A per-layer cache of fixed capacity allocated up front: kv_size =
+ *    frame_seqlen * local_attn_size (LingBot-World 2.0 sliding-window
+ *    article, "chunked inference"); memory precomputed once (rCM
+ *    length-extrapolation article, introduction: cache_max_len()).
+ *  - The first sink_size frames are pinned; later frames roll FIFO through
+ *    the remaining window; when new + local_end > kv_size the oldest
+ *    non-sink tokens are evicted (LingBot article, "how the window rolls when
+ *    full" and "sink_size attention sink").  Here eviction is a ring-head
+ *    advance: no cached byte moves.
+ *  - New keys are rotated at their absolute frame number (LingBot article,
+ *    "two easily missed details"; Causal-Forcing article, section 3).
+ *  - Only the current chunk's queries are computed; they attend to the cached
+ *    history plus the new chunk (Causal-Forcing article, section 3).
+ *  - Cached keys can be re-timed in place (rCM article, strategy 4:
+ *    rope_time_delta_; strategy 3: shift, clamp to 0, RoPE cut), compacted to
+ *    a kept subset (strategy 3 KV flush, strategy 4 KVCache.compact_), scored
+ *    by received attention (strategy 4), and the sink refilled from a bank
+ *    of the first blocks (strategy 2; Rolling Sink summary, "method step
+ *    details").
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device (or managed) addresses; host pointers are
+ *    ordinary CPU memory.  Each parameter says which.
+ *  - Tensors are dense row-major.  q, k, v and out are [tokens, heads,
+ *    head_dim]; tokens are frame-major, each frame row-major over its
+ *    (grid_h x grid_w) latent grid.
+ *  - Element type is the cache dtype (KVC_BF16: bfloat16, KVC_F32: float).
+ *  - All GPU work is enqueued on the handle's stream, asynchronously, unless
+ *    stated otherwise.  Inputs must stay valid until that work completes.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    on any error except KVC_EDEVICE the cache state is unchanged.
+ *    KVC_EDEVICE (a HIP launch/copy failure) poisons the handle: every later
+ *    call returns KVC_ESTATE until kvc_destroy.
+ *  - kvc_last_error() returns a thread-local description of the last error.
+ *  - A handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvc_cache* kvc_handle;
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_EINVAL = 1,        /* bad argument; state unchanged                      */
+  KVC_ENOMEM = 2,        /* workspace too small / host allocation failed       */
+  KVC_ESTATE = 3,        /* call not valid in the current state, or poisoned   */
+  KVC_EDEVICE = 4,       /* HIP runtime error; the handle is poisoned          */
+  KVC_EUNSUPPORTED = 5   /* feature not reserved at creation                   */
+} kvc_status;
+
+typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
+
+/* kvc_attend: rotate q at the newest chunk's current time index. */
+#define KVC_T_NEWEST INT32_MIN
+/* kvc_append: re-write the newest chunk's slots in place (a denoising step
+ * before the clean commit); nothing is evicted and global indices are kept. */
+#define KVC_APPEND_REPLACE_NEWEST 1u
+/* kvc_create: reserve the second window buffer that kvc_compact gathers into. */
+#define KVC_CREATE_COMPACT 1u
+/* Largest |time index| and |retime delta| (the RoPE time table covers
+ * positions -KVC_MAX_POS .. KVC_MAX_POS). */
+#define KVC_MAX_POS 16383
+/* Largest number of query frames per kvc_attend / kvc_score call. */
+#define KVC_MAX_Q_FRAMES 32
+
+typedef struct {
+  int32_t capacity;        /* (sink_frames + window_frames) * frame_seqlen        */
+  int32_t n_valid;         /* valid entries = sink_filled + window_filled          */
+  int32_t sink_tokens;     /* sink capacity in tokens                              */
+  int32_t window_tokens;   /* rolling window capacity in tokens                    */
+  int32_t sink_filled;
+  int32_t window_filled;
+  int32_t sink_head;       /* physical slot of the oldest sink entry               */
+  int32_t window_head;     /* physical slot of the oldest window entry             */
+  int64_t global_end;      /* tokens appended so far (not counting re-writes)      */
+  int32_t newest_valid;    /* 1 if the newest chunk is still whole in the cache    */
+  int32_t newest_frames;
+  int32_t newest_t;        /* current time index of the newest chunk's first frame */
+  int32_t bank_tokens;     /* raw-key bank capacity (Rolling Sink), 0 if none      */
+  int64_t newest_g;        /* global index of the newest chunk's first token       */
+  int32_t bank_complete;   /* 1 once global_end >= bank_tokens                     */
+  int32_t window_buffer;   /* which of the two window buffers is current (0/1)     */
+} kvc_info_t;
+
+/* Device bytes the caller must provide to kvc_create for this geometry
+ * (includes K/V planes, time/global-index arrays, RoPE tables, the optional
+ * raw-key bank and, with KVC_CREATE_COMPACT, the second window buffer).
+ * Returns 0 for an unsupported geometry (head_dim not 64/128, bad sizes). */
+size_t kvc_workspace_bytes(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,
+                           int32_t heads, int32_t head_dim, kvc_dtype dt, int32_t bank_frames,
+                           uint32_t create_flags);
+
+/* Create a cache over caller-owned device memory `workspace` (>= the size
+ * above, 256-byte aligned).  grid_w is the latent grid width (frame_seqlen
+ * must be a multiple of it).  The library builds the RoPE tables on the host
+ * (fp64 -> fp32), zero-fills the workspace and uploads the tables on
+ * `hip_stream` (hipStream_t, may be NULL for the default stream), then
+ * synchronizes that stream once.  The library never allocates device memory;
+ * it must not outlive `workspace`.  *out receives the handle. */
+kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,
+                      int32_t heads, int32_t head_dim, int32_t grid_w, kvc_dtype dt,
+                      int32_t bank_frames, uint32_t create_flags, void* workspace, size_t ws_bytes,
+                      void* hip_stream, kvc_handle* out);
+
+/* Free host state; the workspace stays the caller's. */
+kvc_status kvc_destroy(kvc_handle h);
+
+/* Change the stream later calls enqueue on. */
+kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
+
+/* Append n_frames new frames at time indices t_index .. t_index+n_frames-1.
+ * k, v: device, [n_frames*frame_seqlen, heads, head_dim] raw (un-rotated) keys
+ * and values.  Keys are rotated with the 3D RoPE (time band at the absolute
+ * frame, height/width bands at the token's grid position) and stored in the
+ * cache dtype (bf16 round-to-nearest-even).  The first sink tokens ever
+ * appended fill the sink; the rest go to the window, evicting the oldest
+ * window tokens when full (ring-head advance).  While global_end <
+ * bank_tokens, raw k/v are also captured into the bank.
+ * flags: KVC_APPEND_REPLACE_NEWEST re-writes the newest chunk in place (its
+ * frame count must match).  EINVAL if n_frames*frame_seqlen exceeds the
+ * window, or |t_index|+n_frames exceeds KVC_MAX_POS. */
+kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_frames, int32_t t_index,
+                      uint32_t flags);
+
+/* out = softmax(q_hat K^T / sqrt(head_dim)) V over every valid entry (sink,
+ * window and the newest chunk), with no mask.  q: device, [q_frames *
+ * frame_seqlen, heads, head_dim] raw queries, rotated here at time q_t_index
+ * + frame (KVC_T_NEWEST: the newest chunk's current time) and rounded to the
+ * cache dtype.  out: device, same shape and dtype.  ESTATE if the cache is
+ * empty. */
+kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out);
+
+/* Shift the time index of logical entries [slot_lo, slot_hi) by delta
+ * (clamped at 0 when clamp0 != 0) and re-rotate their stored keys' time band
+ * in place by the actual change.  Logical order: sink oldest..newest, then
+ * window oldest..newest.  EINVAL if the range is outside [0, n_valid) or a
+ * resulting |time| exceeds KVC_MAX_POS. */
+kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi);
+
+/* Device scratch bytes kvc_score needs for q_frames query frames. */
+size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);
+
+/* Attention mass received by each valid entry from a window of queries,
+ * summed over heads and query rows: scores[j] = sum_h sum_i softmax_j(q_hat_i
+ * . k_j / sqrt(head_dim)).  q_win: device [q_frames*frame_seqlen, heads,
+ * head_dim] raw queries; q_t: host int32[q_frames], the time index of each
+ * query frame (copied before return); scores: device float[n_valid] in
+ * logical order; scratch: device, >= kvc_score_scratch_bytes. */
+kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
+                     void* scratch, size_t scratch_bytes);
+
+/* Keep exactly the logical entries keep_idx[0..n_keep) (host int32, sorted,
+ * unique, in [0, n_valid), containing every sink entry), packed in that
+ * order; window entries are gathered into the other window buffer.  Requires
+ * KVC_CREATE_COMPACT (else EUNSUPPORTED).  The newest chunk stays
+ * addressable for REPLACE_NEWEST only if all of it is kept. */
+kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep);
+
+/* Rolling-Sink sink step: drop the oldest n_frames sink frames and append
+ * bank frames [bank_frame, bank_frame+n_frames) (raw keys captured during the
+ * first appends), rotated afresh at times t_index .. t_index+n_frames-1.
+ * ESTATE unless the bank is complete and the sink full. */
+kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int32_t t_index);
+
+/* Counters (host-side, no synchronization). */
+kvc_status kvc_info(kvc_handle h, kvc_info_t* out);
+
+/* Host mirror of each valid entry's time and global index, logical order
+ * (host arrays of n_valid elements; either may be NULL).  No synchronization. */
+kvc_status kvc_slot_times(kvc_handle h, int32_t* t, int64_t* g);
+
+/* Gather the valid entries in logical order: k, v device [n_valid, heads,
+ * head_dim] (stored, i.e. rotated, keys), t device int32[n_valid], g device
+ * int64[n_valid].  Synchronizes the stream before returning. */
+kvc_status kvc_export(kvc_handle h, void* k, void* v, int32_t* t, int64_t* g);
+
+/* Copy RoPE table rows to the host: band 0 = time (positions may be
+ * negative), 1 = height, 2 = width; positions [pos_lo, pos_lo + n_pos);
+ * out: host float[n_pos][band_width/2][2] as (cos, sin).  Synchronizes. */
+kvc_status kvc_export_tables(kvc_handle h, int32_t band, int32_t pos_lo, int32_t n_pos, float* out);
+
+/* Thread-local message for the last failing call on this thread. */
+const char* kvc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

@@ -156,5 +156,6 @@ class DeepForcingRun:
 
 
 def make_run(w):
-    return {"tiny": SlidingWindowRun, "c2": SlidingWindowRun, "c3": SlidingWindowRun,
-            "c4": RollingSinkRun, "c5a": InfinityRopeRun, "c5b": DeepForcingRun}[w.name.split("_")[0]](w)
+    """Run of a workload by name prefix; anything else is a plain sliding window / global cache."""
+    return {"c4": RollingSinkRun, "c5a": InfinityRopeRun, "c5b": DeepForcingRun}.get(
+        w.name.split("_")[0], SlidingWindowRun)(w)

@@ -1,0 +1,90 @@
+// kvc_common.hip.hpp -- device helpers shared by the HIP kernels of libkvc.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvc_device.hpp"
+
+namespace kvc {
+
+// bfloat16 <-> float.  Storage rounding is round-to-nearest-even written out
+// on the bit pattern so the cache contents do not depend on a conversion
+// instruction's denormal mode.
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {
+  static constexpr int E = 8;   // elements per 16 bytes
+  __device__ __forceinline__ static float ld(uint16_t x) { return bf2f(x); }
+  __device__ __forceinline__ static uint16_t st(float f) { return f2bf_rne(f); }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int E = 4;
+  __device__ __forceinline__ static float ld(float x) { return x; }
+  __device__ __forceinline__ static float st(float f) { return f; }
+};
+
+template <typename T>
+union Vec16 {
+  uint4 u;
+  T e[16 / sizeof(T)];
+};
+
+// One RoPE pair rotation with every product and sum rounded to fp32 (no fused
+// multiply-add):  x' = (x*c) - (y*s),  y' = (x*s) + (y*c).
+__device__ __forceinline__ void rot_pair(float& x, float& y, float c, float s) {
+#pragma clang fp contract(off)
+  const float xc = x * c;
+  const float ys = y * s;
+  const float xs = x * s;
+  const float yc = y * c;
+  x = xc - ys;
+  y = xs + yc;
+}
+
+// (cos, sin) of the pair that starts at head dim d (even), for a token at
+// time t and grid position (hp, wp).  Bands: [0, dt) time, [dt, dt+bw)
+// height, [dt+bw, D) width; pair index restarts at 0 in each band.
+__device__ __forceinline__ void pair_cs(const Geo& g, const Tables& tb, int d, int t, int hp, int wp, float& c,
+                                        float& s) {
+  const float* p;
+  if (d < g.dt)
+    p = tb.tcs + ((size_t)(t + tb.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
+  else if (d < g.dt + g.bw)
+    p = tb.hcs + ((size_t)hp * (g.bw >> 1) + ((d - g.dt) >> 1)) * 2;
+  else
+    p = tb.wcs + ((size_t)wp * (g.bw >> 1) + ((d - g.dt - g.bw) >> 1)) * 2;
+  c = p[0];
+  s = p[1];
+}
+
+// Rotate E consecutive elements (E/2 pairs) starting at head dim d0.
+template <int E>
+__device__ __forceinline__ void rotate_run(float* x, const Geo& g, const Tables& tb, int d0, int t, int hp, int wp) {
+#pragma unroll
+  for (int p = 0; p < E / 2; ++p) {
+    float c, s;
+    pair_cs(g, tb, d0 + 2 * p, t, hp, wp, c, s);
+    rot_pair(x[2 * p], x[2 * p + 1], c, s);
+  }
+}
+
+// Index of the V element (head h, slot j, dim d) in the tile-transposed layout.
+__device__ __forceinline__ size_t v_index(int h, int cap, int D, int j, int d) {
+  return (((size_t)h * (cap / kTile) + (j / kTile)) * D + d) * kTile + (j % kTile);
+}
+
+}  // namespace kvc

@@ -1,0 +1,141 @@
+// kvc_device.hpp -- argument blocks shared by the host layer and the HIP kernels.
+//
+// HBM layout of one cache (all per layer, head-major):
+//   region r in {sink, window0, window1}: capacity cap (a multiple of 64 slots)
+//     KA[H][cap][DA]   stored keys, dims [0, DA): the time band (+ padding dims
+//                      of the height band so rows are 16-byte multiples);
+//                      retime touches only this plane, so its traffic is
+//                      dense and coalesced
+//     KB[H][cap][DB]   stored keys, dims [DA, D)
+//     V [H][cap/64][D][64]  values in 64-slot tiles stored transposed
+//                      (d-major inside a tile): attention reads a tile as one
+//                      contiguous 16 KB block already in the layout its
+//                      P.V matrix-core product wants
+//     t [cap] int32, g [cap] int64
+//   bank (Rolling Sink): raw K, V [H][bank_tok][D]
+//   RoPE tables (fp32 cos/sin pairs): time [2*MAXPOS+1][Pt][2],
+//     height [grid_h][Pb][2], width [grid_w][Pb][2]
+#pragma once
+
+#include <cstdint>
+
+namespace kvc {
+
+constexpr int kTile = 64;        // slots per V tile / attention key tile
+constexpr int kMaxSegs = 4;
+
+struct RegionPtrs {
+  void* ka;
+  void* kb;
+  void* v;
+  int32_t* t;
+  int64_t* g;
+  int32_t cap;
+};
+
+struct Geo {
+  int32_t H, D, S, grid_w;
+  int32_t DA, DB;      // plane widths
+  int32_t dt, bw;      // time band width, height/width band width
+  int32_t esz;         // element bytes (2 bf16, 4 f32)
+};
+
+struct Tables {
+  const float* tcs;    // [(pos + maxpos)][dt/2][2]
+  const float* hcs;    // [h][bw/2][2]
+  const float* wcs;    // [w][bw/2][2]
+  int32_t maxpos;
+};
+
+struct SegW {
+  int32_t region, dst, src, n;
+  int64_t k0, v0;      // prefix offsets of this segment's K and V work items
+  int32_t vg0;         // first aligned 8-slot group of the segment
+};
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  int64_t k_tok, k_head, v_tok, v_head;   // element strides of the sources
+  RegionPtrs reg[2];                      // [sink, current window]
+  SegW seg[kMaxSegs];
+  int32_t nseg;
+  int64_t nk, nv;                         // total K / V work items
+  int32_t t0;                             // time of source frame 0
+  int64_t g0;                             // global index of source token 0
+  void* bank_k;
+  void* bank_v;
+  int32_t bank_tok;
+  int32_t bank_lo, bank_hi;               // source tokens captured raw into the bank at g0 + src
+  Geo geo;
+  Tables tab;
+};
+
+struct RangeW {
+  int32_t region, lo, n;
+  int32_t blk0;                           // first block of this range
+};
+
+struct RetimeArgs {
+  RegionPtrs reg[2];
+  RangeW rng[4];
+  int32_t nrng;
+  int32_t delta, clamp0;
+  Geo geo;
+  Tables tab;
+};
+
+struct CompactArgs {
+  RegionPtrs src, dst;
+  const int32_t* idx;                     // source slot of each destination slot
+  int32_t n;
+  int64_t nk, nv, nt;
+  Geo geo;
+};
+
+struct ExportArgs {
+  RegionPtrs reg[2];
+  int32_t ns, hs, S_tok, nw, hw, W_tok;
+  void* k;
+  void* v;
+  int32_t* t;
+  int64_t* g;
+  Geo geo;
+};
+
+struct KeyRegions {
+  const void* ka[2];
+  const void* kb[2];
+  const void* v[2];
+  int32_t cap[2];
+  int32_t n[2];                           // valid slots (a prefix of each region)
+};
+
+struct AttendArgs {
+  const void* q;
+  void* out;
+  int32_t Lq;
+  int32_t t0;                             // time of query frame 0
+  KeyRegions keys;
+  Geo geo;
+  Tables tab;
+  float scale;                            // 1/sqrt(D)
+};
+
+struct ScoreArgs {
+  const void* q;                          // raw query window [Nq][H][D]
+  float* qh;                              // scratch: rotated queries [H][Nq][D] (fp32 holding cache-dtype values)
+  float* m;                               // scratch: row max [H][Nq]
+  float* l;                               // scratch: row sum [H][Nq]
+  float* part;                            // scratch: per-head column sums [H][cap0 + cap1]
+  float* scores;                          // out: [n_valid] logical order
+  int32_t Nq;
+  int32_t qt[32];                         // time of each query frame
+  KeyRegions keys;
+  int32_t ns, hs, S_tok, nw, hw, W_tok;   // physical -> logical map
+  Geo geo;
+  Tables tab;
+  float scale;
+};
+
+}  // namespace kvc

@@ -1,0 +1,602 @@
+// kvc_host.cpp -- the C ABI of libkvc: validation, ring planning, workspace
+// layout, RoPE tables and kernel launches.  No device memory is allocated here:
+// the caller provides the workspace (and the score scratch).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_device.hpp"
+#include "kvc_launch.hpp"
+#include "kvc_ring.hpp"
+
+static_assert(KVC_MAX_POS == kvc::kMaxPos, "time table range");
+
+namespace {
+
+thread_local std::string g_err;
+
+kvc_status fail(kvc_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int32_t round64(int32_t x) { return (x + kvc::kTile - 1) / kvc::kTile * kvc::kTile; }
+
+struct RegionLayout {
+  size_t ka, kb, v, t, g;
+};
+
+struct Layout {
+  bool ok = false;
+  int32_t S_tok = 0, W_tok = 0, SP = 0, WP = 0, bank_tok = 0;
+  int32_t D = 0, DA = 0, DB = 0, dt = 0, bw = 0, esz = 0;
+  RegionLayout sink{}, win[2]{};
+  size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, total = 0;
+};
+
+Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_t H, int32_t D, kvc_dtype dt,
+                   int32_t bank_frames, uint32_t cflags) {
+  Layout L;
+  if (sink_frames < 0 || window_frames < 1 || S < 1 || H < 1 || bank_frames < 0) return L;
+  if (D != 64 && D != 128) return L;
+  if (dt != KVC_BF16 && dt != KVC_F32) return L;
+  const int64_t s_tok = (int64_t)sink_frames * S, w_tok = (int64_t)window_frames * S;
+  const int64_t b_tok = (int64_t)bank_frames * S;
+  if (s_tok + w_tok > (1 << 26) || b_tok > (1 << 26) || H > 4096) return L;
+  L.S_tok = (int32_t)s_tok;
+  L.W_tok = (int32_t)w_tok;
+  L.SP = round64(L.S_tok);
+  L.WP = round64(L.W_tok);
+  L.bank_tok = (int32_t)b_tok;
+  L.D = D;
+  L.esz = dt == KVC_BF16 ? 2 : 4;
+  L.bw = 2 * (D / 6);
+  L.dt = D - 2 * L.bw;
+  const int32_t E = 16 / L.esz;
+  L.DA = (L.dt + E - 1) / E * E;
+  L.DB = D - L.DA;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  auto region = [&](int32_t cap) {
+    RegionLayout r;
+    r.ka = take((size_t)H * cap * L.DA * L.esz);
+    r.kb = take((size_t)H * cap * L.DB * L.esz);
+    r.v = take((size_t)H * cap * D * L.esz);
+    r.t = take((size_t)cap * 4);
+    r.g = take((size_t)cap * 8);
+    return r;
+  };
+  L.sink = region(L.SP);
+  L.win[0] = region(L.WP);
+  if (cflags & KVC_CREATE_COMPACT) L.win[1] = region(L.WP);
+  L.bank_k = take((size_t)H * L.bank_tok * D * L.esz);
+  L.bank_v = take((size_t)H * L.bank_tok * D * L.esz);
+  L.tab_t = take((size_t)(2 * KVC_MAX_POS + 1) * (L.dt / 2) * 2 * 4);
+  L.tab_h = take((size_t)S * (L.bw / 2) * 2 * 4);
+  L.tab_w = take((size_t)S * (L.bw / 2) * 2 * 4);
+  L.keep = take((size_t)L.WP * 4);
+  L.total = off;
+  L.ok = true;
+  return L;
+}
+
+}  // namespace
+
+struct kvc_cache {
+  int32_t sink_frames, window_frames, S, H, D, grid_w, grid_h, bank_frames;
+  kvc_dtype dt;
+  uint32_t cflags;
+  Layout L;
+  char* ws;
+  kvc::Geo geo;
+  kvc::Tables tab;
+  kvc::RegionPtrs sink, win[2];
+  void* bank_k;
+  void* bank_v;
+  int32_t* keep_dev;
+  int32_t* keep_pinned;
+  hipEvent_t keep_evt;
+  bool keep_pending;
+  hipStream_t stream;
+  kvc::RingState st;
+  bool poisoned;
+};
+
+namespace {
+
+kvc::RegionPtrs region_ptrs(char* ws, const RegionLayout& r, int32_t cap) {
+  kvc::RegionPtrs p;
+  p.ka = ws + r.ka;
+  p.kb = ws + r.kb;
+  p.v = ws + r.v;
+  p.t = (int32_t*)(ws + r.t);
+  p.g = (int64_t*)(ws + r.g);
+  p.cap = cap;
+  return p;
+}
+
+kvc_status check(kvc_handle h) {
+  if (!h) return fail(KVC_EINVAL, "null handle");
+  if (h->poisoned) return fail(KVC_ESTATE, "handle poisoned by an earlier device error");
+  return KVC_OK;
+}
+
+kvc_status device_result(kvc_handle h, hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVC_OK;
+  h->poisoned = true;
+  return fail(KVC_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// The window region the cache currently reads from.
+const kvc::RegionPtrs& cur_win(kvc_handle h) { return h->win[h->st.win_buf]; }
+
+kvc::KeyRegions key_regions(kvc_handle h) {
+  kvc::KeyRegions k;
+  const kvc::RegionPtrs& w = cur_win(h);
+  k.ka[0] = h->sink.ka;
+  k.kb[0] = h->sink.kb;
+  k.v[0] = h->sink.v;
+  k.cap[0] = h->sink.cap;
+  k.n[0] = h->st.ns;
+  k.ka[1] = w.ka;
+  k.kb[1] = w.kb;
+  k.v[1] = w.v;
+  k.cap[1] = w.cap;
+  k.n[1] = h->st.nw;
+  return k;
+}
+
+// Launch the append kernel over a list of segments (in batches of kMaxSegs).
+hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, const void* k, const void* v,
+                           int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head, int32_t t0, int64_t g0,
+                           int32_t bank_lo, int32_t bank_hi) {
+  const int32_t CH = h->D * h->geo.esz / 16;
+  for (size_t b = 0; b < segs.size(); b += kvc::kMaxSegs) {
+    kvc::AppendArgs a{};
+    a.k = k;
+    a.v = v;
+    a.k_tok = k_tok;
+    a.k_head = k_head;
+    a.v_tok = v_tok;
+    a.v_head = v_head;
+    a.reg[0] = h->sink;
+    a.reg[1] = cur_win(h);
+    int64_t nk = 0, nv = 0;
+    int32_t ns = 0;
+    for (size_t i = b; i < segs.size() && ns < kvc::kMaxSegs; ++i, ++ns) {
+      const kvc::Seg& s = segs[i];
+      kvc::SegW& w = a.seg[ns];
+      w.region = s.region;
+      w.dst = s.dst;
+      w.src = s.src;
+      w.n = s.n;
+      w.k0 = nk;
+      w.v0 = nv;
+      w.vg0 = s.dst / 8;
+      const int32_t g_end = (s.dst + s.n + 7) / 8;
+      nk += (int64_t)s.n * h->H * CH;
+      nv += (int64_t)(g_end - w.vg0) * h->H * CH;
+    }
+    a.nseg = ns;
+    a.nk = nk;
+    a.nv = nv;
+    a.t0 = t0;
+    a.g0 = g0;
+    a.bank_k = h->bank_k;
+    a.bank_v = h->bank_v;
+    a.bank_tok = h->L.bank_tok;
+    a.bank_lo = bank_lo;
+    a.bank_hi = bank_hi;
+    a.geo = h->geo;
+    a.tab = h->tab;
+    hipError_t e = kvc::launch_append(a, h->stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+void build_tables(int32_t D, int32_t S, int32_t grid_w, std::vector<float>* tt, std::vector<float>* th,
+                  std::vector<float>* tw) {
+  const int32_t bw = 2 * (D / 6), dt = D - 2 * bw;
+  const int32_t Pt = dt / 2, Pb = bw / 2;
+  auto theta = [](int32_t j, int32_t width) { return std::pow(10000.0, -(2.0 * j) / (double)width); };
+  tt->assign((size_t)(2 * KVC_MAX_POS + 1) * Pt * 2, 0.f);
+  for (int32_t p = -KVC_MAX_POS; p <= KVC_MAX_POS; ++p)
+    for (int32_t j = 0; j < Pt; ++j) {
+      const double ang = (double)p * theta(j, dt);
+      float* o = &(*tt)[((size_t)(p + KVC_MAX_POS) * Pt + j) * 2];
+      o[0] = (float)std::cos(ang);
+      o[1] = (float)std::sin(ang);
+    }
+  const int32_t grid_h = S / grid_w;
+  th->assign((size_t)S * Pb * 2, 0.f);
+  tw->assign((size_t)S * Pb * 2, 0.f);
+  for (int32_t p = 0; p < grid_h; ++p)
+    for (int32_t j = 0; j < Pb; ++j) {
+      const double ang = (double)p * theta(j, bw);
+      (*th)[((size_t)p * Pb + j) * 2] = (float)std::cos(ang);
+      (*th)[((size_t)p * Pb + j) * 2 + 1] = (float)std::sin(ang);
+    }
+  for (int32_t p = 0; p < grid_w; ++p)
+    for (int32_t j = 0; j < Pb; ++j) {
+      const double ang = (double)p * theta(j, bw);
+      (*tw)[((size_t)p * Pb + j) * 2] = (float)std::cos(ang);
+      (*tw)[((size_t)p * Pb + j) * 2 + 1] = (float)std::sin(ang);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvc_workspace_bytes(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen, int32_t heads,
+                           int32_t head_dim, kvc_dtype dt, int32_t bank_frames, uint32_t create_flags) {
+  Layout L = make_layout(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames, create_flags);
+  return L.ok ? L.total : 0;
+}
+
+kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen, int32_t heads,
+                      int32_t head_dim, int32_t grid_w, kvc_dtype dt, int32_t bank_frames, uint32_t create_flags,
+                      void* workspace, size_t ws_bytes, void* hip_stream, kvc_handle* out) {
+  if (!out) return fail(KVC_EINVAL, "out is null");
+  *out = nullptr;
+  Layout L = make_layout(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames, create_flags);
+  if (!L.ok) return fail(KVC_EINVAL, "unsupported geometry (head_dim must be 64 or 128; sizes positive)");
+  if (grid_w < 1 || frame_seqlen % grid_w != 0) return fail(KVC_EINVAL, "frame_seqlen must be a multiple of grid_w");
+  if (create_flags & ~KVC_CREATE_COMPACT) return fail(KVC_EINVAL, "unknown create flag");
+  if (!workspace) return fail(KVC_EINVAL, "workspace is null");
+  if ((uintptr_t)workspace % kAlign != 0) return fail(KVC_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total) return fail(KVC_ENOMEM, "workspace smaller than kvc_workspace_bytes()");
+  kvc_cache* h = new (std::nothrow) kvc_cache();
+  if (!h) return fail(KVC_ENOMEM, "host allocation failed");
+  h->sink_frames = sink_frames;
+  h->window_frames = window_frames;
+  h->S = frame_seqlen;
+  h->H = heads;
+  h->D = head_dim;
+  h->grid_w = grid_w;
+  h->grid_h = frame_seqlen / grid_w;
+  h->bank_frames = bank_frames;
+  h->dt = dt;
+  h->cflags = create_flags;
+  h->L = L;
+  h->ws = (char*)workspace;
+  h->stream = (hipStream_t)hip_stream;
+  h->poisoned = false;
+  h->geo = kvc::Geo{heads, head_dim, frame_seqlen, grid_w, L.DA, L.DB, L.dt, L.bw, L.esz};
+  h->tab = kvc::Tables{(const float*)(h->ws + L.tab_t), (const float*)(h->ws + L.tab_h),
+                       (const float*)(h->ws + L.tab_w), KVC_MAX_POS};
+  h->sink = region_ptrs(h->ws, L.sink, L.SP);
+  h->win[0] = region_ptrs(h->ws, L.win[0], L.WP);
+  h->win[1] = (create_flags & KVC_CREATE_COMPACT) ? region_ptrs(h->ws, L.win[1], L.WP) : h->win[0];
+  h->bank_k = h->ws + L.bank_k;
+  h->bank_v = h->ws + L.bank_v;
+  h->keep_dev = (int32_t*)(h->ws + L.keep);
+  h->keep_pinned = nullptr;
+  h->keep_pending = false;
+  h->st.init(frame_seqlen, L.S_tok, L.W_tok);
+  hipError_t e = hipSuccess;
+  if (create_flags & KVC_CREATE_COMPACT) {
+    e = hipHostMalloc((void**)&h->keep_pinned, (size_t)L.WP * 4, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->keep_evt, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (h->keep_pinned) (void)hipHostFree(h->keep_pinned);
+      delete h;
+      return fail(KVC_ENOMEM, std::string("pinned staging: ") + hipGetErrorString(e));
+    }
+  }
+  std::vector<float> tt, th, tw;
+  build_tables(head_dim, frame_seqlen, grid_w, &tt, &th, &tw);
+  e = kvc::launch_fill_zero(h->ws, L.total, h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->ws + L.tab_t, tt.data(), tt.size() * 4, hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->ws + L.tab_h, th.data(), th.size() * 4, hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->ws + L.tab_w, tw.data(), tw.size() * 4, hipMemcpyHostToDevice, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) {
+    if (h->keep_pinned) {
+      (void)hipHostFree(h->keep_pinned);
+      (void)hipEventDestroy(h->keep_evt);
+    }
+    delete h;
+    return fail(KVC_EDEVICE, std::string("create: ") + hipGetErrorString(e));
+  }
+  *out = h;
+  return KVC_OK;
+}
+
+kvc_status kvc_destroy(kvc_handle h) {
+  if (!h) return fail(KVC_EINVAL, "null handle");
+  if (h->keep_pinned) {
+    if (h->keep_pending) (void)hipEventSynchronize(h->keep_evt);
+    (void)hipEventDestroy(h->keep_evt);
+    (void)hipHostFree(h->keep_pinned);
+  }
+  delete h;
+  return KVC_OK;
+}
+
+kvc_status kvc_set_stream(kvc_handle h, void* hip_stream) {
+  if (kvc_status s = check(h)) return s;
+  h->stream = (hipStream_t)hip_stream;
+  return KVC_OK;
+}
+
+kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_frames, int32_t t_index,
+                      uint32_t flags) {
+  if (kvc_status s = check(h)) return s;
+  if (!k || !v) return fail(KVC_EINVAL, "k/v null");
+  if (flags & ~KVC_APPEND_REPLACE_NEWEST) return fail(KVC_EINVAL, "unknown append flag");
+  const bool replace = (flags & KVC_APPEND_REPLACE_NEWEST) != 0;
+  kvc::RingState nx = h->st;
+  std::vector<kvc::Seg> segs;
+  int64_t g0 = 0;
+  std::string err;
+  if (!kvc::plan_append(nx, n_frames, t_index, replace, &segs, &g0, &err)) return fail(KVC_EINVAL, err);
+  const int32_t N = n_frames * h->S;
+  int32_t bank_lo = 0, bank_hi = 0;
+  if (h->L.bank_tok > 0 && g0 < h->L.bank_tok) bank_hi = (int32_t)std::min<int64_t>(N, h->L.bank_tok - g0);
+  const int64_t HD = (int64_t)h->H * h->D;
+  // the window region read by the kernel must be the post-plan buffer (unchanged by append)
+  hipError_t e = launch_segments(h, segs, k, v, HD, h->D, HD, h->D, t_index, g0, bank_lo, bank_hi);
+  if (kvc_status s = device_result(h, e, "append")) return s;
+  h->st = std::move(nx);
+  return KVC_OK;
+}
+
+kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out) {
+  if (kvc_status s = check(h)) return s;
+  if (!q || !out) return fail(KVC_EINVAL, "q/out null");
+  if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
+  if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "attend on an empty cache");
+  int32_t t0 = q_t_index;
+  if (q_t_index == KVC_T_NEWEST) {
+    if (!h->st.newest_valid) return fail(KVC_ESTATE, "no newest chunk for KVC_T_NEWEST");
+    const kvc::Seg& s0 = h->st.newest_segs.front();
+    t0 = h->st.t_at(s0.region, s0.dst) - s0.src / h->S;
+  }
+  if (t0 < -KVC_MAX_POS || (int64_t)t0 + q_frames - 1 > KVC_MAX_POS) return fail(KVC_EINVAL, "q time out of range");
+  kvc::AttendArgs a{};
+  a.q = q;
+  a.out = out;
+  a.Lq = q_frames * h->S;
+  a.t0 = t0;
+  a.keys = key_regions(h);
+  a.geo = h->geo;
+  a.tab = h->tab;
+  a.scale = (float)(1.0 / std::sqrt((double)h->D));
+  const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
+  hipError_t e = kvc::launch_attend(a, h->stream, force_general);
+  return device_result(h, e, "attend");
+}
+
+kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi) {
+  if (kvc_status s = check(h)) return s;
+  kvc::RingState nx = h->st;
+  std::vector<kvc::Range> rs;
+  std::string err;
+  if (!kvc::plan_retime(nx, delta, clamp0 != 0, slot_lo, slot_hi, &rs, &err)) return fail(KVC_EINVAL, err);
+  kvc::RetimeArgs a{};
+  a.reg[0] = h->sink;
+  a.reg[1] = cur_win(h);
+  int32_t blocks = 0;
+  a.nrng = (int32_t)rs.size();
+  for (size_t i = 0; i < rs.size(); ++i) {
+    a.rng[i].region = rs[i].region;
+    a.rng[i].lo = rs[i].lo;
+    a.rng[i].n = rs[i].n;
+    a.rng[i].blk0 = blocks;
+    blocks += (rs[i].n + 31) / 32;
+  }
+  a.delta = delta;
+  a.clamp0 = clamp0 != 0;
+  a.geo = h->geo;
+  a.tab = h->tab;
+  hipError_t e = kvc::launch_retime(a, blocks, h->stream);
+  if (kvc_status s = device_result(h, e, "retime")) return s;
+  h->st = std::move(nx);
+  return KVC_OK;
+}
+
+size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames) {
+  if (!h || q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return 0;
+  const size_t Nq = (size_t)q_frames * h->S;
+  return align_up((size_t)h->H * Nq * h->D * 4) + 2 * align_up((size_t)h->H * Nq * 4) +
+         align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4);
+}
+
+kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
+                     void* scratch, size_t scratch_bytes) {
+  if (kvc_status s = check(h)) return s;
+  if (!q_win || !q_t || !scores || !scratch) return fail(KVC_EINVAL, "null argument");
+  if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
+  if (scratch_bytes < kvc_score_scratch_bytes(h, q_frames)) return fail(KVC_ENOMEM, "score scratch too small");
+  if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
+  if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "score on an empty cache");
+  kvc::ScoreArgs a{};
+  for (int32_t f = 0; f < q_frames; ++f) {
+    if (q_t[f] < -KVC_MAX_POS || q_t[f] > KVC_MAX_POS) return fail(KVC_EINVAL, "q_t out of range");
+    a.qt[f] = q_t[f];
+  }
+  const size_t Nq = (size_t)q_frames * h->S;
+  char* p = (char*)scratch;
+  a.qh = (float*)p;
+  p += align_up((size_t)h->H * Nq * h->D * 4);
+  a.m = (float*)p;
+  p += align_up((size_t)h->H * Nq * 4);
+  a.l = (float*)p;
+  p += align_up((size_t)h->H * Nq * 4);
+  a.part = (float*)p;
+  a.q = q_win;
+  a.scores = scores;
+  a.Nq = (int32_t)Nq;
+  a.keys = key_regions(h);
+  a.ns = h->st.ns;
+  a.hs = h->st.hs;
+  a.S_tok = std::max(1, h->st.S_tok);
+  a.nw = h->st.nw;
+  a.hw = h->st.hw;
+  a.W_tok = h->st.W_tok;
+  a.geo = h->geo;
+  a.tab = h->tab;
+  a.scale = (float)(1.0 / std::sqrt((double)h->D));
+  hipError_t e = kvc::launch_score(a, h->stream);
+  return device_result(h, e, "score");
+}
+
+kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
+  if (kvc_status s = check(h)) return s;
+  if (!(h->cflags & KVC_CREATE_COMPACT)) return fail(KVC_EUNSUPPORTED, "compact needs KVC_CREATE_COMPACT");
+  kvc::RingState nx = h->st;
+  std::vector<int32_t> src;
+  std::string err;
+  if (!kvc::plan_compact(nx, keep_idx, n_keep, &src, &err)) return fail(KVC_EINVAL, err);
+  hipError_t e = hipSuccess;
+  if (!src.empty()) {
+    if (h->keep_pending) {
+      e = hipEventSynchronize(h->keep_evt);
+      h->keep_pending = false;
+    }
+    if (e == hipSuccess) {
+      std::memcpy(h->keep_pinned, src.data(), src.size() * 4);
+      e = hipMemcpyAsync(h->keep_dev, h->keep_pinned, src.size() * 4, hipMemcpyHostToDevice, h->stream);
+    }
+    if (e == hipSuccess) {
+      e = hipEventRecord(h->keep_evt, h->stream);
+      h->keep_pending = e == hipSuccess;
+    }
+    if (e == hipSuccess) {
+      kvc::CompactArgs a{};
+      a.src = h->win[h->st.win_buf];
+      a.dst = h->win[h->st.win_buf ^ 1];
+      a.idx = h->keep_dev;
+      a.n = (int32_t)src.size();
+      const int32_t CH = h->D * h->geo.esz / 16;
+      a.nk = (int64_t)a.n * h->H * CH;
+      a.nv = (int64_t)((a.n + 7) / 8) * h->D * h->H;
+      a.nt = a.n;
+      a.geo = h->geo;
+      e = kvc::launch_compact(a, h->stream);
+    }
+  }
+  if (kvc_status s = device_result(h, e, "compact")) return s;
+  h->st = std::move(nx);
+  return KVC_OK;
+}
+
+kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int32_t t_index) {
+  if (kvc_status s = check(h)) return s;
+  if (h->L.bank_tok == 0) return fail(KVC_ESTATE, "no bank (bank_frames was 0)");
+  if (h->st.global_end < h->L.bank_tok) return fail(KVC_ESTATE, "bank not complete yet");
+  if (bank_frame < 0 || n_frames < 1 || (int64_t)(bank_frame + n_frames) * h->S > h->L.bank_tok)
+    return fail(KVC_EINVAL, "bank frame range");
+  const int32_t b0 = bank_frame * h->S;
+  kvc::RingState nx = h->st;
+  std::vector<kvc::Seg> segs;
+  std::string err;
+  if (!kvc::plan_sink_push(nx, n_frames, b0, t_index, &segs, &err))
+    return fail(h->st.ns != h->st.S_tok || h->st.S_tok == 0 ? KVC_ESTATE : KVC_EINVAL, err);
+  const int64_t D = h->D;
+  const char* bk = (const char*)h->bank_k + (size_t)b0 * D * h->geo.esz;
+  const char* bv = (const char*)h->bank_v + (size_t)b0 * D * h->geo.esz;
+  const int64_t head = (int64_t)h->L.bank_tok * D;
+  hipError_t e = launch_segments(h, segs, bk, bv, D, head, D, head, t_index, b0, 0, 0);
+  if (kvc_status s = device_result(h, e, "sink_push")) return s;
+  h->st = std::move(nx);
+  return KVC_OK;
+}
+
+kvc_status kvc_info(kvc_handle h, kvc_info_t* out) {
+  if (!h || !out) return fail(KVC_EINVAL, "null argument");
+  const kvc::RingState& s = h->st;
+  std::memset(out, 0, sizeof(*out));
+  out->capacity = s.S_tok + s.W_tok;
+  out->n_valid = s.n_valid();
+  out->sink_tokens = s.S_tok;
+  out->window_tokens = s.W_tok;
+  out->sink_filled = s.ns;
+  out->window_filled = s.nw;
+  out->sink_head = s.hs;
+  out->window_head = s.hw;
+  out->global_end = s.global_end;
+  out->newest_valid = s.newest_valid ? 1 : 0;
+  out->newest_frames = s.newest_valid ? s.newest_frames : 0;
+  if (s.newest_valid) {
+    const kvc::Seg& s0 = s.newest_segs.front();
+    out->newest_t = s.t_at(s0.region, s0.dst) - s0.src / h->S;
+    out->newest_g = s.newest_g;
+  }
+  out->bank_tokens = h->L.bank_tok;
+  out->bank_complete = (h->L.bank_tok > 0 && s.global_end >= h->L.bank_tok) ? 1 : 0;
+  out->window_buffer = s.win_buf;
+  return KVC_OK;
+}
+
+kvc_status kvc_slot_times(kvc_handle h, int32_t* t, int64_t* g) {
+  if (!h) return fail(KVC_EINVAL, "null handle");
+  h->st.logical_times(t, g);
+  return KVC_OK;
+}
+
+kvc_status kvc_export(kvc_handle h, void* k, void* v, int32_t* t, int64_t* g) {
+  if (kvc_status s = check(h)) return s;
+  if (!k || !v || !t || !g) return fail(KVC_EINVAL, "null argument");
+  kvc::ExportArgs a{};
+  a.reg[0] = h->sink;
+  a.reg[1] = cur_win(h);
+  a.ns = h->st.ns;
+  a.hs = h->st.hs;
+  a.S_tok = std::max(1, h->st.S_tok);
+  a.nw = h->st.nw;
+  a.hw = h->st.hw;
+  a.W_tok = h->st.W_tok;
+  a.k = k;
+  a.v = v;
+  a.t = t;
+  a.g = g;
+  a.geo = h->geo;
+  hipError_t e = kvc::launch_export(a, h->st.n_valid(), h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  return device_result(h, e, "export");
+}
+
+kvc_status kvc_export_tables(kvc_handle h, int32_t band, int32_t pos_lo, int32_t n_pos, float* out) {
+  if (kvc_status s = check(h)) return s;
+  if (!out || n_pos < 0) return fail(KVC_EINVAL, "bad argument");
+  const int32_t Pt = h->L.dt / 2, Pb = h->L.bw / 2;
+  const char* src;
+  size_t row;
+  if (band == 0) {
+    if (pos_lo < -KVC_MAX_POS || pos_lo + n_pos - 1 > KVC_MAX_POS) return fail(KVC_EINVAL, "time positions");
+    row = (size_t)Pt * 2 * 4;
+    src = h->ws + h->L.tab_t + (size_t)(pos_lo + KVC_MAX_POS) * row;
+  } else if (band == 1 || band == 2) {
+    const int32_t lim = band == 1 ? h->grid_h : h->grid_w;
+    if (pos_lo < 0 || pos_lo + n_pos > lim) return fail(KVC_EINVAL, "grid positions");
+    row = (size_t)Pb * 2 * 4;
+    src = h->ws + (band == 1 ? h->L.tab_h : h->L.tab_w) + (size_t)pos_lo * row;
+  } else {
+    return fail(KVC_EINVAL, "band must be 0, 1 or 2");
+  }
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess) e = hipMemcpy(out, src, row * n_pos, hipMemcpyDeviceToHost);
+  return device_result(h, e, "export_tables");
+}
+
+const char* kvc_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

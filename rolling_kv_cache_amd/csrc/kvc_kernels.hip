@@ -1,0 +1,545 @@
+// kvc_kernels.hip -- HBM-bound kernels of libkvc for gfx950, and the general
+// (non matrix-core) attention and scoring paths.
+//
+//   append_kernel   fused 3D RoPE of new keys + ring scatter of K and V
+//                   (+ raw capture into the Rolling-Sink bank); also serves
+//                   the Rolling-Sink push, whose source is the bank
+//   retime_kernel   in-place time-band re-rotation by a per-slot delta
+//   compact_kernel  gather of kept window entries into the other buffer
+//   export_kernel   logical-order gather for inspection
+//   attend_general  one thread per (query, head), any dtype / head_dim
+//   score_*         per-entry attention mass, four small passes
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+
+#include "kvc_common.hip.hpp"
+#include "kvc_launch.hpp"
+
+namespace kvc {
+
+// ----------------------------------------------------------------------------
+// zero fill
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n16);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// append: K part (one thread per token x head x 16-byte chunk) rotates and
+// writes the key planes; V part (one thread per aligned 8-slot group x head x
+// chunk) transposes eight tokens' chunks into the d-major V tile rows.
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int E = Elem<T>::E;
+  const Geo& g = a.geo;
+  const int CH = g.D / E;
+  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid < a.nk) {
+    int si = 0;
+    while (si + 1 < a.nseg && gid >= a.seg[si + 1].k0) ++si;
+    const SegW& sg = a.seg[si];
+    const int64_t w = gid - sg.k0;
+    const int c = (int)(w % CH);
+    const int64_t r = w / CH;
+    const int h = (int)(r % g.H);
+    const int i = (int)(r / g.H);
+    const int src = sg.src + i;
+    const int slot = sg.dst + i;
+    Vec16<T> x;
+    x.u = *reinterpret_cast<const uint4*>((const T*)a.k + (int64_t)src * a.k_tok + (int64_t)h * a.k_head + c * E);
+    if (src >= a.bank_lo && src < a.bank_hi)
+      *reinterpret_cast<uint4*>((T*)a.bank_k + ((int64_t)h * a.bank_tok + (a.g0 + src)) * g.D + c * E) = x.u;
+    const int f = src / g.S, tok = src % g.S;
+    const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok % g.grid_w;
+    float xf[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
+    rotate_run<E>(xf, g, a.tab, c * E, t, hp, wp);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x.e[e] = Elem<T>::st(xf[e]);
+    const RegionPtrs& R = a.reg[sg.region];
+    const int d0 = c * E;
+    if (d0 < g.DA)
+      *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + slot) * g.DA + d0) = x.u;
+    else
+      *reinterpret_cast<uint4*>((T*)R.kb + ((int64_t)h * R.cap + slot) * g.DB + (d0 - g.DA)) = x.u;
+    if (h == 0 && c == 0) {
+      R.t[slot] = t;
+      R.g[slot] = a.g0 + src;
+    }
+    return;
+  }
+  gid -= a.nk;
+  if (gid >= a.nv) return;
+  int si = 0;
+  while (si + 1 < a.nseg && gid >= a.seg[si + 1].v0) ++si;
+  const SegW& sg = a.seg[si];
+  const int64_t w = gid - sg.v0;
+  const int c = (int)(w % CH);
+  const int64_t r = w / CH;
+  const int h = (int)(r % g.H);
+  const int grp = (int)(r / g.H);
+  const int slot0 = (sg.vg0 + grp) * 8;
+  const RegionPtrs& R = a.reg[sg.region];
+  Vec16<T> rows[8];
+  bool full = true;
+  bool valid[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int slot = slot0 + j;
+    valid[j] = slot >= sg.dst && slot < sg.dst + sg.n;
+    full = full && valid[j];
+    if (valid[j]) {
+      const int src = sg.src + (slot - sg.dst);
+      rows[j].u =
+          *reinterpret_cast<const uint4*>((const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
+      if (src >= a.bank_lo && src < a.bank_hi)
+        *reinterpret_cast<uint4*>((T*)a.bank_v + ((int64_t)h * a.bank_tok + (a.g0 + src)) * g.D + c * E) =
+            rows[j].u;
+    } else {
+      rows[j].u = make_uint4(0, 0, 0, 0);
+    }
+  }
+  T* vb = (T*)R.v + v_index(h, R.cap, g.D, slot0, 0);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    T* dst = vb + (size_t)(c * E + e) * kTile;
+    if (full) {
+      union {
+        uint4 u[sizeof(T) * 8 / 16];
+        T v[8];
+      } o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o.v[j] = rows[j].e[e];
+#pragma unroll
+      for (int q = 0; q < (int)(sizeof(T) * 8 / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = o.u[q];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (valid[j]) dst[j] = rows[j].e[e];
+    }
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t total = a.nk + a.nv;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (a.geo.esz == 2)
+    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// retime: each block owns up to 32 consecutive slots of one physical range,
+// reads their times, rotates the time band of every head's key by the slot's
+// actual change (t' - t) and finally writes t'.  Only the KA plane chunks that
+// hold time dims are touched.
+template <typename T>
+__global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
+  constexpr int E = Elem<T>::E;
+  const Geo& g = a.geo;
+  const int b = blockIdx.x;
+  int ri = 0;
+  while (ri + 1 < a.nrng && b >= a.rng[ri + 1].blk0) ++ri;
+  const RangeW& rg = a.rng[ri];
+  const int s0 = rg.lo + (b - rg.blk0) * 32;
+  const int ns = min(32, rg.lo + rg.n - s0);
+  const RegionPtrs& R = a.reg[rg.region];
+  __shared__ int s_dl[32];
+  __shared__ int s_tn[32];
+  const int tid = threadIdx.x;
+  if (tid < ns) {
+    const int t = R.t[s0 + tid];
+    const int tn = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
+    s_dl[tid] = tn - t;
+    s_tn[tid] = tn;
+  }
+  __syncthreads();
+  const int CHA = (g.dt + E - 1) / E;
+  const int total = g.H * ns * CHA;
+  for (int w = tid; w < total; w += 256) {
+    const int c = w % CHA;
+    const int rr = w / CHA;
+    const int j = rr % ns;
+    const int h = rr / ns;
+    T* p = (T*)R.ka + ((int64_t)h * R.cap + s0 + j) * g.DA + c * E;
+    Vec16<T> x;
+    x.u = *reinterpret_cast<const uint4*>(p);
+    float xf[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
+    const int dl = s_dl[j];
+#pragma unroll
+    for (int q = 0; q < E / 2; ++q) {
+      const int d = c * E + 2 * q;
+      if (d < g.dt) {
+        const float* cs = a.tab.tcs + ((size_t)(dl + a.tab.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
+        rot_pair(xf[2 * q], xf[2 * q + 1], cs[0], cs[1]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) x.e[e] = Elem<T>::st(xf[e]);
+    *reinterpret_cast<uint4*>(p) = x.u;
+  }
+  __syncthreads();
+  if (tid < ns) R.t[s0 + tid] = s_tn[tid];
+}
+
+hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  if (a.geo.esz == 2)
+    hipLaunchKernelGGL(retime_kernel<uint16_t>, dim3(nblocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(retime_kernel<float>, dim3(nblocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// compact: destination slot j <- source slot idx[j] (both window buffers).
+template <typename T>
+__global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
+  constexpr int E = Elem<T>::E;
+  const Geo& g = a.geo;
+  const int CH = g.D / E;
+  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid < a.nk) {
+    const int c = (int)(gid % CH);
+    const int64_t r = gid / CH;
+    const int h = (int)(r % g.H);
+    const int j = (int)(r / g.H);
+    const int sj = a.idx[j];
+    const int d0 = c * E;
+    if (d0 < g.DA) {
+      *reinterpret_cast<uint4*>((T*)a.dst.ka + ((int64_t)h * a.dst.cap + j) * g.DA + d0) =
+          *reinterpret_cast<const uint4*>((const T*)a.src.ka + ((int64_t)h * a.src.cap + sj) * g.DA + d0);
+    } else {
+      *reinterpret_cast<uint4*>((T*)a.dst.kb + ((int64_t)h * a.dst.cap + j) * g.DB + (d0 - g.DA)) =
+          *reinterpret_cast<const uint4*>((const T*)a.src.kb + ((int64_t)h * a.src.cap + sj) * g.DB + (d0 - g.DA));
+    }
+    return;
+  }
+  gid -= a.nk;
+  if (gid < a.nv) {
+    const int NG = (a.n + 7) / 8;
+    const int grp = (int)(gid % NG);
+    const int64_t r = gid / NG;
+    const int d = (int)(r % g.D);
+    const int h = (int)(r / g.D);
+    union {
+      uint4 u[sizeof(T) * 8 / 16];
+      T v[8];
+    } o;
+    const int j0 = grp * 8;
+    const int nn = min(8, a.n - j0);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      o.v[jj] = T(0);
+      if (jj < nn) o.v[jj] = ((const T*)a.src.v)[v_index(h, a.src.cap, g.D, a.idx[j0 + jj], d)];
+    }
+    T* dst = (T*)a.dst.v + v_index(h, a.dst.cap, g.D, j0, d);
+    if (nn == 8) {
+#pragma unroll
+      for (int q = 0; q < (int)(sizeof(T) * 8 / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = o.u[q];
+    } else {
+      for (int jj = 0; jj < nn; ++jj) dst[jj] = o.v[jj];
+    }
+    return;
+  }
+  gid -= a.nv;
+  if (gid < a.nt) {
+    const int j = (int)gid;
+    a.dst.t[j] = a.src.t[a.idx[j]];
+    a.dst.g[j] = a.src.g[a.idx[j]];
+  }
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  const int64_t total = a.nk + a.nv + a.nt;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (a.geo.esz == 2)
+    hipLaunchKernelGGL(compact_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(compact_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// export: logical entry l -> dense [l][h][D] K and V, t[l], g[l].
+__device__ __forceinline__ void logical_slot(int l, int ns, int hs, int S_tok, int hw, int W_tok, int& region,
+                                             int& slot) {
+  if (l < ns) {
+    region = 0;
+    slot = (hs + l) % S_tok;
+  } else {
+    region = 1;
+    slot = (hw + (l - ns)) % W_tok;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void export_kernel(ExportArgs a, int n) {
+  constexpr int E = Elem<T>::E;
+  const Geo& g = a.geo;
+  const int CH = g.D / E;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)n * g.H * CH) return;
+  const int c = (int)(gid % CH);
+  const int64_t r = gid / CH;
+  const int h = (int)(r % g.H);
+  const int l = (int)(r / g.H);
+  int region, slot;
+  logical_slot(l, a.ns, a.hs, a.S_tok, a.hw, a.W_tok, region, slot);
+  const RegionPtrs& R = a.reg[region];
+  const int d0 = c * E;
+  uint4 kk;
+  if (d0 < g.DA)
+    kk = *reinterpret_cast<const uint4*>((const T*)R.ka + ((int64_t)h * R.cap + slot) * g.DA + d0);
+  else
+    kk = *reinterpret_cast<const uint4*>((const T*)R.kb + ((int64_t)h * R.cap + slot) * g.DB + (d0 - g.DA));
+  *reinterpret_cast<uint4*>((T*)a.k + ((int64_t)l * g.H + h) * g.D + d0) = kk;
+  Vec16<T> vv;
+#pragma unroll
+  for (int e = 0; e < E; ++e) vv.e[e] = ((const T*)R.v)[v_index(h, R.cap, g.D, slot, d0 + e)];
+  *reinterpret_cast<uint4*>((T*)a.v + ((int64_t)l * g.H + h) * g.D + d0) = vv.u;
+  if (h == 0 && c == 0) {
+    a.t[l] = R.t[slot];
+    a.g[l] = R.g[slot];
+  }
+}
+
+hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s) {
+  const int64_t total = (int64_t)n_valid * a.geo.H * (a.geo.D * a.geo.esz / 16);
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (a.geo.esz == 2)
+    hipLaunchKernelGGL(export_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a, n_valid);
+  else
+    hipLaunchKernelGGL(export_kernel<float>, dim3(blocks), dim3(256), 0, s, a, n_valid);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Query rotation shared by the general attention and the score passes:
+// rotate row (token i, head h) of a raw [N][H][D] query tensor at the time of
+// its frame and round it to the cache dtype.
+template <typename T, int D>
+__device__ __forceinline__ void load_rotated_query(const T* q, int i, int h, int t, const Geo& g, const Tables& tb,
+                                                   float* out) {
+  constexpr int E = Elem<T>::E;
+  const int tok = i % g.S;
+  const int hp = tok / g.grid_w, wp = tok % g.grid_w;
+  const T* row = q + ((int64_t)i * g.H + h) * D;
+#pragma unroll
+  for (int c = 0; c < D / E; ++c) {
+    Vec16<T> x;
+    x.u = *reinterpret_cast<const uint4*>(row + c * E);
+    float xf[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
+    rotate_run<E>(xf, g, tb, c * E, t, hp, wp);
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[c * E + e] = Elem<T>::ld(Elem<T>::st(xf[e]));
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ float key_dot(const float* qv, const KeyRegions& kr, int r, int h, int j, const Geo& g) {
+  constexpr int E = Elem<T>::E;
+  const T* ka = (const T*)kr.ka[r] + ((int64_t)h * kr.cap[r] + j) * g.DA;
+  const T* kb = (const T*)kr.kb[r] + ((int64_t)h * kr.cap[r] + j) * g.DB;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / E; ++c) {
+    Vec16<T> x;
+    const int d0 = c * E;
+    x.u = d0 < g.DA ? *reinterpret_cast<const uint4*>(ka + d0) : *reinterpret_cast<const uint4*>(kb + (d0 - g.DA));
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(qv[d0 + e], Elem<T>::ld(x.e[e]), acc);
+  }
+  return acc;
+}
+
+// General attention: one thread per (query row, head), online softmax.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
+  const Geo& g = a.geo;
+  const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (gid >= (int64_t)a.Lq * g.H) return;
+  const int h = (int)(gid % g.H);
+  const int i = (int)(gid / g.H);
+  float qv[D];
+  load_rotated_query<T, D>((const T*)a.q, i, h, a.t0 + i / g.S, g, a.tab, qv);
+  float m = -INFINITY, l = 0.f;
+  float o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) o[d] = 0.f;
+  for (int r = 0; r < 2; ++r) {
+    const T* vbase = (const T*)a.keys.v[r];
+    for (int j = 0; j < a.keys.n[r]; ++j) {
+      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g) * a.scale;
+      const float mn = fmaxf(m, s);
+      const float alpha = expf(m - mn);
+      const float p = expf(s - mn);
+      l = l * alpha + p;
+      m = mn;
+      const T* vrow = vbase + v_index(h, a.keys.cap[r], D, j, 0);
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = o[d] * alpha + p * Elem<T>::ld(vrow[(size_t)d * kTile]);
+    }
+  }
+  T* out = (T*)a.out + ((int64_t)i * g.H + h) * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) out[d] = Elem<T>::st(o[d] * inv);
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general) {
+  if (!force_general && a.geo.esz == 2 && a.geo.D == 128) return launch_attend_mfma(a, s);
+  const int64_t total = (int64_t)a.Lq * a.geo.H;
+  const unsigned blocks = (unsigned)((total + 63) / 64);
+  if (a.geo.esz == 2) {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((attend_general_kernel<uint16_t, 128>), dim3(blocks), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_general_kernel<uint16_t, 64>), dim3(blocks), dim3(64), 0, s, a);
+  } else {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((attend_general_kernel<float, 128>), dim3(blocks), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_general_kernel<float, 64>), dim3(blocks), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// score: (1) rotate the query window, (2) per-row max and sum of exp, (3) per
+// (key, head) column sum of the normalized probabilities, (4) sum over heads
+// into logical order.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
+  const Geo& g = a.geo;
+  const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (gid >= (int64_t)a.Nq * g.H) return;
+  const int h = (int)(gid % g.H);
+  const int i = (int)(gid / g.H);
+  float qv[D];
+  load_rotated_query<T, D>((const T*)a.q, i, h, a.qt[i / g.S], g, a.tab, qv);
+  float* dst = a.qh + ((int64_t)h * a.Nq + i) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) dst[d] = qv[d];
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void score_rows_kernel(ScoreArgs a) {
+  const Geo& g = a.geo;
+  const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (gid >= (int64_t)a.Nq * g.H) return;
+  const int h = (int)(gid / a.Nq);
+  const int i = (int)(gid % a.Nq);
+  float qv[D];
+  const float* src = a.qh + ((int64_t)h * a.Nq + i) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) qv[d] = src[d];
+  float m = -INFINITY, l = 0.f;
+  for (int r = 0; r < 2; ++r)
+    for (int j = 0; j < a.keys.n[r]; ++j) {
+      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g) * a.scale;
+      const float mn = fmaxf(m, s);
+      l = l * expf(m - mn) + expf(s - mn);
+      m = mn;
+    }
+  a.m[(int64_t)h * a.Nq + i] = m;
+  a.l[(int64_t)h * a.Nq + i] = l;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void score_cols_kernel(ScoreArgs a) {
+  const Geo& g = a.geo;
+  const int ncap = a.keys.cap[0] + a.keys.cap[1];
+  const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (gid >= (int64_t)ncap * g.H) return;
+  const int h = (int)(gid / ncap);
+  const int p = (int)(gid % ncap);
+  const int r = p < a.keys.cap[0] ? 0 : 1;
+  const int j = r == 0 ? p : p - a.keys.cap[0];
+  if (j >= a.keys.n[r]) return;
+  constexpr int E = Elem<T>::E;
+  float kv[D];
+  const T* ka = (const T*)a.keys.ka[r] + ((int64_t)h * a.keys.cap[r] + j) * g.DA;
+  const T* kb = (const T*)a.keys.kb[r] + ((int64_t)h * a.keys.cap[r] + j) * g.DB;
+#pragma unroll
+  for (int d = 0; d < D; ++d) kv[d] = Elem<T>::ld(d < g.DA ? ka[d] : kb[d - g.DA]);
+  (void)E;
+  double acc = 0.0;
+  for (int i = 0; i < a.Nq; ++i) {
+    const float* qv = a.qh + ((int64_t)h * a.Nq + i) * D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qv[d], kv[d], s);
+    s *= a.scale;
+    acc += (double)(expf(s - a.m[(int64_t)h * a.Nq + i]) / a.l[(int64_t)h * a.Nq + i]);
+  }
+  a.part[(int64_t)h * ncap + p] = (float)acc;
+}
+
+__global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
+  const int ncap = a.keys.cap[0] + a.keys.cap[1];
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= ncap) return;
+  const int r = p < a.keys.cap[0] ? 0 : 1;
+  const int j = r == 0 ? p : p - a.keys.cap[0];
+  if (j >= a.keys.n[r]) return;
+  float acc = 0.f;
+  for (int h = 0; h < a.geo.H; ++h) acc += a.part[(int64_t)h * ncap + p];
+  int l;
+  if (r == 0)
+    l = (j - a.hs + a.S_tok) % a.S_tok;
+  else
+    l = a.ns + (j - a.hw + a.W_tok) % a.W_tok;
+  a.scores[l] = acc;
+}
+
+template <typename T, int D>
+static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.Nq * a.geo.H;
+  const unsigned b1 = (unsigned)((rows + 63) / 64);
+  hipLaunchKernelGGL((score_rot_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((score_rows_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
+  const int64_t cols = (int64_t)(a.keys.cap[0] + a.keys.cap[1]) * a.geo.H;
+  hipLaunchKernelGGL((score_cols_kernel<T, D>), dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, a);
+  const int ncap = a.keys.cap[0] + a.keys.cap[1];
+  hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
+}
+
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
+  if (a.geo.esz == 2) {
+    if (a.geo.D == 128)
+      score_launch_all<uint16_t, 128>(a, s);
+    else
+      score_launch_all<uint16_t, 64>(a, s);
+  } else {
+    if (a.geo.D == 128)
+      score_launch_all<float, 128>(a, s);
+    else
+      score_launch_all<float, 64>(a, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

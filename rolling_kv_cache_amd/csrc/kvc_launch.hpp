@@ -1,0 +1,21 @@
+// kvc_launch.hpp -- host-callable launchers of the libkvc HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "kvc_device.hpp"
+
+namespace kvc {
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s);
+// Attention: the matrix-core path for bf16 with head_dim 128, else the
+// general per-row path.  `force_general` selects the latter (tests).
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general);
+hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+
+}  // namespace kvc

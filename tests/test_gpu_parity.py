@@ -1,0 +1,191 @@
+"""GPU parity of libkvc against the CPU oracle on small shapes that still span several key tiles and
+ragged tails, plus error paths.  Every call goes through the C ABI (ctypes binding)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_state_equal, check_attention, dev, log, new_cache, gpu_bits
+from oracle import OracleCache, cos_sin_table, make_run, band_split
+from workloads import WORKLOADS, Workload, chunk_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _drive(w, n_chunks=None, full_attention=True, compact=False, general=False):
+    from rolling_kv_cache_amd.policies import driver_for
+    gc = new_cache(w, compact=compact)
+    drv = driver_for(w.name)(gc, w)
+    run = make_run(w)
+    q_prev_d = q_prev = None
+    for i in range(n_chunks or w.n_chunks):
+        log(f"  {w.name} chunk {i}")
+        q, k, v = chunk_inputs(w, i)
+        qd, kd, vd = dev(q, w), dev(k, w), dev(v, w)
+        if general:
+            os.environ["KVC_ATTEND_GENERAL"] = "1"
+        try:
+            out = drv.step(i, qd, kd, vd, q_prev=q_prev_d)
+        finally:
+            os.environ.pop("KVC_ATTEND_GENERAL", None)
+        kw = {}
+        if getattr(drv, "last", None):
+            kw["keep_override"] = drv.last["keep"]
+        if w.name.startswith("c5b"):
+            ref = run.step(i, q, k, v, q_prev=q_prev, f64=w.dtype == "f32", **kw)
+        else:
+            ref = run.step(i, q, k, v, f64=w.dtype == "f32")
+        assert_state_equal(gc, run.cache, w, f"{w.name} chunk {i}")
+        check_attention(out.float().cpu().numpy(), ref, f"{w.name} chunk {i}")
+        q_prev, q_prev_d = q, qd
+    return gc, run
+
+
+# ---------------------------------------------------------------- tables
+def test_rope_tables_bitwise():
+    w = WORKLOADS["c3"]
+    gc = new_cache(Workload("tab", 300, 2, 128, "bf16", 30, 52, 1, 2, (1,)))
+    (ts, tw), (hs, hw), _ = band_split(128)
+    for lo, n in [(-60, 400), (16383 - 50, 51), (-16383, 20)]:
+        got = gc.export_tables(0, lo, n)
+        c, s = cos_sin_table(range(lo, lo + n), tw)
+        assert np.array_equal(got[..., 0].view(np.uint32), c.view(np.uint32))
+        assert np.array_equal(got[..., 1].view(np.uint32), s.view(np.uint32))
+    for band, npos in ((1, w.grid_h), (2, w.grid_w)):
+        got = gc.export_tables(band, 0, npos)
+        c, s = cos_sin_table(range(npos), hw)
+        assert np.array_equal(got[..., 0].view(np.uint32), c.view(np.uint32))
+        assert np.array_equal(got[..., 1].view(np.uint32), s.view(np.uint32))
+
+
+# ---------------------------------------------------------------- streams at small sizes
+def test_tiny_fp32_stream():
+    """The Tiny workload in full: 12 one-frame chunks, eviction from chunk 5, fp64 brute-force reference."""
+    _drive(WORKLOADS["tiny"])
+
+
+SMALL_SW = Workload("sw_small", 201, 3, 128, "bf16", 6, 10, 2, 6, (1, 3, 3, 3, 2, 3, 3, 1, 3))
+
+
+def test_small_bf16_sliding_window_mfma():
+    """bf16 head_dim 128 through the matrix-core kernel: 60-token frames, a 1-frame first chunk so later
+    chunks straddle the sink/window boundary, ragged 64-slot tiles in both regions, wrap-around."""
+    _drive(SMALL_SW)
+
+
+def test_small_bf16_sliding_window_general_path():
+    _drive(SMALL_SW, general=True)
+
+
+def test_small_rolling_sink():
+    base = WORKLOADS["c4"]
+    _drive(Workload("c4_small", 203, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
+                    (3,) * 20 + (2,), base.bank_frames))
+
+
+def test_small_infinity_rope():
+    base = WORKLOADS["c5a"]
+    _drive(Workload("c5a_small", 204, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
+                    (3,) * 14 + (2,), cut_chunks=(7, 11)), compact=True)
+
+
+def test_small_deep_forcing():
+    base = WORKLOADS["c5b"]
+    gc, run = _drive(Workload("c5b_small", 205, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
+                              (3,) * 16), compact=True)
+
+
+def test_scores_match_oracle():
+    w = Workload("score_small", 206, 3, 128, "bf16", 4, 8, 1, 5, (2, 2, 2))
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(3):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    qw, _, _ = chunk_inputs(w, 7, frames=2)
+    s_gpu = gc.score(dev(qw, w), [3, 4]).cpu().numpy().astype(np.float64)
+    s_ref = oc.score(qw, 2, [3, 4], f64=True)
+    assert abs(s_gpu.sum() - w.heads * 2 * w.frame_seqlen) < 1e-3
+    assert np.max(np.abs(s_gpu - s_ref)) < 1e-4 * max(1.0, s_ref.max())
+
+
+def test_replace_newest_denoise_steps():
+    """Four denoising re-writes of the newest chunk, then the clean commit, before each new chunk."""
+    w = Workload("replace", 207, 2, 128, "bf16", 4, 8, 1, 4, (2,) * 6)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(6):
+        for step in range(5):
+            q, k, v = chunk_inputs(w, 10 * i + step, frames=2)
+            rep = step > 0
+            gc.append(dev(k, w), dev(v, w), 2 * i, replace_newest=rep)
+            oc.append(k, v, 2, 2 * i, replace_newest=rep)
+            out = gc.attend(dev(q, w))
+            check_attention(out.float().cpu().numpy(), oc.attend(q, 2), f"replace {i}.{step}")
+        assert_state_equal(gc, oc, w, f"replace chunk {i}")
+
+
+def test_uniform_retime_keeps_attention():
+    """Relative-position invariance on the GPU: shift every entry and the queries by the same delta."""
+    w = SMALL_SW
+    gc = new_cache(w)
+    for i in range(5):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), w.chunk_start_frame(i))
+    a = gc.attend(dev(q, w), 30).float().cpu().numpy()
+    gc.retime(57)
+    b = gc.attend(dev(q, w), 87).float().cpu().numpy()
+    check_attention(b, a, "uniform retime")
+
+
+# ---------------------------------------------------------------- edge and error paths
+def test_error_paths_leave_state_unchanged():
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("err", 208, 2, 128, "bf16", 4, 8, 1, 3, (1,) * 4, bank_frames=2)
+    gc = new_cache(w)
+    q, k, v = chunk_inputs(w, 0)
+    with pytest.raises(KVCError) as e:
+        gc.attend(dev(q, w), 0)                                   # empty cache
+    assert e.value.code == 3
+    with pytest.raises(KVCError):
+        gc.sink_push(0, 1, 0)                                     # bank incomplete
+    gc.append(dev(k, w), dev(v, w), 0)
+    gc.append(dev(k, w), dev(v, w), 1)
+    before = {n: gpu_bits(x) if x.dtype != torch.int32 and x.dtype != torch.int64 else x.cpu().numpy()
+              for n, x in gc.export().items()}
+    info = gc.info()
+    big = torch.zeros((4 * 32, 2, 128), dtype=torch.bfloat16, device="cuda")
+    bad_calls = [
+        lambda: gc.append(big, big, 5),                           # chunk larger than the window
+        lambda: gc.append(torch.cat([dev(k, w)] * 2), torch.cat([dev(v, w)] * 2), 1, replace_newest=True),
+        lambda: gc.retime(1, False, 0, info["n_valid"] + 1),        # range past n_valid
+        lambda: gc.retime(20000),                                   # |delta| > KVC_MAX_POS
+        lambda: gc.compact([0, 1]),                                 # no KVC_CREATE_COMPACT
+        lambda: gc.append(dev(k, w), dev(v, w), 16384),            # time past the table
+        lambda: gc.sink_push(1, 2, 5),                              # bank frames past the bank
+    ]
+    for j, call in enumerate(bad_calls):
+        with pytest.raises(KVCError):
+            call()
+        after = gc.export()
+        for n, x in after.items():
+            y = gpu_bits(x) if x.dtype not in (torch.int32, torch.int64) else x.cpu().numpy()
+            assert np.array_equal(y, before[n]), (j, n)
+        assert gc.info() == info, j
+
+
+def test_compact_validation():
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("cval", 209, 2, 128, "bf16", 4, 8, 1, 3, (1,) * 4)
+    gc = new_cache(w, compact=True)
+    for i in range(4):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), i)
+    n = gc.info()["n_valid"]
+    for keep in ([0, 2, 1], [1, 2, 3], list(range(32)) + [n], list(range(32)) + [40, 40]):
+        with pytest.raises(KVCError):
+            gc.compact(keep)
+    gc.compact(list(range(32)) + [40, 70, 71, 127])
+    assert gc.info()["n_valid"] == 36

@@ -100,9 +100,10 @@ def gen(cfg_id: int, chunk: int, tensor_id: int, n_tokens: int, heads: int,
     return np.ascontiguousarray(x)
 
 
-def chunk_inputs(w: Workload, chunk: int, tensors=(TENSOR_Q, TENSOR_K, TENSOR_V)):
-    """The seeded q/k/v of one chunk of workload w (tokens = frames * frame_seqlen)."""
-    n = w.chunk_frames[chunk] * w.frame_seqlen
+def chunk_inputs(w: Workload, chunk: int, tensors=(TENSOR_Q, TENSOR_K, TENSOR_V), frames=None):
+    """The seeded q/k/v of one chunk of workload w (tokens = frames * frame_seqlen); `frames` overrides the
+    schedule's frame count (and allows chunk ids past the schedule)."""
+    n = (w.chunk_frames[chunk] if frames is None else frames) * w.frame_seqlen
     return tuple(gen(w.cfg_id, chunk, tid, n, w.heads, w.head_dim, w.dtype) for tid in tensors)
 
 
