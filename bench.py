@@ -133,18 +133,37 @@ def main():
         torch.cuda.synchronize()
         if i >= 2:
             app_cold.append(a.elapsed_time(b))
-    del flush
+    # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
+    cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cy = torch.empty_like(cx)
+    cy.copy_(cx)
+    cp_ms = []
+    for i in range(5):
+        a, b = ev(), ev()
+        a.record(stream)
+        cy.copy_(cx)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cp_ms.append(a.elapsed_time(b))
+    copy_gbps = 2.0 * (1 << 30) / (float(np.median(cp_ms)) * 1e-3) / 1e9
+    del flush, cx, cy
 
     dt = D - 4 * (D // 6)
     app_bytes = 4.0 * N * H * D * 2
-    ret_bytes = 4.0 * Lk * H * dt * 2
+    ret_bytes = 2.0 * Lk * H * dt * 2
     att_tflops = flop / (att_avg * 1e-3) / 1e12
     value = flop / (ms_step * 1e-3) / 1e12
 
     traffic = None
     if os.path.exists(args.traffic):
+        # counters taken on an older version of the kernel source do not count
+        import hashlib
+        src = os.path.join(ROOT, "rolling_kv_cache_amd", "csrc", "kvc_attend.hip")
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
         try:
-            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+            rec = json.load(open(args.traffic))
+            if rec.get("kernel_source_sha256") == digest:
+                traffic = rec.get("bytes_per_launch")
         except Exception:
             traffic = None
 
@@ -177,6 +196,7 @@ def main():
             "retime_GBps_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9, 1),
             "append_hbm_frac_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "retime_hbm_frac_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "hbm_copy_GBps_measured": round(copy_gbps, 1),
         },
     }
     if not args.no_cpu_baseline:

@@ -49,8 +49,7 @@ struct Tables {
 
 struct SegW {
   int32_t region, dst, src, n;
-  int64_t k0, v0;      // prefix offsets of this segment's K and V work items
-  int32_t vg0;         // first aligned 8-slot group of the segment
+  int32_t kb0, vb0;    // first K-part / V-part block of this segment
 };
 
 struct AppendArgs {
@@ -60,7 +59,7 @@ struct AppendArgs {
   RegionPtrs reg[2];                      // [sink, current window]
   SegW seg[kMaxSegs];
   int32_t nseg;
-  int64_t nk, nv;                         // total K / V work items
+  int32_t nkb, nvb;                       // K-part / V-part blocks
   int32_t t0;                             // time of source frame 0
   int64_t g0;                             // global index of source token 0
   void* bank_k;

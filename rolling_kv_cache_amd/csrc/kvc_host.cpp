@@ -162,7 +162,6 @@ kvc::KeyRegions key_regions(kvc_handle h) {
 hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, const void* k, const void* v,
                            int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head, int32_t t0, int64_t g0,
                            int32_t bank_lo, int32_t bank_hi) {
-  const int32_t CH = h->D * h->geo.esz / 16;
   for (size_t b = 0; b < segs.size(); b += kvc::kMaxSegs) {
     kvc::AppendArgs a{};
     a.k = k;
@@ -173,7 +172,6 @@ hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, cons
     a.v_head = v_head;
     a.reg[0] = h->sink;
     a.reg[1] = cur_win(h);
-    int64_t nk = 0, nv = 0;
     int32_t ns = 0;
     for (size_t i = b; i < segs.size() && ns < kvc::kMaxSegs; ++i, ++ns) {
       const kvc::Seg& s = segs[i];
@@ -182,16 +180,8 @@ hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, cons
       w.dst = s.dst;
       w.src = s.src;
       w.n = s.n;
-      w.k0 = nk;
-      w.v0 = nv;
-      w.vg0 = s.dst / 8;
-      const int32_t g_end = (s.dst + s.n + 7) / 8;
-      nk += (int64_t)s.n * h->H * CH;
-      nv += (int64_t)(g_end - w.vg0) * h->H * CH;
     }
     a.nseg = ns;
-    a.nk = nk;
-    a.nv = nv;
     a.t0 = t0;
     a.g0 = g0;
     a.bank_k = h->bank_k;

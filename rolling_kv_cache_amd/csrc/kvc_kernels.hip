@@ -37,82 +37,124 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// append: K part (one thread per token x head x 16-byte chunk) rotates and
-// writes the key planes; V part (one thread per aligned 8-slot group x head x
-// chunk) transposes eight tokens' chunks into the d-major V tile rows.
+// append.  One grid, two kinds of 256-thread blocks:
+//   K blocks: one head x (256/CH)*4 consecutive tokens of a segment; lanes run
+//     over the row's 16-byte chunks first, so a wave reads whole 256-byte
+//     source rows and writes consecutive destination rows of that head's key
+//     planes; each thread keeps four chunks in flight.
+//   V blocks: one 64-slot tile x (256/(8*CH)) heads; thread (group of 8 slots,
+//     chunk) loads eight tokens' chunk, transposes it in registers and writes
+//     eight d-rows of the tile, so eight lanes fill one 128-byte tile row.
+// All index arithmetic is 32-bit.
 template <typename T>
+__device__ __forceinline__ SegW pick_seg_k(const AppendArgs& a, int b) {
+  SegW sg = a.seg[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < a.nseg && b >= a.seg[i].kb0) sg = a.seg[i];
+  return sg;
+}
+
+template <typename T>
+__device__ __forceinline__ SegW pick_seg_v(const AppendArgs& a, int b) {
+  SegW sg = a.seg[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < a.nseg && b >= a.seg[i].vb0) sg = a.seg[i];
+  return sg;
+}
+
+template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int E = Elem<T>::E;
+  constexpr int CH = D / E;                 // 16-byte chunks per row
+  constexpr int TL = 256 / CH;              // token lanes per K block
+  constexpr int TPB = TL * 4;               // tokens per K block
+  constexpr int HPB = 256 / (8 * CH);       // heads per V block
   const Geo& g = a.geo;
-  const int CH = g.D / E;
-  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid < a.nk) {
-    int si = 0;
-    while (si + 1 < a.nseg && gid >= a.seg[si + 1].k0) ++si;
-    const SegW& sg = a.seg[si];
-    const int64_t w = gid - sg.k0;
-    const int c = (int)(w % CH);
-    const int64_t r = w / CH;
-    const int h = (int)(r % g.H);
-    const int i = (int)(r / g.H);
-    const int src = sg.src + i;
-    const int slot = sg.dst + i;
-    Vec16<T> x;
-    x.u = *reinterpret_cast<const uint4*>((const T*)a.k + (int64_t)src * a.k_tok + (int64_t)h * a.k_head + c * E);
-    if (src >= a.bank_lo && src < a.bank_hi)
-      *reinterpret_cast<uint4*>((T*)a.bank_k + ((int64_t)h * a.bank_tok + (a.g0 + src)) * g.D + c * E) = x.u;
-    const int f = src / g.S, tok = src % g.S;
-    const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok % g.grid_w;
-    float xf[E];
+  const int tid = threadIdx.x;
+  int b = blockIdx.x;
+  if (b < a.nkb) {
+    const SegW sg = pick_seg_k<T>(a, b);
+    const RegionPtrs R = sg.region == 0 ? a.reg[0] : a.reg[1];
+    const int local = b - sg.kb0;
+    const int h = local % g.H;
+    const int tok0 = (local / g.H) * TPB;
+    const int c = tid % CH;
+    const int tl = tid / CH;
+    Vec16<T> x[4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
-    rotate_run<E>(xf, g, a.tab, c * E, t, hp, wp);
+    for (int u = 0; u < 4; ++u) {
+      const int i = tok0 + tl + u * TL;
+      if (i < sg.n) {
+        const int src = sg.src + i;
+        x[u].u = *reinterpret_cast<const uint4*>((const T*)a.k + (int64_t)src * a.k_tok + (int64_t)h * a.k_head +
+                                                 c * E);
+      }
+    }
 #pragma unroll
-    for (int e = 0; e < E; ++e) x.e[e] = Elem<T>::st(xf[e]);
-    const RegionPtrs& R = a.reg[sg.region];
-    const int d0 = c * E;
-    if (d0 < g.DA)
-      *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + slot) * g.DA + d0) = x.u;
-    else
-      *reinterpret_cast<uint4*>((T*)R.kb + ((int64_t)h * R.cap + slot) * g.DB + (d0 - g.DA)) = x.u;
-    if (h == 0 && c == 0) {
-      R.t[slot] = t;
-      R.g[slot] = a.g0 + src;
+    for (int u = 0; u < 4; ++u) {
+      const int i = tok0 + tl + u * TL;
+      if (i >= sg.n) break;
+      const int src = sg.src + i;
+      const int slot = sg.dst + i;
+      if (src >= a.bank_lo && src < a.bank_hi)
+        *reinterpret_cast<uint4*>((T*)a.bank_k + ((int64_t)h * a.bank_tok + (a.g0 + src)) * D + c * E) = x[u].u;
+      const int f = src / g.S, tok = src - f * g.S;
+      const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok - hp * g.grid_w;
+      float xf[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
+      rotate_run<E>(xf, g, a.tab, c * E, t, hp, wp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
+      const int d0 = c * E;
+      if (d0 < g.DA)
+        *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + slot) * g.DA + d0) = x[u].u;
+      else
+        *reinterpret_cast<uint4*>((T*)R.kb + ((int64_t)h * R.cap + slot) * g.DB + (d0 - g.DA)) = x[u].u;
+      if (h == 0 && c == 0) {
+        R.t[slot] = t;
+        R.g[slot] = a.g0 + src;
+      }
     }
     return;
   }
-  gid -= a.nk;
-  if (gid >= a.nv) return;
-  int si = 0;
-  while (si + 1 < a.nseg && gid >= a.seg[si + 1].v0) ++si;
-  const SegW& sg = a.seg[si];
-  const int64_t w = gid - sg.v0;
-  const int c = (int)(w % CH);
-  const int64_t r = w / CH;
-  const int h = (int)(r % g.H);
-  const int grp = (int)(r / g.H);
-  const int slot0 = (sg.vg0 + grp) * 8;
-  const RegionPtrs& R = a.reg[sg.region];
+  b -= a.nkb;
+  const SegW sg = pick_seg_v<T>(a, b);
+  const RegionPtrs R = sg.region == 0 ? a.reg[0] : a.reg[1];
+  const int local = b - sg.vb0;
+  const int nhb = (g.H + HPB - 1) / HPB;
+  const int hb = local % nhb;
+  const int tile = local / nhb + sg.dst / kTile;
+  const int grp = tid & 7;
+  const int c = (tid >> 3) % CH;
+  const int h = hb * HPB + tid / (8 * CH);
+  if (h >= g.H) return;
+  const int slot0 = tile * kTile + grp * 8;
   Vec16<T> rows[8];
   bool full = true;
-  bool valid[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int slot = slot0 + j;
-    valid[j] = slot >= sg.dst && slot < sg.dst + sg.n;
-    full = full && valid[j];
-    if (valid[j]) {
+    const bool ok = slot >= sg.dst && slot < sg.dst + sg.n;
+    full = full && ok;
+    if (ok) {
       const int src = sg.src + (slot - sg.dst);
       rows[j].u =
           *reinterpret_cast<const uint4*>((const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
-      if (src >= a.bank_lo && src < a.bank_hi)
-        *reinterpret_cast<uint4*>((T*)a.bank_v + ((int64_t)h * a.bank_tok + (a.g0 + src)) * g.D + c * E) =
-            rows[j].u;
     } else {
       rows[j].u = make_uint4(0, 0, 0, 0);
     }
   }
-  T* vb = (T*)R.v + v_index(h, R.cap, g.D, slot0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int slot = slot0 + j;
+    const int src = sg.src + (slot - sg.dst);
+    if (slot >= sg.dst && slot < sg.dst + sg.n && src >= a.bank_lo && src < a.bank_hi)
+      *reinterpret_cast<uint4*>((T*)a.bank_v + ((int64_t)h * a.bank_tok + (a.g0 + src)) * D + c * E) = rows[j].u;
+  }
+  T* vb = (T*)R.v + v_index(h, R.cap, D, slot0, 0);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     T* dst = vb + (size_t)(c * E + e) * kTile;
@@ -127,39 +169,70 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       for (int q = 0; q < (int)(sizeof(T) * 8 / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = o.u[q];
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (valid[j]) dst[j] = rows[j].e[e];
+      for (int j = 0; j < 8; ++j) {
+        const int slot = slot0 + j;
+        if (slot >= sg.dst && slot < sg.dst + sg.n) dst[j] = rows[j].e[e];
+      }
     }
   }
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  const int64_t total = a.nk + a.nv;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (a.geo.esz == 2)
-    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+// Blocks of the append grid for one segment list (host and kernel agree on
+// these counts through the same constants).
+template <typename T, int D>
+static void append_blocks(AppendArgs& a) {
+  constexpr int CH = D / Elem<T>::E;
+  constexpr int TPB = (256 / CH) * 4;
+  constexpr int HPB = 256 / (8 * CH);
+  int kb = 0, vb = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    SegW& s = a.seg[i];
+    s.kb0 = kb;
+    s.vb0 = vb;
+    kb += ((s.n + TPB - 1) / TPB) * a.geo.H;
+    const int t0 = s.dst / kTile, t1 = (s.dst + s.n - 1) / kTile;
+    vb += (t1 - t0 + 1) * ((a.geo.H + HPB - 1) / HPB);
+  }
+  a.nkb = kb;
+  a.nvb = vb;
+}
+
+template <typename T, int D>
+static hipError_t append_launch(AppendArgs a, hipStream_t s) {
+  append_blocks<T, D>(a);
+  const int blocks = a.nkb + a.nvb;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.nseg == 0) return hipSuccess;
+  if (a.geo.esz == 2) return a.geo.D == 128 ? append_launch<uint16_t, 128>(a, s) : append_launch<uint16_t, 64>(a, s);
+  return a.geo.D == 128 ? append_launch<float, 128>(a, s) : append_launch<float, 64>(a, s);
+}
+
 // ----------------------------------------------------------------------------
-// retime: each block owns up to 32 consecutive slots of one physical range,
-// reads their times, rotates the time band of every head's key by the slot's
-// actual change (t' - t) and finally writes t'.  Only the KA plane chunks that
-// hold time dims are touched.
-template <typename T>
+// retime: a block owns 32 consecutive slots of one physical range; it reads
+// their times, rotates the time band of every head's key by the slot's
+// actual change (t' - t) and finally writes t'.  Each wave walks one head's
+// 32 contiguous KA rows as a flat run of 16-byte chunks (fully coalesced),
+// two heads at a time so six or more chunks are in flight per lane.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
   constexpr int E = Elem<T>::E;
+  constexpr int DT = D - 4 * (D / 6);           // time band width
+  constexpr int CAM = (DT + E - 1) / E;         // chunks per KA row
+  constexpr int U = (32 * CAM + 63) / 64;       // chunks per lane per head
   const Geo& g = a.geo;
   const int b = blockIdx.x;
-  int ri = 0;
-  while (ri + 1 < a.nrng && b >= a.rng[ri + 1].blk0) ++ri;
-  const RangeW& rg = a.rng[ri];
+  RangeW rg = a.rng[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (i < a.nrng && b >= a.rng[i].blk0) rg = a.rng[i];
   const int s0 = rg.lo + (b - rg.blk0) * 32;
   const int ns = min(32, rg.lo + rg.n - s0);
-  const RegionPtrs& R = a.reg[rg.region];
+  const RegionPtrs R = rg.region == 0 ? a.reg[0] : a.reg[1];
   __shared__ int s_dl[32];
   __shared__ int s_tn[32];
   const int tid = threadIdx.x;
@@ -170,31 +243,50 @@ __global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
     s_tn[tid] = tn;
   }
   __syncthreads();
-  const int CHA = (g.dt + E - 1) / E;
-  const int total = g.H * ns * CHA;
-  for (int w = tid; w < total; w += 256) {
-    const int c = w % CHA;
-    const int rr = w / CHA;
-    const int j = rr % ns;
-    const int h = rr / ns;
-    T* p = (T*)R.ka + ((int64_t)h * R.cap + s0 + j) * g.DA + c * E;
-    Vec16<T> x;
-    x.u = *reinterpret_cast<const uint4*>(p);
-    float xf[E];
+  const int CA = g.DA / E;                  // chunks per KA row
+  const int nch = ns * CA;                  // chunks per head in this block
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int h0 = wave; h0 < g.H; h0 += 8) {
+    // two heads per pass: h0 and h0 + 4
+    Vec16<T> x[2][U];
+    int idx[2][U];
 #pragma unroll
-    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
-    const int dl = s_dl[j];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = h0 + 4 * hh;
 #pragma unroll
-    for (int q = 0; q < E / 2; ++q) {
-      const int d = c * E + 2 * q;
-      if (d < g.dt) {
-        const float* cs = a.tab.tcs + ((size_t)(dl + a.tab.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
-        rot_pair(xf[2 * q], xf[2 * q + 1], cs[0], cs[1]);
+      for (int u = 0; u < U; ++u) {
+        const int f = lane + 64 * u;
+        idx[hh][u] = (h < g.H && f < nch) ? f : -1;
+        if (idx[hh][u] >= 0)
+          x[hh][u].u = *reinterpret_cast<const uint4*>((const T*)R.ka + ((int64_t)h * R.cap + s0) * g.DA + f * E);
       }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) x.e[e] = Elem<T>::st(xf[e]);
-    *reinterpret_cast<uint4*>(p) = x.u;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = h0 + 4 * hh;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = idx[hh][u];
+        if (f < 0) continue;
+        const int j = f / CA;
+        const int c = f - j * CA;
+        const int dl = s_dl[j];
+        float xf[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[hh][u].e[e]);
+#pragma unroll
+        for (int q = 0; q < E / 2; ++q) {
+          const int d = c * E + 2 * q;
+          if (d < g.dt) {
+            const float* cs = a.tab.tcs + ((size_t)(dl + a.tab.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
+            rot_pair(xf[2 * q], xf[2 * q + 1], cs[0], cs[1]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[hh][u].e[e] = Elem<T>::st(xf[e]);
+        *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + s0) * g.DA + f * E) = x[hh][u].u;
+      }
+    }
   }
   __syncthreads();
   if (tid < ns) R.t[s0 + tid] = s_tn[tid];
@@ -202,10 +294,17 @@ __global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
 
 hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
-  if (a.geo.esz == 2)
-    hipLaunchKernelGGL(retime_kernel<uint16_t>, dim3(nblocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(retime_kernel<float>, dim3(nblocks), dim3(256), 0, s, a);
+  if (a.geo.esz == 2) {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), dim3(nblocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), dim3(nblocks), dim3(256), 0, s, a);
+  } else {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((retime_kernel<float, 128>), dim3(nblocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((retime_kernel<float, 64>), dim3(nblocks), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
