@@ -121,40 +121,6 @@ __device__ __forceinline__ void tile_store(const TileRegs& tr, u32x4_t* lk, u32x
   }
 }
 
-// Direct-to-LDS loads (global_load_lds_dwordx4): lane `lane` of wave `wave`
-// fetches the chunk that belongs at LDS position blk*64 + lane.
-__device__ __forceinline__ void dma_k(const KeyRegions& kr, int h, int rg, int base, u32x4_t* lk, int tid) {
-  const uint16_t* ka = (const uint16_t*)(rg == 0 ? kr.ka[0] : kr.ka[1]);
-  const uint16_t* kb = (const uint16_t*)(rg == 0 ? kr.kb[0] : kr.kb[1]);
-  const int cap = rg == 0 ? kr.cap[0] : kr.cap[1];
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = i * 4 + wave;
-    const int p = blk * 64 + lane;
-    const int row = p >> 4, c = (p & 15) ^ kswz(row);
-    const int64_t slot = (int64_t)h * cap + base + row;
-    const uint16_t* src = c < 6 ? ka + slot * kDA + c * 8 : kb + slot * kDB + (c - 6) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lk + blk * 64), 16,
-                                     0, 0);
-  }
-}
-
-__device__ __forceinline__ void dma_v(const KeyRegions& kr, int h, int rg, int base, u32x4_t* lv, int tid) {
-  const uint16_t* vv = (const uint16_t*)(rg == 0 ? kr.v[0] : kr.v[1]);
-  const int cap = rg == 0 ? kr.cap[0] : kr.cap[1];
-  const uint16_t* vt = vv + ((int64_t)h * (cap / kTile) + base / kTile) * kVTile;
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = i * 4 + wave;
-    const int p = blk * 64 + lane;
-    const int d = p >> 3, c = (p & 7) ^ vswz(d);
-    __builtin_amdgcn_global_load_lds((const void*)(vt + d * 64 + c * 8),
-                                     (__attribute__((address_space(3))) void*)(lv + blk * 64), 16, 0, 0);
-  }
-}
-
 // Rotate this lane's 64 query elements (row qc, halves hl) and pack them as the
 // eight B operands of S^T = K . Q^T.
 __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, int h, int qc, int hl) {
@@ -283,7 +249,8 @@ struct TileSeq {
 };
 
 // ---------------------------------------------------------------------------
-// Main kernel: register-staged prefetch of tile t+1 while tile t is computed.
+// Simple kernel: register-staged prefetch of tile t+1 while tile t is computed
+// (XOR-swizzled LDS, no cross-tile pipelining).
 __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                              int ntile0, int ntiles) {
   __shared__ u32x4_t lks[2][kBN * kKCh];
@@ -332,14 +299,93 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a, int m
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined variant: while the softmax of tile t runs on the VALU,
-// the matrix cores already compute S^T(t+1); then O^T += V^T(t) P^T(t).  K
-// tiles run one tile ahead of V tiles, each double buffered (same 64 KB of
-// LDS), filled with direct-to-LDS loads.
-__global__ __launch_bounds__(256, 2) void attend_pipe_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                             int ntile0, int ntiles) {
-  __shared__ u32x4_t lks[2][kBN * kKCh];
-  __shared__ u32x4_t lvs[2][128 * kVCh];
+// Interleaved pipeline (v3).  LDS rows are padded by one 16-byte chunk (K rows
+// 272 B, V^T rows 144 B) instead of XOR-swizzled, so every operand read is a
+// per-lane base plus an immediate offset, and any 16 consecutive lanes still
+// hit 16 distinct 16-byte bank slots.  Iteration t issues the global loads of
+// K(t+2) and V(t+1), then computes S^T(t+1) on the matrix cores interleaved
+// instruction by instruction (sched_group_barrier) with the softmax of tile t
+// on the VALU; the rare O rescale and the P.V product of tile t follow.
+constexpr int kKSt = 17;                       // K row stride in 16-byte chunks
+constexpr int kVSt = 9;                        // V^T row stride in 16-byte chunks
+constexpr int kKTileP = kBN * kKSt;            // padded K tile, 16-byte chunks
+constexpr int kVTileP = 128 * kVSt;            // padded V^T tile
+
+__device__ __forceinline__ void tile_store_padded(const TileRegs& tr, u32x4_t* lk, u32x4_t* lv, int tid) {
+  const int c = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lk[((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + 256 * i;
+    lv[(ci >> 3) * kVSt + (ci & 7)] = tr.v[i];
+  }
+}
+
+// S^T for one tile into s, with the softmax of the previous tile (sp) woven in:
+// returns P(previous) packed in pb, the tile's row-sum in psum and the scale
+// factor alpha for O (1 unless the running max moved).  Scheduling groups ask
+// the compiler to emit, per MFMA, one LDS operand read, two exp2 and a few VALU
+// operations (FMA, bf16 pack, dot2 sum), so the softmax runs on the VALU while
+// the matrix core is busy.
+__device__ __forceinline__ void qk_and_softmax(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int kbase,
+                                               const f32x16_t* sp, float& m, float c2, bf16x8_t pb[2][2],
+                                               float& psum, float& alpha, bool& upd) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+  float mt = sp[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sp[kb][i]);
+  mt = xhalf_max(mt) * c2;
+  upd = mt > m + 8.f;
+  const float mn = upd ? mt : m;
+  alpha = exp2f(m - mn);
+  m = mn;
+  const float negm = -m;
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  psum = 0.f;
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    const int kb = step >> 3, ks = step & 7;
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
+    const int e = step * 2;
+    const int pkb = e >> 4, phf = (e >> 3) & 1, pj = e & 7;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj], c2, negm));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj + 1], c2, negm));
+    const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+    pb[pkb][phf][pj] = pr[0];
+    pb[pkb][phf][pj + 1] = pr[1];
+    psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // first two operand reads
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next operand read
+    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // exp2 x2
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // FMA, pack, dot2
+  }
+}
+
+__device__ __forceinline__ void pv_padded(f32x16_t* o, const u32x4_t* lv, int vbase, bf16x8_t pb[2][2]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lv[vbase + db * 32 * kVSt + ks * 2]);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks >> 1][ks & 1], o[db], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
+                                                           int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kKTileP];
+  __shared__ u32x4_t lvs[2][kVTileP];
   const int wg = blockIdx.x;
   const int lin = (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
@@ -349,6 +395,8 @@ __global__ __launch_bounds__(256, 2) void attend_pipe_kernel(AttendArgs a, int m
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * kBM + wave * 32 + l32;
   const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const int kbase = perm_row(l32) * kKSt + hl;
+  const int vbase = l32 * kVSt + hl;
 
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
@@ -360,38 +408,76 @@ __global__ __launch_bounds__(256, 2) void attend_pipe_kernel(AttendArgs a, int m
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
   const float c2 = a.scale * 1.4426950408889634f;
+  const int last = ntiles - 1;
 
-  dma_k(a.keys, h, ts.region(0), ts.base(0), lks[0], tid);
-  dma_v(a.keys, h, ts.region(0), ts.base(0), lvs[0], tid);
-  if (ntiles > 1) dma_k(a.keys, h, ts.region(1), ts.base(1), lks[1], tid);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16_t sc[2];
-  qk_tile(sc, lks[0], qf, l32, hl);
-  mask_tile(sc, ts.valid(0), hl);
-
-  for (int it = 0; it < ntiles; ++it) {
-    const bool has1 = it + 1 < ntiles;
-    const bool has2 = it + 2 < ntiles;
-    if (has2) dma_k(a.keys, h, ts.region(it + 2), ts.base(it + 2), lks[it & 1], tid);
-    if (has1) dma_v(a.keys, h, ts.region(it + 1), ts.base(it + 1), lvs[(it + 1) & 1], tid);
-    f32x16_t sn[2];
-    if (has1) qk_tile(sn, lks[(it + 1) & 1], qf, l32, hl);
-    bf16x8_t pb[2][2];
-    softmax_tile(sc, o, m, lsum, c2, pb);
-    pv_tile(o, lvs[it & 1], pb, l32, hl);
-    if (has1) mask_tile(sn, ts.valid(it + 1), hl);
-    if (has1) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (has1) {
-      sc[0] = sn[0];
-      sc[1] = sn[1];
-    }
+  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+  TileRegs tr;
+  // K(0), V(0) -> buffer 0; K(1) -> buffer 1
+  tile_load(tr, tp, 0, 0);
+  tile_store_padded(tr, lks[0], lvs[0], tid);
+  {
+    const int t1 = min(1, last);
+    tile_load(tr, tp, ts.region(t1), ts.base(t1));
+    const int c = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lks[1][((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
   }
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  {
+    // S^T(0) alone
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kKSt + ks * 2]);
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
+      }
+    }
+    mask_tile(sa, ts.valid(0), hl);
+  }
+
+  // one pipeline step: scur holds S^T(t); computes S^T(t+1) into snext
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
+    const int tk = min(t + 2, last), tv = min(t + 1, last);
+    // K(t+2) and V(t+1) in flight (clamped at the last tile: harmless re-loads)
+    {
+      const uint16_t* kp = (ts.region(tk) == 0 ? tp.k[0] : tp.k[1]) + ts.base(tk) * tp.kstride;
+      const uint16_t* vp = (ts.region(tv) == 0 ? tp.v[0] : tp.v[1]) + (ts.base(tv) / kTile) * kVTile;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * tp.kstride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tr.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 2048 * i);
+    }
+    bf16x8_t pb[2][2];
+    float psum, alpha;
+    bool upd;
+    qk_and_softmax(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
+    if (__ballot(upd) != 0) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+    lsum = lsum * alpha + psum;
+    pv_padded(o, lvs[t & 1], vbase, pb);
+    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    tile_store_padded(tr, lks[t & 1], lvs[(t + 1) & 1], tid);
+    __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < ntiles) step(t, sa, sb);
   store_out(a, o, lsum, qrow, h, hl);
 }
 
-template <bool PIPE>
+template <int VAR>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int mblocks = (a.Lq + kBM - 1) / kBM;
   const int total = mblocks * a.geo.H;
@@ -412,17 +498,18 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     n0 = ntile1;
     nt = ntile1;
   }
-  if (PIPE)
-    hipLaunchKernelGGL(attend_pipe_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
-  else
+  if (VAR == 1)
     hipLaunchKernelGGL(attend_mfma_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
+  else
+    hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
   return hipGetLastError();
 }
 
+// KVC_ATTEND_VARIANT=simple selects the non-pipelined kernel (A/B timing).
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
-  if (v && std::string(v) == "p") return attend_launch<true>(a, s);
-  return attend_launch<false>(a, s);
+  if (v && std::string(v) == "simple") return attend_launch<1>(a, s);
+  return attend_launch<0>(a, s);
 }
 
 }  // namespace kvc
