@@ -107,11 +107,12 @@ def main():
     app_avg = float(np.mean(app_ms))
     assert cache.info()["n_valid"] == 28080
 
-    # ---- retime over the whole cache (time band only), MALL flushed between samples
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # ---- retime over the whole cache (time band only), MALL flushed between samples by reading
+    # 1 GiB of unrelated data (a read leaves no dirty lines to write back inside the timed kernel)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     ret_ms = []
     for i in range(12):
-        flush.fill_(i & 0xFF)
+        flush.sum()
         a, b = ev(), ev()
         a.record(stream)
         cache.retime(1 if i % 2 == 0 else -1)
@@ -123,7 +124,7 @@ def main():
     # append with the MALL flushed as well (the step loop above runs warm)
     app_cold = []
     for i in range(8):
-        flush.fill_(i & 0xFF)
+        flush.sum()
         a, b = ev(), ev()
         q, k, v = pool[i % 4]
         a.record(stream)
