@@ -362,13 +362,19 @@ __device__ __forceinline__ void qk_and_softmax(f32x16_t* s, const u32x4_t* lk, c
     pb[pkb][phf][pj + 1] = pr[1];
     psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // first two operand reads
+  // keep the softmax in this block: without these uses the compiler sinks the
+  // exp2s past the caller's rescale branch, away from the MFMAs they should hide
+  asm volatile("" ::"v"(psum));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[kb][hf])));
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // first operand reads (lookahead)
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next operand read
-    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // exp2 x2
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // FMA, pack, dot2
+    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // exp2 x2 (the other VALU work follows its inputs)
   }
 }
 
@@ -380,6 +386,13 @@ __device__ __forceinline__ void pv_padded(f32x16_t* o, const u32x4_t* lv, int vb
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lv[vbase + db * 32 * kVSt + ks * 2]);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks >> 1][ks & 1], o[db], 0, 0, 0);
     }
+  // keep several V^T operand reads in flight ahead of the MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
@@ -477,9 +490,123 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
   store_out(a, o, lsum, qrow, h, hl);
 }
 
+// ---------------------------------------------------------------------------
+// v5: v3's interleaved pipeline with 8 waves (256 query rows) per workgroup.
+// A 32 KB K+V^T tile is then 16 staging registers per thread instead of 32,
+// which leaves the compiler room to keep LDS operand reads in flight; every
+// tile loaded to LDS also feeds twice as many query rows (half the L2 traffic
+// per query).  Padded LDS rows, double buffered (70 KB), one block per CU.
+struct Stage5 {
+  u32x4_t k[2];
+  u32x4_t v[2];
+};
+
+__device__ __forceinline__ void load5(Stage5& st, const TilePtrs& p, int rk, int bk, int rv, int bv) {
+  const uint16_t* kp = (rk == 0 ? p.k[0] : p.k[1]) + bk * p.kstride;
+  const uint16_t* vp = (rv == 0 ? p.v[0] : p.v[1]) + (bv / kTile) * kVTile;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) st.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 32 * i * p.kstride);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) st.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 4096 * i);
+}
+
+__device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* lv, int tid, bool k, bool v) {
+  const int c = tid & 15;
+  if (k) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lk[((tid >> 4) + 32 * i) * kKSt + c] = st.k[i];
+  }
+  if (v) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 512 * i;
+      lv[(ci >> 3) * kVSt + (ci & 7)] = st.v[i];
+    }
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
+                                                           int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kKTileP];
+  __shared__ u32x4_t lvs[2][kVTileP];
+  const int wg = blockIdx.x;
+  const int lin = (wg & 7) * per_xcd + (wg >> 3);
+  if (lin >= total) return;
+  const int h = lin / mblocks;
+  const int mb = lin - h * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * 256 + wave * 32 + l32;
+  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const int kbase = perm_row(l32) * kKSt + hl;
+  const int vbase = l32 * kVSt + hl;
+  const int last = ntiles - 1;
+  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+
+  Stage5 st;
+  load5(st, tp, 0, 0, 0, 0);
+  bf16x8_t qf[8];
+  load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
+  store5(st, lks[0], lvs[0], tid, true, true);
+  {
+    const int t1 = min(1, last);
+    load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+    store5(st, lks[1], lvs[1], tid, true, false);
+  }
+  f32x16_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  const float c2 = a.scale * 1.4426950408889634f;
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kKSt + ks * 2]);
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
+    }
+  }
+  mask_tile(sa, ts.valid(0), hl);
+
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
+    const int tk = min(t + 2, last), tv = min(t + 1, last);
+    load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    bf16x8_t pb[2][2];
+    float psum, alpha;
+    bool upd;
+    qk_and_softmax(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
+    if (__ballot(upd) != 0) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+    lsum = lsum * alpha + psum;
+    pv_padded(o, lvs[t & 1], vbase, pb);
+    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < ntiles) step(t, sa, sb);
+  store_out(a, o, lsum, qrow, h, hl);
+}
+
 template <int VAR>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int mblocks = (a.Lq + kBM - 1) / kBM;
+  const int bm = VAR == 2 ? 256 : kBM;
+  const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
   const int ntile0 = (a.keys.n[0] + kBN - 1) / kBN;
@@ -500,16 +627,20 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   }
   if (VAR == 1)
     hipLaunchKernelGGL(attend_mfma_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
+  else if (VAR == 2)
+    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
   return hipGetLastError();
 }
 
-// KVC_ATTEND_VARIANT=simple selects the non-pipelined kernel (A/B timing).
+// The 8-wave pipelined kernel is the default; KVC_ATTEND_VARIANT=v3 (4-wave pipeline) or
+// =simple (no pipeline) selects an older kernel for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
   if (v && std::string(v) == "simple") return attend_launch<1>(a, s);
-  return attend_launch<0>(a, s);
+  if (v && std::string(v) == "v3") return attend_launch<0>(a, s);
+  return attend_launch<2>(a, s);
 }
 
 }  // namespace kvc
