@@ -32,7 +32,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
+    p.add_argument("--no-context", action="store_true", help="skip the vendor-library reference timings")
+    p.add_argument("--cpu-rows", type=int, default=3840, help="query rows of the oracle sample (about 10 s of host BLAS)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_attend_c3.json"))
     return p.parse_args()
 
@@ -148,6 +149,7 @@ def main():
         cp_ms.append(a.elapsed_time(b))
     copy_gbps = 2.0 * (1 << 30) / (float(np.median(cp_ms)) * 1e-3) / 1e9
     del flush, cx, cy
+    context = None if args.no_context else vendor_context(dev, stream, H, N, Lk, D)
 
     dt = D - 4 * (D // 6)
     app_bytes = 4.0 * N * H * D * 2
@@ -200,9 +202,48 @@ def main():
             "hbm_copy_GBps_measured": round(copy_gbps, 1),
         },
     }
+    if context:
+        res["context"] = context
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_rows, w, cache)
     print(json.dumps(res), flush=True)
+
+
+def vendor_context(dev, stream, H, N, Lk, D):
+    """Reference points on the same board (not the product path): torch's fused attention at the same
+    shape (same flop count, no cache or RoPE), and a plain bf16 GEMM through torch (hipBLASLt)."""
+    import numpy as np
+    import torch
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    out = {}
+    try:
+        from torch.nn.attention import sdpa_kernel, SDPBackend
+        q = torch.randn(1, H, N, D, device=dev, dtype=torch.bfloat16)
+        k = torch.randn(1, H, Lk, D, device=dev, dtype=torch.bfloat16)
+        v = torch.randn(1, H, Lk, D, device=dev, dtype=torch.bfloat16)
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
+        out["torch_sdpa_flash_tflops"] = round(4.0 * H * N * Lk * D / (ms * 1e-3) / 1e12, 1)
+        del q, k, v
+    except Exception as e:  # backend not available in this build
+        out["torch_sdpa_flash_error"] = str(e)[:120]
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    ms = timed(lambda: torch.mm(a, b))
+    out["torch_gemm_bf16_8192_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    return out
 
 
 def cpu_baseline(rows, w, cache):

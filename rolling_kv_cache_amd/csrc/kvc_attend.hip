@@ -6,8 +6,10 @@
 // which already holds the new block).
 //
 // Design (bf16 inputs, fp32 accumulation, head_dim 128):
-//  * workgroup = 4 waves x 32 query rows; key tiles of 64 slots staged in LDS
-//    (16 KB K + 16 KB V^T), double buffered, one barrier per tile;
+//  * workgroup = 8 waves x 32 query rows (one per CU, two waves per SIMD); key
+//    tiles of 64 slots staged in LDS (K + V^T, 35 KB with row padding), double
+//    buffered, one barrier per tile; a 4-wave variant with two workgroups per
+//    CU is kept for comparison (KVC_ATTEND_VARIANT=v3);
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16, so every lane owns one query
 //    row: the row max needs one exchange between the wave's halves
 //    (v_permlane32_swap), the row sum none;
@@ -16,9 +18,12 @@
 //    registers exactly the B operand of O^T = V^T . P^T: P goes from fp32
 //    registers to packed bf16 and straight into the second MFMA;
 //  * V^T comes from the cache already tile-transposed, so both LDS operand
-//    reads are single 16-byte loads.  The XOR swizzles make every group of 16
-//    consecutive lanes touch 16 distinct 16-byte bank slots (and every group of
-//    8 lanes 8 distinct slots), for reads and for the tile stores;
+//    reads are single 16-byte loads.  LDS rows are padded by one 16-byte chunk
+//    (K rows 272 B, V^T rows 144 B): every operand read is a per-lane base plus
+//    an immediate, and any 16 consecutive lanes hit 16 distinct bank groups;
+//  * the softmax of tile t is interleaved instruction by instruction with the
+//    QK^T MFMAs of tile t+1 (sched_group_barrier), and four LDS operand reads
+//    stay in flight ahead of every MFMA;
 //  * online softmax in the log2 domain (exp2 with log2(e)/sqrt(D) folded into
 //    one FMA); the running max only moves when a tile's max exceeds it by more
 //    than 8 (log2 units), so the O rescale is skipped on almost every tile; the
@@ -48,17 +53,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;                       // queries per workgroup
 constexpr int kBN = 64;                        // keys per tile
-constexpr int kKCh = 16;                       // 16-byte chunks per K row
-constexpr int kVCh = 8;                        // 16-byte chunks per V^T row
 constexpr int kDA = 48, kDB = 80;              // key plane widths for head_dim 128
 constexpr int kVTile = 128 * kTile;            // elements of one V^T tile
 
 // swap bits 2 and 3 of a row index inside a 32-row block
 __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-// K tile: chunk c of row r is stored at chunk c ^ kswz(r)
-__device__ __forceinline__ int kswz(int row) { return perm_row(row & 31) & 15; }
-// V^T tile (128-byte rows): chunk c of row d is stored at chunk c ^ vswz(d)
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
 // exchange with the lane 32 apart: {own, partner} in some order
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -106,21 +105,6 @@ __device__ __forceinline__ void tile_load(TileRegs& tr, const TilePtrs& p, int r
   for (int i = 0; i < 4; ++i) tr.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 2048 * i);
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& tr, u32x4_t* lk, u32x4_t* lv, int tid) {
-  const int c = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    lk[row * kKCh + (c ^ kswz(row))] = tr.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ci = tid + 256 * i;
-    const int d = ci >> 3, cv = ci & 7;
-    lv[d * kVCh + (cv ^ vswz(d))] = tr.v[i];
-  }
-}
-
 // Rotate this lane's 64 query elements (row qc, halves hl) and pack them as the
 // eight B operands of S^T = K . Q^T.
 __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, int h, int qc, int hl) {
@@ -148,20 +132,6 @@ __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, in
   }
 }
 
-__device__ __forceinline__ void qk_tile(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int l32, int hl) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    const int row = kb * 32 + perm_row(l32);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[row * kKCh + ((ks * 2 + hl) ^ (l32 & 15))]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
-    }
-  }
-}
-
 __device__ __forceinline__ void mask_tile(f32x16_t* s, int nv, int hl) {
   if (nv >= kBN) return;
 #pragma unroll
@@ -171,55 +141,6 @@ __device__ __forceinline__ void mask_tile(f32x16_t* s, int nv, int hl) {
       const int key = kb * 32 + perm_row((i >> 2) * 8 + hl * 4 + (i & 3));
       if (key >= nv) s[kb][i] = -INFINITY;
     }
-}
-
-// Online softmax of one tile in the log2 domain; returns P packed to bf16 as
-// the four B operands of O^T += V^T . P^T.
-__device__ __forceinline__ void softmax_tile(const f32x16_t* s, f32x16_t* o, float& m, float& lsum, float c2,
-                                             bf16x8_t pb[2][2]) {
-  float mt = s[0][0];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-  mt = xhalf_max(mt) * c2;
-  const bool upd = mt > m + 8.f;
-  if (__ballot(upd) != 0) {
-    const float mn = upd ? mt : m;
-    const float alpha = upd ? exp2f(m - mn) : 1.f;
-    m = mn;
-    lsum *= alpha;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-  }
-  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[kb][hf][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][hf * 8 + j], c2, -m));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2_t pr = {pb[kb][hf][2 * j], pb[kb][hf][2 * j + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
-      }
-    }
-}
-
-__device__ __forceinline__ void pv_tile(f32x16_t* o, const u32x4_t* lv, bf16x8_t pb[2][2], int l32, int hl) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = db * 32 + l32;
-    const int sw = vswz(d);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lv[d * kVCh + ((ks * 2 + hl) ^ sw)]);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks >> 1][ks & 1], o[db], 0, 0, 0);
-    }
-  }
 }
 
 __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o, float lsum, int qrow, int h, int hl) {
@@ -247,56 +168,6 @@ struct TileSeq {
   __device__ __forceinline__ int base(int it) const { return (it < ntile0 ? it : it - ntile0) * kBN; }
   __device__ __forceinline__ int valid(int it) const { return (it < ntile0 ? n0 : n1) - base(it); }
 };
-
-// ---------------------------------------------------------------------------
-// Simple kernel: register-staged prefetch of tile t+1 while tile t is computed
-// (XOR-swizzled LDS, no cross-tile pipelining).
-__global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                             int ntile0, int ntiles) {
-  __shared__ u32x4_t lks[2][kBN * kKCh];
-  __shared__ u32x4_t lvs[2][128 * kVCh];
-  const int wg = blockIdx.x;
-  const int lin = (wg & 7) * per_xcd + (wg >> 3);
-  if (lin >= total) return;
-  const int h = lin / mblocks;
-  const int mb = lin - h * mblocks;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int qrow = mb * kBM + wave * 32 + l32;
-  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
-
-  bf16x8_t qf[8];
-  load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
-  const float c2 = a.scale * 1.4426950408889634f;
-
-  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
-  TileRegs tr;
-  tile_load(tr, tp, 0, 0);
-  tile_store(tr, lks[0], lvs[0], tid);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) tile_load(tr, tp, ts.region(it + 1), ts.base(it + 1));
-    f32x16_t s[2];
-    qk_tile(s, lks[buf], qf, l32, hl);
-    mask_tile(s, ts.valid(it), hl);
-    bf16x8_t pb[2][2];
-    softmax_tile(s, o, m, lsum, c2, pb);
-    pv_tile(o, lvs[buf], pb, l32, hl);
-    if (has_next) tile_store(tr, lks[buf ^ 1], lvs[buf ^ 1], tid);
-    __syncthreads();
-  }
-  store_out(a, o, lsum, qrow, h, hl);
-}
 
 // ---------------------------------------------------------------------------
 // Interleaved pipeline (v3).  LDS rows are padded by one 16-byte chunk (K rows
@@ -625,20 +496,17 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     n0 = ntile1;
     nt = ntile1;
   }
-  if (VAR == 1)
-    hipLaunchKernelGGL(attend_mfma_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
-  else if (VAR == 2)
+  if (VAR == 2)
     hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
   return hipGetLastError();
 }
 
-// The 8-wave pipelined kernel is the default; KVC_ATTEND_VARIANT=v3 (4-wave pipeline) or
-// =simple (no pipeline) selects an older kernel for A/B timing.
+// The 8-wave kernel is the default; KVC_ATTEND_VARIANT=v3 selects the 4-wave
+// variant (two workgroups per CU) for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
-  if (v && std::string(v) == "simple") return attend_launch<1>(a, s);
   if (v && std::string(v) == "v3") return attend_launch<0>(a, s);
   return attend_launch<2>(a, s);
 }

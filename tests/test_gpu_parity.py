@@ -140,6 +140,30 @@ def test_uniform_retime_keeps_attention():
     check_attention(b, a, "uniform retime")
 
 
+@pytest.mark.parametrize("variant", ["", "v3"])
+def test_attend_score_jump(variant):
+    """Keys of the oldest frames are tiny and a later chunk's keys and queries are 4x N(0,1): the later
+    scores exceed every score of the first key tile by about 48 to 90 in exp2 units, so the kernels must
+    raise their running maximum mid-row and rescale O (without it P overflows to inf)."""
+    w = Workload("jump", 207, 2, 128, "bf16", 9, 23, 1, 6, (2,) * 4)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(3):
+        q, k, v = chunk_inputs(w, i, frames=2)
+        f = 4.0 if i == 2 else 1.0 / 64
+        k = (k * f).astype(np.float32)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    q = (q * 4.0).astype(np.float32)
+    if variant:
+        os.environ["KVC_ATTEND_VARIANT"] = variant
+    try:
+        out = gc.attend(dev(q, w), 4).float().cpu().numpy()
+    finally:
+        os.environ.pop("KVC_ATTEND_VARIANT", None)
+    check_attention(out, oc.attend(q, 2, 4), f"score jump {variant or 'default'}")
+
+
 # ---------------------------------------------------------------- edge and error paths
 def test_error_paths_leave_state_unchanged():
     from rolling_kv_cache_amd import KVCError
