@@ -215,15 +215,24 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
 // ----------------------------------------------------------------------------
 // retime: a block owns 32 consecutive slots of one physical range; it reads
 // their times, rotates the time band of every head's key by the slot's
-// actual change (t' - t) and finally writes t'.  Each wave walks one head's
-// 32 contiguous KA rows as a flat run of 16-byte chunks (fully coalesced),
-// two heads at a time so six or more chunks are in flight per lane.
+// actual change (t' - t) and finally writes t'.  Thread p owns chunk p % CA of
+// slot p / CA for every head: its (cos, sin) pairs depend only on the slot's
+// change and the chunk, so they are read from the table once and reused for
+// all heads, and for each head the block's threads cover the 32 contiguous KA
+// rows as one run of 16-byte chunks (fully coalesced).  Heads go eight at a
+// time, so eight chunks are in flight per thread.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
-  constexpr int E = Elem<T>::E;
-  constexpr int DT = D - 4 * (D / 6);           // time band width
-  constexpr int CAM = (DT + E - 1) / E;         // chunks per KA row
-  constexpr int U = (32 * CAM + 63) / 64;       // chunks per lane per head
+struct RetimeShape {
+  static constexpr int E = Elem<T>::E;
+  static constexpr int DT = D - 4 * (D / 6);            // time band width
+  static constexpr int CA = (DT + E - 1) / E;           // chunks per KA row (time band, padded)
+  static constexpr int THREADS = (32 * CA + 63) / 64 * 64;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(RetimeArgs a) {
+  using Sh = RetimeShape<T, D>;
+  constexpr int E = Sh::E, DT = Sh::DT, CA = Sh::CA, HU = 8;
   const Geo& g = a.geo;
   const int b = blockIdx.x;
   RangeW rg = a.rng[0];
@@ -243,48 +252,36 @@ __global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
     s_tn[tid] = tn;
   }
   __syncthreads();
-  const int CA = g.DA / E;                  // chunks per KA row
-  const int nch = ns * CA;                  // chunks per head in this block
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int h0 = wave; h0 < g.H; h0 += 8) {
-    // two heads per pass: h0 and h0 + 4
-    Vec16<T> x[2][U];
-    int idx[2][U];
+  const int j = tid / CA, c = tid - (tid / CA) * CA;
+  if (j < ns) {
+    // this chunk's rotation, shared by every head
+    float cs[E / 2][2];
+    const float* tp = a.tab.tcs + ((size_t)(s_dl[j] + a.tab.maxpos) * (DT / 2)) * 2;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int h = h0 + 4 * hh;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int f = lane + 64 * u;
-        idx[hh][u] = (h < g.H && f < nch) ? f : -1;
-        if (idx[hh][u] >= 0)
-          x[hh][u].u = *reinterpret_cast<const uint4*>((const T*)R.ka + ((int64_t)h * R.cap + s0) * g.DA + f * E);
-      }
+    for (int q = 0; q < E / 2; ++q) {
+      const int d = c * E + 2 * q;
+      cs[q][0] = d < DT ? tp[d] : 1.f;
+      cs[q][1] = d < DT ? tp[d + 1] : 0.f;
     }
+    T* base = (T*)R.ka + ((int64_t)s0 + j) * (CA * E) + c * E;
+    const int64_t hstride = (int64_t)R.cap * (CA * E);
+    for (int h0 = 0; h0 < g.H; h0 += HU) {
+      Vec16<T> x[HU];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int h = h0 + 4 * hh;
+      for (int u = 0; u < HU; ++u)
+        if (h0 + u < g.H) x[u].u = *reinterpret_cast<const uint4*>(base + (h0 + u) * hstride);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int f = idx[hh][u];
-        if (f < 0) continue;
-        const int j = f / CA;
-        const int c = f - j * CA;
-        const int dl = s_dl[j];
+      for (int u = 0; u < HU; ++u) {
+        if (h0 + u >= g.H) break;
         float xf[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[hh][u].e[e]);
+        for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
 #pragma unroll
-        for (int q = 0; q < E / 2; ++q) {
-          const int d = c * E + 2 * q;
-          if (d < g.dt) {
-            const float* cs = a.tab.tcs + ((size_t)(dl + a.tab.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
-            rot_pair(xf[2 * q], xf[2 * q + 1], cs[0], cs[1]);
-          }
-        }
+        for (int q = 0; q < E / 2; ++q)
+          if (c * E + 2 * q < DT) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[hh][u].e[e] = Elem<T>::st(xf[e]);
-        *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + s0) * g.DA + f * E) = x[hh][u].u;
+        for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
+        *reinterpret_cast<uint4*>(base + (h0 + u) * hstride) = x[u].u;
       }
     }
   }
@@ -296,14 +293,16 @@ hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
   if (a.geo.esz == 2) {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), dim3(nblocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), dim3(nblocks), dim3(RetimeShape<uint16_t, 128>::THREADS), 0,
+                         s, a);
     else
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), dim3(nblocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), dim3(nblocks), dim3(RetimeShape<uint16_t, 64>::THREADS), 0, s,
+                         a);
   } else {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<float, 128>), dim3(nblocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<float, 128>), dim3(nblocks), dim3(RetimeShape<float, 128>::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((retime_kernel<float, 64>), dim3(nblocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<float, 64>), dim3(nblocks), dim3(RetimeShape<float, 64>::THREADS), 0, s, a);
   }
   return hipGetLastError();
 }
