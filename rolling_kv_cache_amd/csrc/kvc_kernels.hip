@@ -64,13 +64,24 @@ __device__ __forceinline__ SegW pick_seg_v(const AppendArgs& a, int b) {
   return sg;
 }
 
+// Key blocks: KTB tokens x up to KHB heads.  Thread (token i, chunk c) owns
+// chunk c of token i for every head of its block: the token's frame, grid
+// position and the chunk's (cos, sin) pairs are computed once and reused for
+// each head, and the heads go eight at a time (eight 16-byte loads in flight).
+constexpr int KHB = 20;                     // heads per key block
+
+template <typename T, int D>
+struct AppendShape {
+  static constexpr int E = Elem<T>::E;
+  static constexpr int CH = D / E;          // 16-byte chunks per row
+  static constexpr int KTB = 256 / CH;      // tokens per key block
+  static constexpr int HPB = 256 / (8 * CH);  // heads per value block
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int E = Elem<T>::E;
-  constexpr int CH = D / E;                 // 16-byte chunks per row
-  constexpr int TL = 256 / CH;              // token lanes per K block
-  constexpr int TPB = TL * 4;               // tokens per K block
-  constexpr int HPB = 256 / (8 * CH);       // heads per V block
+  using Sh = AppendShape<T, D>;
+  constexpr int E = Sh::E, CH = Sh::CH, KTB = Sh::KTB, HPB = Sh::HPB, HU = 8;
   const Geo& g = a.geo;
   const int tid = threadIdx.x;
   int b = blockIdx.x;
@@ -78,45 +89,55 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const SegW sg = pick_seg_k<T>(a, b);
     const RegionPtrs R = sg.region == 0 ? a.reg[0] : a.reg[1];
     const int local = b - sg.kb0;
-    const int h = local % g.H;
-    const int tok0 = (local / g.H) * TPB;
+    const int nhg = (g.H + KHB - 1) / KHB;
+    const int hg = local % nhg;
+    const int i = (local / nhg) * KTB + tid / CH;
     const int c = tid % CH;
-    const int tl = tid / CH;
-    Vec16<T> x[4];
+    if (i >= sg.n) return;
+    const int src = sg.src + i, slot = sg.dst + i;
+    const int f = src / g.S, tok = src - f * g.S;
+    const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok - hp * g.grid_w;
+    const int d0 = c * E;
+    float cs[E / 2][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tok0 + tl + u * TL;
-      if (i < sg.n) {
-        const int src = sg.src + i;
-        x[u].u = *reinterpret_cast<const uint4*>((const T*)a.k + (int64_t)src * a.k_tok + (int64_t)h * a.k_head +
-                                                 c * E);
+    for (int q = 0; q < E / 2; ++q) pair_cs(g, a.tab, d0 + 2 * q, t, hp, wp, cs[q][0], cs[q][1]);
+    const bool bank = src >= a.bank_lo && src < a.bank_hi;
+    const T* sp = (const T*)a.k + (int64_t)src * a.k_tok + d0;
+    T* dp;
+    int64_t dstride;
+    if (d0 < g.DA) {
+      dp = (T*)R.ka + (int64_t)slot * g.DA + d0;
+      dstride = (int64_t)R.cap * g.DA;
+    } else {
+      dp = (T*)R.kb + (int64_t)slot * g.DB + (d0 - g.DA);
+      dstride = (int64_t)R.cap * g.DB;
+    }
+    T* bp = (T*)a.bank_k + ((int64_t)a.g0 + src) * D + d0;
+    const int64_t bstride = (int64_t)a.bank_tok * D;
+    const int h_lo = hg * KHB, h_hi = min(g.H, h_lo + KHB);
+    for (int h0 = h_lo; h0 < h_hi; h0 += HU) {
+      Vec16<T> x[HU];
+#pragma unroll
+      for (int u = 0; u < HU; ++u)
+        if (h0 + u < h_hi) x[u].u = *reinterpret_cast<const uint4*>(sp + (int64_t)(h0 + u) * a.k_head);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+        const int h = h0 + u;
+        if (h >= h_hi) break;
+        if (bank) *reinterpret_cast<uint4*>(bp + h * bstride) = x[u].u;
+        float xf[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
+#pragma unroll
+        for (int q = 0; q < E / 2; ++q) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
+        *reinterpret_cast<uint4*>(dp + h * dstride) = x[u].u;
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tok0 + tl + u * TL;
-      if (i >= sg.n) break;
-      const int src = sg.src + i;
-      const int slot = sg.dst + i;
-      if (src >= a.bank_lo && src < a.bank_hi)
-        *reinterpret_cast<uint4*>((T*)a.bank_k + ((int64_t)h * a.bank_tok + (a.g0 + src)) * D + c * E) = x[u].u;
-      const int f = src / g.S, tok = src - f * g.S;
-      const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok - hp * g.grid_w;
-      float xf[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
-      rotate_run<E>(xf, g, a.tab, c * E, t, hp, wp);
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
-      const int d0 = c * E;
-      if (d0 < g.DA)
-        *reinterpret_cast<uint4*>((T*)R.ka + ((int64_t)h * R.cap + slot) * g.DA + d0) = x[u].u;
-      else
-        *reinterpret_cast<uint4*>((T*)R.kb + ((int64_t)h * R.cap + slot) * g.DB + (d0 - g.DA)) = x[u].u;
-      if (h == 0 && c == 0) {
-        R.t[slot] = t;
-        R.g[slot] = a.g0 + src;
-      }
+    if (c == 0 && hg == 0) {
+      R.t[slot] = t;
+      R.g[slot] = a.g0 + src;
     }
     return;
   }
@@ -181,15 +202,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // these counts through the same constants).
 template <typename T, int D>
 static void append_blocks(AppendArgs& a) {
-  constexpr int CH = D / Elem<T>::E;
-  constexpr int TPB = (256 / CH) * 4;
-  constexpr int HPB = 256 / (8 * CH);
+  using Sh = AppendShape<T, D>;
+  constexpr int KTB = Sh::KTB, HPB = Sh::HPB;
+  const int nhg = (a.geo.H + KHB - 1) / KHB;
   int kb = 0, vb = 0;
   for (int i = 0; i < a.nseg; ++i) {
     SegW& s = a.seg[i];
     s.kb0 = kb;
     s.vb0 = vb;
-    kb += ((s.n + TPB - 1) / TPB) * a.geo.H;
+    kb += ((s.n + KTB - 1) / KTB) * nhg;
     const int t0 = s.dst / kTile, t1 = (s.dst + s.n - 1) / kTile;
     vb += (t1 - t0 + 1) * ((a.geo.H + HPB - 1) / HPB);
   }
