@@ -474,6 +474,216 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   store_out(a, o, lsum, qrow, h, hl);
 }
 
+// ---------------------------------------------------------------------------
+// Attention-mass scores on the matrix cores (bf16, head_dim 128).  The query
+// window arrives already rotated and rounded (qbf: [H][Nq][128] bf16).
+//
+// Rows pass: per (head, query) the softmax normaliser over every valid key,
+// folded into one log2-domain constant  M = m + log2(l)  with
+// m = max_j c2 s_j and l = sum_j exp2(c2 s_j - m), c2 = log2(e)/sqrt(D); the
+// probability of key j is then exp2(c2 s_j - M).  Workgroup = 4 waves x 32
+// queries, S^T = K.Q^T per 64-key tile as in attention, no P.V.
+//
+// Columns pass: per (head, key) the sum over queries of exp2(c2 s - M).
+// S = Q.K^T with the lane owning one key column: workgroup = 4 waves x 32
+// keys of one region, their K fragments held in registers; query tiles of 32
+// rows (and their M) stream through LDS, double buffered; each lane sums its
+// 16 rows of every tile, and the two wave halves are added at the end.
+
+__device__ __forceinline__ void tile_load_k(TileRegs& tr, const TilePtrs& p, int r, int base) {
+  const uint16_t* kp = (r == 0 ? p.k[0] : p.k[1]) + base * p.kstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * p.kstride);
+}
+
+__device__ __forceinline__ void tile_store_k_padded(const TileRegs& tr, u32x4_t* lk, int tid) {
+  const int c = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lk[((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
+}
+
+__global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a, const uint16_t* qbf, int mblocks,
+                                                                 int total, int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kKTileP];
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int h = lin / mblocks;
+  const int mb = lin - h * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * kBM + wave * 32 + l32;
+  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const int kbase = perm_row(l32) * kKSt + hl;
+  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+
+  TileRegs tr;
+  tile_load_k(tr, tp, 0, 0);
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = qbf + ((int64_t)h * a.Nq + min(qrow, a.Nq - 1)) * 128 + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+  }
+  tile_store_k_padded(tr, lks[0], tid);
+  __syncthreads();
+  const float c2 = a.scale * 1.4426950408889634f;
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) tile_load_k(tr, tp, ts.region(t + 1), ts.base(t + 1));
+    f32x16_t sc[2];
+    const u32x4_t* lk = lks[t & 1];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]),
+                                                         qf[ks], sc[kb], 0, 0, 0);
+    }
+    mask_tile(sc, ts.valid(t), hl);
+    float mt = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[kb][i]);
+    const float mn = fmaxf(m, xhalf_max(mt) * c2);
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c2, -mn));
+    l = l * __builtin_amdgcn_exp2f(m - mn) + ps;
+    m = mn;
+    if (more) tile_store_k_padded(tr, lks[(t + 1) & 1], tid);
+    __syncthreads();
+  }
+  const float lt = xhalf_sum(l);
+  if (hl == 0 && qrow < a.Nq) a.m[(int64_t)h * a.Nq + qrow] = m + log2f(lt);
+}
+
+constexpr int kQT = 32;                          // query rows per columns-pass tile
+
+__global__ __launch_bounds__(256, 2) void score_cols_mfma_kernel(ScoreArgs a, const uint16_t* qbf, int region,
+                                                                 int kblocks, int total) {
+  __shared__ u32x4_t lq[2][kQT * kKSt];
+  __shared__ __attribute__((aligned(16))) float lm[2][kQT];
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int h = lin / kblocks;
+  const int kblk = lin - h * kblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int nk = a.keys.n[region];
+  const int key = kblk * 128 + wave * 32 + l32;
+  // this lane's key column: B operand fragments of S = Q.K^T
+  bf16x8_t kf[8];
+  {
+    const int kk = min(key, nk - 1);
+    const int64_t row = (int64_t)h * a.keys.cap[region] + kk;
+    const uint16_t* ka = (const uint16_t*)a.keys.ka[region] + row * kDA;
+    const uint16_t* kb = (const uint16_t*)a.keys.kb[region] + row * kDB;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int d = ks * 16 + hl * 8;
+      const uint16_t* src = d < kDA ? ka + d : kb + (d - kDA);
+      kf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src));
+    }
+  }
+  const int nqt = (a.Nq + kQT - 1) / kQT;
+  const uint16_t* qh = qbf + (int64_t)h * a.Nq * 128;
+  const float* mrow = a.m + (int64_t)h * a.Nq;
+  // thread tid stages chunks tid and tid + 256 of a 32 x 16-chunk query tile
+  auto load_q = [&](int qt, u32x4_t* st, float& mv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 256 * i;
+      const int r = min(qt * kQT + (ci >> 4), a.Nq - 1);
+      st[i] = *reinterpret_cast<const u32x4_t*>(qh + (int64_t)r * 128 + (ci & 15) * 8);
+    }
+    if (tid < kQT) {
+      const int r = qt * kQT + tid;
+      mv = r < a.Nq ? mrow[r] : INFINITY;   // rows past the window contribute exp2(-inf) = 0
+    }
+  };
+  auto store_q = [&](int buf, const u32x4_t* st, float mv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 256 * i;
+      lq[buf][(ci >> 4) * kKSt + (ci & 15)] = st[i];
+    }
+    if (tid < kQT) lm[buf][tid] = mv;
+  };
+  u32x4_t st[2];
+  float mv = 0.f;
+  load_q(0, st, mv);
+  store_q(0, st, mv);
+  __syncthreads();
+  const float c2 = a.scale * 1.4426950408889634f;
+  const int qbase = l32 * kKSt + hl;
+  float acc = 0.f;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const bool more = qt + 1 < nqt;
+    if (more) load_q(qt + 1, st, mv);
+    const u32x4_t* q = lq[qt & 1];
+    f32x16_t c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q[qbase + ks * 2]), kf[ks], c, 0, 0, 0);
+    // accumulator i is query row (i/4)*8 + hl*4 + i%4 of the tile
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 mg = *reinterpret_cast<const float4*>(&lm[qt & 1][g4 * 8 + hl * 4]);
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 0], c2, -mg.x));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 1], c2, -mg.y));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 2], c2, -mg.z));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 3], c2, -mg.w));
+    }
+    if (more) store_q((qt + 1) & 1, st, mv);
+    __syncthreads();
+  }
+  const float tot = xhalf_sum(acc);
+  if (hl == 0 && key < nk) {
+    const int ncap = a.keys.cap[0] + a.keys.cap[1];
+    const int p = region == 0 ? key : a.keys.cap[0] + key;
+    a.part[(int64_t)h * ncap + p] = tot;
+  }
+}
+
+hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s) {
+  const int mblocks = (a.Nq + kBM - 1) / kBM;
+  const int ntile0 = (a.keys.n[0] + kBN - 1) / kBN;
+  const int ntile1 = (a.keys.n[1] + kBN - 1) / kBN;
+  ScoreArgs b = a;
+  int n0 = ntile0, nt = ntile0 + ntile1;
+  if (ntile0 == 0) {   // keep region 0 non-empty for the tile sequence
+    b.keys.ka[0] = a.keys.ka[1];
+    b.keys.kb[0] = a.keys.kb[1];
+    b.keys.v[0] = a.keys.v[1];
+    b.keys.cap[0] = a.keys.cap[1];
+    b.keys.n[0] = a.keys.n[1];
+    b.keys.n[1] = 0;
+    n0 = ntile1;
+    nt = ntile1;
+  }
+  if (nt == 0 || a.Nq == 0) return hipSuccess;
+  const int total = mblocks * a.geo.H;
+  hipLaunchKernelGGL(score_rows_mfma_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // columns: original region numbering (part is indexed by physical slot)
+  for (int r = 0; r < 2; ++r) {
+    if (a.keys.n[r] == 0) continue;
+    const int kblocks = (a.keys.n[r] + 127) / 128;
+    const int tot = kblocks * a.geo.H;
+    hipLaunchKernelGGL(score_cols_mfma_kernel, dim3(tot), dim3(256), 0, s, a, qbf, r, kblocks, tot);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int VAR>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int bm = VAR == 2 ? 256 : kBM;

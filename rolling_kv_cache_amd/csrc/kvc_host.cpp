@@ -444,7 +444,7 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   a.geo = h->geo;
   a.tab = h->tab;
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
-  hipError_t e = kvc::launch_score(a, h->stream);
+  hipError_t e = kvc::launch_score(a, h->stream, std::getenv("KVC_ATTEND_GENERAL") != nullptr);
   return device_result(h, e, "score");
 }
 

@@ -550,7 +550,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general)
 // score: (1) rotate the query window, (2) per-row max and sum of exp, (3) per
 // (key, head) column sum of the normalized probabilities, (4) sum over heads
 // into logical order.
-template <typename T, int D>
+// rotated queries to scratch as [H][Nq][D]: fp32 for the general passes, or
+// bf16 (exact: the values are already rounded) for the matrix-core passes
+template <typename T, int D, bool BF16OUT>
 __global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
   const Geo& g = a.geo;
   const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
@@ -559,9 +561,15 @@ __global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
   const int i = (int)(gid / g.H);
   float qv[D];
   load_rotated_query<T, D>((const T*)a.q, i, h, a.qt[i / g.S], g, a.tab, qv);
-  float* dst = a.qh + ((int64_t)h * a.Nq + i) * D;
+  if (BF16OUT) {
+    uint16_t* dst = (uint16_t*)a.qh + ((int64_t)h * a.Nq + i) * D;
 #pragma unroll
-  for (int d = 0; d < D; ++d) dst[d] = qv[d];
+    for (int d = 0; d < D; ++d) dst[d] = f2bf_rne(qv[d]);
+  } else {
+    float* dst = a.qh + ((int64_t)h * a.Nq + i) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) dst[d] = qv[d];
+  }
 }
 
 template <typename T, int D>
@@ -638,7 +646,7 @@ template <typename T, int D>
 static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.Nq * a.geo.H;
   const unsigned b1 = (unsigned)((rows + 63) / 64);
-  hipLaunchKernelGGL((score_rot_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((score_rot_kernel<T, D, false>), dim3(b1), dim3(64), 0, s, a);
   hipLaunchKernelGGL((score_rows_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
   const int64_t cols = (int64_t)(a.keys.cap[0] + a.keys.cap[1]) * a.geo.H;
   hipLaunchKernelGGL((score_cols_kernel<T, D>), dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, a);
@@ -646,7 +654,15 @@ static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
 }
 
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general) {
+  if (!force_general && a.geo.esz == 2 && a.geo.D == 128) {
+    const int64_t rows = (int64_t)a.Nq * a.geo.H;
+    hipLaunchKernelGGL((score_rot_kernel<uint16_t, 128, true>), dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, a);
+    if (hipError_t e = launch_score_mfma(a, (const uint16_t*)a.qh, s); e != hipSuccess) return e;
+    const int ncap = a.keys.cap[0] + a.keys.cap[1];
+    hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.geo.esz == 2) {
     if (a.geo.D == 128)
       score_launch_all<uint16_t, 128>(a, s);

@@ -16,6 +16,11 @@ hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s);
 // general per-row path.  `force_general` selects the latter (tests).
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general);
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+// Scores: the matrix-core passes for bf16 with head_dim 128, else the general
+// per-row/per-column path (force_general selects the latter).
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general);
+// rows + columns passes over a query window already rotated into qbf
+// ([H][Nq][128] bf16); writes a.m (log2 normaliser per row) and a.part
+hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s);
 
 }  // namespace kvc

@@ -96,7 +96,10 @@ def test_small_deep_forcing():
                               (3,) * 16), compact=True)
 
 
-def test_scores_match_oracle():
+@pytest.mark.parametrize("general", [False, True])
+def test_scores_match_oracle(general):
+    """Attention-mass scores on the matrix-core passes and on the general path: 206-token frames give a
+    ragged sink region, ragged key tiles and a ragged last query tile."""
     w = Workload("score_small", 206, 3, 128, "bf16", 4, 8, 1, 5, (2, 2, 2))
     gc = new_cache(w)
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
@@ -105,7 +108,12 @@ def test_scores_match_oracle():
         gc.append(dev(k, w), dev(v, w), 2 * i)
         oc.append(k, v, 2, 2 * i)
     qw, _, _ = chunk_inputs(w, 7, frames=2)
-    s_gpu = gc.score(dev(qw, w), [3, 4]).cpu().numpy().astype(np.float64)
+    if general:
+        os.environ["KVC_ATTEND_GENERAL"] = "1"
+    try:
+        s_gpu = gc.score(dev(qw, w), [3, 4]).cpu().numpy().astype(np.float64)
+    finally:
+        os.environ.pop("KVC_ATTEND_GENERAL", None)
     s_ref = oc.score(qw, 2, [3, 4], f64=True)
     assert abs(s_gpu.sum() - w.heads * 2 * w.frame_seqlen) < 1e-3
     assert np.max(np.abs(s_gpu - s_ref)) < 1e-4 * max(1.0, s_ref.max())
