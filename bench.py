@@ -135,6 +135,20 @@ def main():
         torch.cuda.synchronize()
         if i >= 2:
             app_cold.append(a.elapsed_time(b))
+    # attention-mass scores of this chunk's queries over the whole cache (the Deep-Forcing scoring pass)
+    sc_ms = []
+    qwin = pool[0][0]
+    cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
+    torch.cuda.synchronize()
+    for i in range(6):
+        a, b = ev(), ev()
+        a.record(stream)
+        cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
+        b.record(stream)
+        torch.cuda.synchronize()
+        sc_ms.append(a.elapsed_time(b))
+    score_ms = float(np.median(sc_ms))
+    extras = sink_push_and_compact(dev, stream, flush, ev)
     # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
     cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cy = torch.empty_like(cx)
@@ -200,6 +214,9 @@ def main():
             "append_hbm_frac_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "retime_hbm_frac_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "hbm_copy_GBps_measured": round(copy_gbps, 1),
+            "score_ms": round(score_ms, 4),
+            "score_tflops": round(flop / (score_ms * 1e-3) / 1e12, 2),
+            **extras,
         },
     }
     if context:
@@ -207,6 +224,70 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_rows, w, cache)
     print(json.dumps(res), flush=True)
+
+
+def sink_push_and_compact(dev, stream, flush, ev):
+    """The two remaining data-movement kernels at their workloads' shapes, MALL flushed before each sample:
+    a Rolling-Sink push of one 3-frame bank block (12 heads x 1560-token frames, 15 sink + 6 window frames,
+    18-frame bank) and a Deep-Forcing compaction keeping the 3-frame sink plus 9360 of 28080 window entries
+    (12 heads, 3 sink + 18 window frames).  Bytes = read + write of K and V for every moved entry."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import WORKLOADS, chunk_inputs
+
+    def cold(fn, n=8):
+        ts = []
+        for i in range(n):
+            fn(i, False)
+            flush.sum()
+            a, b = ev(), ev()
+            a.record(stream)
+            fn(i, True)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(a.elapsed_time(b))
+        return float(np.mean(ts)) * 1e3
+
+    out = {}
+    w = WORKLOADS["c4"]
+    S, H, D = w.frame_seqlen, w.heads, w.head_dim
+    chunks = [tuple(torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, c)[1:]) for c in range(7)]
+    c4 = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16, bank_frames=w.bank_frames)
+    for c in range(7):
+        c4.append(*chunks[c], 3 * c)
+
+    def push(i, timed):
+        if timed:
+            c4.sink_push(3 * (i % 6), 3, 30 + 3 * i)
+    us = cold(push)
+    byt = 4.0 * 3 * S * H * D * 2
+    out["sink_push_us_cold"] = round(us, 2)
+    out["sink_push_GBps_cold"] = round(byt / (us * 1e-6) / 1e9, 1)
+    del c4
+
+    w = WORKLOADS["c5b"]
+    c5 = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16, compact=True)
+    tf = [0]
+    ns = w.sink_frames * S
+    keep = np.concatenate([np.arange(ns), ns + np.arange(0, 28080, 3)]).astype(np.int32)   # sink + every 3rd
+
+    def fill():
+        while c5.info()["n_valid"] < (w.sink_frames + w.window_frames) * S:
+            c5.append(*chunks[tf[0] % 7], tf[0] * 3)
+            tf[0] += 1
+
+    def comp(i, timed):
+        if not timed:
+            fill()
+        else:
+            c5.compact(keep)
+    us = cold(comp)
+    byt = 4.0 * (len(keep) - ns) * H * D * 2
+    out["compact_us_cold"] = round(us, 2)
+    out["compact_GBps_cold"] = round(byt / (us * 1e-6) / 1e9, 1)
+    return out
 
 
 def vendor_context(dev, stream, H, N, Lk, D):

@@ -88,7 +88,7 @@ struct CompactArgs {
   RegionPtrs src, dst;
   const int32_t* idx;                     // source slot of each destination slot
   int32_t n;
-  int64_t nk, nv, nt;
+  int64_t nk, nv, nt;                     // block counts, set by the launcher
   Geo geo;
 };
 

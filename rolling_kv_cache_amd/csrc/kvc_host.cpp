@@ -475,10 +475,6 @@ kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
       a.dst = h->win[h->st.win_buf ^ 1];
       a.idx = h->keep_dev;
       a.n = (int32_t)src.size();
-      const int32_t CH = h->D * h->geo.esz / 16;
-      a.nk = (int64_t)a.n * h->H * CH;
-      a.nv = (int64_t)((a.n + 7) / 8) * h->D * h->H;
-      a.nt = a.n;
       a.geo = h->geo;
       e = kvc::launch_compact(a, h->stream);
     }

@@ -329,73 +329,132 @@ hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// compact: destination slot j <- source slot idx[j] (both window buffers).
-template <typename T>
+// compact: destination slot j <- source slot idx[j] (the two window buffers;
+// idx sorted and unique).  Two block kinds in one launch:
+//  * key blocks: KS destination slots x all heads; thread (slot, chunk) copies
+//    that 16-byte chunk of the slot's key row for every head (eight heads in
+//    flight) and, for chunk 0, the slot's t and g;
+//  * value blocks: one destination V^T tile (64 slots) of one head.  A slot's
+//    value is a column of a V^T tile (one element per 128-byte row), so the
+//    block brings whole source tiles into LDS -- only those holding kept
+//    entries, in order -- gathers the columns there, and writes the
+//    destination tile as full rows.  Since idx is sorted, each source tile is
+//    read by at most two destination tiles.
+template <typename T, int D>
+struct CompactShape {
+  static constexpr int E = Elem<T>::E;
+  static constexpr int CH = D / E;          // 16-byte chunks per key row
+  static constexpr int KS = 256 / CH;       // destination slots per key block
+};
+
+template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
-  constexpr int E = Elem<T>::E;
+  using Sh = CompactShape<T, D>;
+  constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, HU = 8;
   const Geo& g = a.geo;
-  const int CH = g.D / E;
-  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid < a.nk) {
-    const int c = (int)(gid % CH);
-    const int64_t r = gid / CH;
-    const int h = (int)(r % g.H);
-    const int j = (int)(r / g.H);
+  const int tid = threadIdx.x;
+  int b = blockIdx.x;
+  if (b < a.nk) {
+    const int j = b * KS + tid / CH;
+    const int c = tid % CH;
+    if (j >= a.n) return;
     const int sj = a.idx[j];
+    if (c == 0) {
+      a.dst.t[j] = a.src.t[sj];
+      a.dst.g[j] = a.src.g[sj];
+    }
     const int d0 = c * E;
+    const T* sp;
+    T* dp;
+    int64_t ss, ds;
     if (d0 < g.DA) {
-      *reinterpret_cast<uint4*>((T*)a.dst.ka + ((int64_t)h * a.dst.cap + j) * g.DA + d0) =
-          *reinterpret_cast<const uint4*>((const T*)a.src.ka + ((int64_t)h * a.src.cap + sj) * g.DA + d0);
+      sp = (const T*)a.src.ka + (int64_t)sj * g.DA + d0;
+      dp = (T*)a.dst.ka + (int64_t)j * g.DA + d0;
+      ss = (int64_t)a.src.cap * g.DA;
+      ds = (int64_t)a.dst.cap * g.DA;
     } else {
-      *reinterpret_cast<uint4*>((T*)a.dst.kb + ((int64_t)h * a.dst.cap + j) * g.DB + (d0 - g.DA)) =
-          *reinterpret_cast<const uint4*>((const T*)a.src.kb + ((int64_t)h * a.src.cap + sj) * g.DB + (d0 - g.DA));
+      sp = (const T*)a.src.kb + (int64_t)sj * g.DB + (d0 - g.DA);
+      dp = (T*)a.dst.kb + (int64_t)j * g.DB + (d0 - g.DA);
+      ss = (int64_t)a.src.cap * g.DB;
+      ds = (int64_t)a.dst.cap * g.DB;
+    }
+    // native 16-byte vectors (HIP's uint4 class would land in private memory here)
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    for (int h0 = 0; h0 < g.H; h0 += HU) {
+      v4u x[HU];
+#pragma unroll
+      for (int u = 0; u < HU; ++u)
+        if (h0 + u < g.H) x[u] = *reinterpret_cast<const v4u*>(sp + (h0 + u) * ss);
+#pragma unroll
+      for (int u = 0; u < HU; ++u)
+        if (h0 + u < g.H) *reinterpret_cast<v4u*>(dp + (h0 + u) * ds) = x[u];
     }
     return;
   }
-  gid -= a.nk;
-  if (gid < a.nv) {
-    const int NG = (a.n + 7) / 8;
-    const int grp = (int)(gid % NG);
-    const int64_t r = gid / NG;
-    const int d = (int)(r % g.D);
-    const int h = (int)(r / g.D);
-    union {
-      uint4 u[sizeof(T) * 8 / 16];
-      T v[8];
-    } o;
-    const int j0 = grp * 8;
-    const int nn = min(8, a.n - j0);
+  b -= (int)a.nk;
+  const int NT = (a.n + kTile - 1) / kTile;
+  const int h = b / NT, dt = b - (b / NT) * NT;
+  const int j0 = dt * kTile, nn = min(kTile, a.n - j0);
+  constexpr int TE = D * kTile;                       // elements per V^T tile
+  constexpr int PER = TE * (int)sizeof(T) / (256 * 16);   // 16-byte pieces per thread
+  __shared__ uint4 s_src[TE * sizeof(T) / 16];
+  __shared__ uint4 s_dst[TE * sizeof(T) / 16];
+  __shared__ int s_idx[kTile];
+  if (tid < kTile) s_idx[tid] = tid < nn ? a.idx[j0 + tid] : INT32_MAX;
+  __syncthreads();
+  const T* vsrc = (const T*)a.src.v + (size_t)h * (a.src.cap / kTile) * TE;
+  T* sdst = (T*)s_dst;
+  const T* ssrc = (const T*)s_src;
+  int st = s_idx[0] / kTile;
+  const int st_last = s_idx[nn - 1] / kTile;
+  while (true) {
+    // stage source tile st
+    const uint4* tp = reinterpret_cast<const uint4*>(vsrc + (size_t)st * TE);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      o.v[jj] = T(0);
-      if (jj < nn) o.v[jj] = ((const T*)a.src.v)[v_index(h, a.src.cap, g.D, a.idx[j0 + jj], d)];
+    for (int i = 0; i < PER; ++i) s_src[tid + 256 * i] = tp[tid + 256 * i];
+    __syncthreads();
+    // gather: thread owns destination slot jj = tid % 64 and rows d = tid / 64 + 4k
+    const int jj = tid % kTile;
+    const int sj = s_idx[jj];
+    if (sj / kTile == st) {
+      const int col = sj % kTile;
+      for (int d = tid / kTile; d < D; d += 256 / kTile) sdst[d * kTile + jj] = ssrc[d * kTile + col];
     }
-    T* dst = (T*)a.dst.v + v_index(h, a.dst.cap, g.D, j0, d);
-    if (nn == 8) {
+    __syncthreads();
+    if (st >= st_last) break;
+    // next source tile holding a kept entry
+    int nxt = INT32_MAX;
+    for (int q = 0; q < nn; ++q) {
+      const int tq = s_idx[q] / kTile;
+      if (tq > st) {
+        nxt = tq;
+        break;
+      }
+    }
+    st = nxt;
+  }
+  // the destination tile as full rows (slots past n in a partial tile hold
+  // stale data; they are outside the valid prefix and never read)
+  uint4* dp = reinterpret_cast<uint4*>((T*)a.dst.v + ((size_t)h * (a.dst.cap / kTile) + dt) * TE);
 #pragma unroll
-      for (int q = 0; q < (int)(sizeof(T) * 8 / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = o.u[q];
-    } else {
-      for (int jj = 0; jj < nn; ++jj) dst[jj] = o.v[jj];
-    }
-    return;
-  }
-  gid -= a.nv;
-  if (gid < a.nt) {
-    const int j = (int)gid;
-    a.dst.t[j] = a.src.t[a.idx[j]];
-    a.dst.g[j] = a.src.g[a.idx[j]];
-  }
+  for (int i = 0; i < PER; ++i) dp[tid + 256 * i] = s_dst[tid + 256 * i];
+}
+
+template <typename T, int D>
+static hipError_t compact_launch(CompactArgs a, hipStream_t s) {
+  a.nk = (a.n + CompactShape<T, D>::KS - 1) / CompactShape<T, D>::KS;
+  a.nv = (int64_t)a.geo.H * ((a.n + kTile - 1) / kTile);
+  a.nt = 0;
+  const int64_t blocks = a.nk + a.nv;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((compact_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  const int64_t total = a.nk + a.nv + a.nt;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (a.geo.esz == 2)
-    hipLaunchKernelGGL(compact_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(compact_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.n == 0) return hipSuccess;
+  if (a.geo.esz == 2) return a.geo.D == 128 ? compact_launch<uint16_t, 128>(a, s) : compact_launch<uint16_t, 64>(a, s);
+  return a.geo.D == 128 ? compact_launch<float, 128>(a, s) : compact_launch<float, 64>(a, s);
 }
 
 // ----------------------------------------------------------------------------
