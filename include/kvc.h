@@ -96,7 +96,8 @@ typedef struct {
 
 /* Device bytes the caller must provide to kvc_create for this geometry
  * (includes K/V planes, time/global-index arrays, RoPE tables, the optional
- * raw-key bank and, with KVC_CREATE_COMPACT, the second window buffer).
+ * raw-key bank, with KVC_CREATE_COMPACT the second window buffer, and the
+ * small per-block flag array kvc_attend uses to mark blocks for recompute).
  * Returns 0 for an unsupported geometry (head_dim not 64/128, bad sizes). */
 size_t kvc_workspace_bytes(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,
                            int32_t heads, int32_t head_dim, kvc_dtype dt, int32_t bank_frames,
@@ -139,7 +140,8 @@ kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_fram
  * frame_seqlen, heads, head_dim] raw queries, rotated here at time q_t_index
  * + frame (KVC_T_NEWEST: the newest chunk's current time) and rounded to the
  * cache dtype.  out: device, same shape and dtype.  ESTATE if the cache is
- * empty. */
+ * empty.  Uses the handle's workspace flags, so attends on one handle must not
+ * overlap on different streams. */
 kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out);
 
 /* Shift the time index of logical entries [slot_lo, slot_hi) by delta

@@ -24,9 +24,11 @@
 //  * the softmax of tile t is interleaved instruction by instruction with the
 //    QK^T MFMAs of tile t+1 (sched_group_barrier), and four LDS operand reads
 //    stay in flight ahead of every MFMA;
-//  * online softmax in the log2 domain (exp2 with log2(e)/sqrt(D) folded into
-//    one FMA); the running max only moves when a tile's max exceeds it by more
-//    than 8 (log2 units), so the O rescale is skipped on almost every tile; the
+//  * softmax in the log2 domain (exp2 with log2(e)/sqrt(D) folded into one
+//    FMA) against a fixed per-row reference (the row's maximum over tile 0),
+//    so no tile needs a maximum or an O rescale; blocks whose probabilities
+//    would leave range are flagged and redone by the running-maximum kernel
+//    (whose maximum moves only when a tile exceeds it by more than 8).  The
 //    row sum is accumulated from the packed bf16 P with v_dot2_f32_bf16, i.e.
 //    from the same rounded probabilities the P.V product uses;
 //  * queries are rotated (3D RoPE, fp32, no FMA) and rounded to bf16 in the
@@ -396,13 +398,16 @@ __device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* l
   }
 }
 
+// With only_flagged set, blocks whose flag is 0 exit at once (the recompute
+// pass behind the fixed-reference kernel).
 __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                           int ntile0, int ntiles) {
+                                                           int ntile0, int ntiles, const int32_t* only_flagged) {
   __shared__ u32x4_t lks[2][kKTileP];
   __shared__ u32x4_t lvs[2][kVTileP];
   const int wg = blockIdx.x;
   const int lin = (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
+  if (only_flagged != nullptr && only_flagged[lin] == 0) return;
   const int h = lin / mblocks;
   const int mb = lin - h * mblocks;
   const int tid = threadIdx.x;
@@ -684,9 +689,146 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// v5f: v5 with a fixed reference per row instead of a running maximum.  Every
+// row keeps m = max of its scores in tile 0 (log2 units) for all tiles, so a
+// tile needs no maximum, no rescale test and no O rescale: P = exp2(c2 s - m).
+// The result is the same normalisation (a constant shift cancels between O and
+// the row sum), exact up to rounding while P stays in range.  A row whose later
+// scores exceed m so far that a 32-term partial sum of P passes 2^48 (or turns
+// inf/NaN) marks its block in a.flags, and the running-maximum v5 kernel then
+// recomputes exactly the marked blocks.
+constexpr float kPLimit = 281474976710656.f;   // 2^48
+
+__device__ __forceinline__ float tile_max(const f32x16_t* sp, float c2) {
+  float mt = sp[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sp[kb][i]);
+  return xhalf_max(mt) * c2;
+}
+
+// S^T(t+1) on the matrix cores, interleaved with P(t) = exp2(c2 S^T(t) - m)
+__device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int kbase,
+                                           const f32x16_t* sp, float negm, float c2, bf16x8_t pb[2][2],
+                                           float& psum) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  psum = 0.f;
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    const int kb = step >> 3, ks = step & 7;
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
+    const int e = step * 2;
+    const int pkb = e >> 4, phf = (e >> 3) & 1, pj = e & 7;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj], c2, negm));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj + 1], c2, negm));
+    const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+    pb[pkb][phf][pj] = pr[0];
+    pb[pkb][phf][pj + 1] = pr[1];
+    psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
+  }
+  asm volatile("" ::"v"(psum));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[kb][hf])));
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
+                                                           int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kKTileP];
+  __shared__ u32x4_t lvs[2][kVTileP];
+  __shared__ int s_flag;
+  const int wg = blockIdx.x;
+  const int lin = (wg & 7) * per_xcd + (wg >> 3);
+  if (lin >= total) return;
+  const int h = lin / mblocks;
+  const int mb = lin - h * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * 256 + wave * 32 + l32;
+  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const int kbase = perm_row(l32) * kKSt + hl;
+  const int vbase = l32 * kVSt + hl;
+  const int last = ntiles - 1;
+  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+  if (tid == 0) s_flag = 0;
+
+  Stage5 st;
+  load5(st, tp, 0, 0, 0, 0);
+  bf16x8_t qf[8];
+  load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
+  store5(st, lks[0], lvs[0], tid, true, true);
+  {
+    const int t1 = min(1, last);
+    load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+    store5(st, lks[1], lvs[1], tid, true, false);
+  }
+  f32x16_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+  float lsum = 0.f, pmax = 0.f;
+  const float c2 = a.scale * 1.4426950408889634f;
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kKSt + ks * 2]);
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
+    }
+  }
+  mask_tile(sa, ts.valid(0), hl);
+  // tile 0 holds at least one valid key, so the reference is finite
+  const float negm = -tile_max(sa, c2);
+
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
+    const int tk = min(t + 2, last), tv = min(t + 1, last);
+    load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    bf16x8_t pb[2][2];
+    float psum;
+    qk_and_exp(snext, lks[(t + 1) & 1], qf, kbase, scur, negm, c2, pb, psum);
+    pmax = fmaxf(pmax, psum);
+    lsum += psum;
+    pv_padded(o, lvs[t & 1], vbase, pb);
+    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < ntiles) step(t, sa, sb);
+  if (__ballot(!(pmax <= kPLimit)) != 0 && lane == 0) s_flag = 1;
+  __syncthreads();
+  if (tid == 0) a.flags[lin] = s_flag;
+  store_out(a, o, lsum, qrow, h, hl);
+}
+
 template <int VAR>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int bm = VAR == 2 ? 256 : kBM;
+  const int bm = (VAR == 2 || VAR == 4) ? 256 : kBM;
   const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
@@ -707,18 +849,28 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     nt = ntile1;
   }
   if (VAR == 2)
-    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
+    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt,
+                       (const int32_t*)nullptr);
+  else if (VAR == 4) {
+    hipLaunchKernelGGL(attend_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt,
+                       (const int32_t*)b.flags);
+  }
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
   return hipGetLastError();
 }
 
-// The 8-wave kernel is the default; KVC_ATTEND_VARIANT=v3 selects the 4-wave
-// variant (two workgroups per CU) for A/B timing.
+// Default: the fixed-reference 8-wave kernel plus the recompute pass (it needs
+// the workspace flags; without them the running-maximum kernel runs alone).
+// KVC_ATTEND_VARIANT=v5 (running maximum, 8 waves) or v3 (4 waves, two
+// workgroups per CU) selects another kernel for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
   if (v && std::string(v) == "v3") return attend_launch<0>(a, s);
-  return attend_launch<2>(a, s);
+  if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2>(a, s);
+  return attend_launch<4>(a, s);
 }
 
 }  // namespace kvc

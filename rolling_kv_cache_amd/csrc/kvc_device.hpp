@@ -119,6 +119,7 @@ struct AttendArgs {
   Geo geo;
   Tables tab;
   float scale;                            // 1/sqrt(D)
+  int32_t* flags;                         // workspace: one recompute flag per 256-query attention block
 };
 
 struct ScoreArgs {

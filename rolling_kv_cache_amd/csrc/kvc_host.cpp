@@ -39,7 +39,7 @@ struct Layout {
   int32_t S_tok = 0, W_tok = 0, SP = 0, WP = 0, bank_tok = 0;
   int32_t D = 0, DA = 0, DB = 0, dt = 0, bw = 0, esz = 0;
   RegionLayout sink{}, win[2]{};
-  size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, total = 0;
+  size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, att_flags = 0, total = 0;
 };
 
 Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_t H, int32_t D, kvc_dtype dt,
@@ -87,6 +87,8 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   L.tab_h = take((size_t)S * (L.bw / 2) * 2 * 4);
   L.tab_w = take((size_t)S * (L.bw / 2) * 2 * 4);
   L.keep = take((size_t)L.WP * 4);
+  // one recompute flag per 256-query attention block of the largest query chunk
+  L.att_flags = take((size_t)H * (((size_t)KVC_MAX_Q_FRAMES * S + 255) / 256) * 4);
   L.total = off;
   L.ok = true;
   return L;
@@ -106,6 +108,7 @@ struct kvc_cache {
   void* bank_k;
   void* bank_v;
   int32_t* keep_dev;
+  int32_t* att_flags;
   int32_t* keep_pinned;
   hipEvent_t keep_evt;
   bool keep_pending;
@@ -274,6 +277,7 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->bank_k = h->ws + L.bank_k;
   h->bank_v = h->ws + L.bank_v;
   h->keep_dev = (int32_t*)(h->ws + L.keep);
+  h->att_flags = (int32_t*)(h->ws + L.att_flags);
   h->keep_pinned = nullptr;
   h->keep_pending = false;
   h->st.init(frame_seqlen, L.S_tok, L.W_tok);
@@ -369,6 +373,7 @@ kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t
   a.geo = h->geo;
   a.tab = h->tab;
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
+  a.flags = h->att_flags;
   const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
   hipError_t e = kvc::launch_attend(a, h->stream, force_general);
   return device_result(h, e, "attend");

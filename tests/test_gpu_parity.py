@@ -148,7 +148,7 @@ def test_uniform_retime_keeps_attention():
     check_attention(b, a, "uniform retime")
 
 
-@pytest.mark.parametrize("variant", ["", "v3"])
+@pytest.mark.parametrize("variant", ["", "v5", "v3"])
 def test_attend_score_jump(variant):
     """Keys of the oldest frames are tiny and a later chunk's keys and queries are 4x N(0,1): the later
     scores exceed every score of the first key tile by about 48 to 90 in exp2 units, so the kernels must
