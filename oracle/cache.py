@@ -222,6 +222,28 @@ class OracleCache:
             return attention_f64(qh, self.K, self.V)
         return attention_f32(qh, self.K, self.V)
 
+    def attend_block_causal(self, q, frames, t0, block_frames, rows=None, f64=False):
+        """Block-causal attention of a whole clip, for a cache that holds the clip from its first frame.
+
+        The rCM length-extrapolation article points to a block-level attention mask for the clip-level
+        (teacher-forced) training path, and the Causal-Forcing article (section 4, block-wise denoising)
+        splits a 21-frame clip into blocks of num_frame_per_block frames.  Reading taken: query frame f
+        (rotated at t0 + f) belongs to block f // block_frames and attends to the cached entries of
+        blocks 0..that block, i.e. to the first min(n, (block + 1) * block_frames * S) entries in logical
+        order; there is no mask inside a block.
+        """
+        qh = self.rotate_queries(q, frames, t0)
+        N = frames * self.S
+        rows = np.arange(N) if rows is None else np.asarray(rows)
+        blk = rows // (block_frames * self.S)
+        fn = attention_f64 if f64 else attention_f32
+        out = np.empty((len(rows), self.H, self.D), np.float64 if f64 else np.float32)
+        for b in np.unique(blk):
+            sel = np.nonzero(blk == b)[0]
+            n_vis = min(self.n, int(b + 1) * block_frames * self.S)
+            out[sel] = fn(qh[rows[sel]], self.K[:n_vis], self.V[:n_vis])
+        return out
+
     def score(self, q_win, frames, t_frames, f64=False):
         """Per-entry attention mass of the query window, summed over heads and query rows."""
         N = frames * self.S

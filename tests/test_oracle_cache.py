@@ -195,3 +195,52 @@ def test_workload_generator_is_seeded_and_bf16():
     assert abs(float(a.std()) - 1.0) < 0.05
     q, k, v = chunk_inputs(WORKLOADS["tiny"], 0)
     assert q.shape == (16, 2, 64) and not np.array_equal(q, k)
+
+
+# ---------------------------------------------------------------- block-causal clip attention
+def _clip_cache(S=12, H=2, D=64, grid_w=4, frames=6, cfg=77, dtype="f32"):
+    oc = OracleCache(0, frames, S, H, D, grid_w, dtype)
+    ks, vs = [], []
+    for f in range(frames):
+        k = gen(cfg, f, 1, S, H, D, dtype)
+        v = gen(cfg, f, 2, S, H, D, dtype)
+        oc.append(k, v, 1, f)
+        ks.append(k)
+        vs.append(v)
+    q = gen(cfg, 99, 0, frames * S, H, D, dtype)
+    return oc, q, ks, vs
+
+
+def test_block_causal_brute_force_mask():
+    """Explicit token mask M[i, j] = (block(j) <= block(i)) with brute-force fp64 loops on tiny inputs."""
+    S, frames, bf = 4, 5, 2
+    oc, q, _, _ = _clip_cache(S=S, H=2, D=16, grid_w=2, frames=frames)
+    qh = oc.rotate_queries(q, frames, 0).astype(np.float64)
+    got = oc.attend_block_causal(q, frames, 0, bf, f64=True)
+    blk = lambda i: (i // S) // bf
+    for i in range(frames * S):
+        vis = [j for j in range(oc.n) if blk(j) <= blk(i)]
+        ref = attention_loops_f64(qh[i:i + 1].tolist(), oc.K[vis].tolist(), oc.V[vis].tolist())
+        assert np.allclose(got[i], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_block_causal_equals_incremental_cache():
+    """Block b's rows equal an ordinary attend after appending only blocks 0..b (the chunk-by-chunk
+    inference path): two different computations of the same masked softmax."""
+    S, frames, bf = 12, 6, 2
+    oc, q, ks, vs = _clip_cache(S=S, frames=frames)
+    full = oc.attend_block_causal(q, frames, 0, bf, f64=True)
+    inc = OracleCache(0, frames, S, 2, 64, 4, "f32")
+    for b in range(frames // bf):
+        for f in range(b * bf, (b + 1) * bf):
+            inc.append(ks[f], vs[f], 1, f)
+        rows = slice(b * bf * S, (b + 1) * bf * S)
+        ref = inc.attend(q[rows], bf, b * bf, f64=True)
+        assert np.allclose(full[rows], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_block_causal_one_block_is_full_attention():
+    oc, q, _, _ = _clip_cache(frames=4)
+    a = oc.attend_block_causal(q, 4, 0, 4, f64=True)
+    b = oc.attend(q, 4, 0, f64=True)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
