@@ -149,6 +149,8 @@ def main():
         sc_ms.append(a.elapsed_time(b))
     score_ms = float(np.median(sc_ms))
     extras = sink_push_and_compact(dev, stream, flush, ev)
+    extras.update(per_gpu_share(dev, stream, ev, w))
+    extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
     # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
     cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cy = torch.empty_like(cx)
@@ -288,6 +290,66 @@ def sink_push_and_compact(dev, stream, flush, ev):
     out["compact_us_cold"] = round(us, 2)
     out["compact_GBps_cold"] = round(byt / (us * 1e-6) / 1e9, 1)
     return out
+
+
+def per_gpu_share(dev, stream, ev, w):
+    """Attention at one GPU's share of the 40-head layer when heads are split over 8 GPUs: 5 heads, the same
+    4680 queries over 28080 keys (19 query blocks x 5 heads = 95 workgroups for 256 CUs)."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import chunk_inputs
+    S, D, Hs = w.frame_seqlen, w.head_dim, 5
+    c = kvc.KVCache(w.sink_frames, w.window_frames, S, Hs, D, w.grid_w, torch.bfloat16)
+    q = None
+    for i in range(6):
+        q_, k, v = (torch.from_numpy(x[:, :Hs].copy()).to(dev, torch.bfloat16) for x in chunk_inputs(w, i))
+        c.append(k, v, 3 * i)
+        q = q_
+    out = c.attend(q, 15)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(8):
+        a, b = ev(), ev()
+        a.record(stream)
+        c.attend(q, 15, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    flop = 4.0 * Hs * q.shape[0] * c.info()["n_valid"] * D
+    return {"attend_5head_share_ms": round(ms, 4), "attend_5head_share_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+
+def block_causal_clip(dev, stream, ev, w, block_frames=3):
+    """Block-causal attention of the Wan-1.3B 21-frame clip (32760 query rows, 12 heads) over the cache
+    that holds it, in blocks of 3 frames: block b's 4680 rows see (b + 1) * 4680 keys."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import chunk_inputs
+    S, D, H, F = w.frame_seqlen, w.head_dim, w.heads, w.total_frames
+    c = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16)
+    for i in range(w.n_chunks):
+        _, k, v = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, i))
+        c.append(k, v, w.chunk_start_frame(i))
+    (q,) = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, 99, tensors=(0,), frames=F))
+    out = c.attend_block_causal(q, 0, block_frames)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(8):
+        a, b = ev(), ev()
+        a.record(stream)
+        c.attend_block_causal(q, 0, block_frames, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    cb = block_frames * S
+    n = c.info()["n_valid"]
+    vis = sum(min(n, (r // cb + 1) * cb) * min(cb, F * S - r) for r in range(0, F * S, cb))
+    flop = 4.0 * H * D * vis
+    return {"block_causal_clip_ms": round(ms, 4), "block_causal_clip_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
 
 
 def vendor_context(dev, stream, H, N, Lk, D):

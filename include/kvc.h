@@ -144,6 +144,20 @@ kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_fram
  * overlap on different streams. */
 kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out);
 
+/* Block-causal attention of a whole clip (the clip-level training /
+ * teacher-forcing path: rCM length-extrapolation article, block-level
+ * attention mask; Causal-Forcing article, section 4, a 21-frame clip split
+ * into blocks of num_frame_per_block frames).  Query frame f (rotated at
+ * q_t_index + f, as in kvc_attend) belongs to block f / block_frames and
+ * attends to the first min(n_valid, (block + 1) * block_frames *
+ * frame_seqlen) cached entries in logical order -- i.e. to blocks 0..its own
+ * when the cache holds the clip from its first frame.  q, out as in
+ * kvc_attend.  EINVAL for block_frames outside 1..KVC_MAX_Q_FRAMES;
+ * EUNSUPPORTED once the window ring has wrapped or the sink rolled (logical
+ * order no longer equals slot order); ESTATE if the cache is empty. */
+kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index,
+                                  int32_t block_frames, void* out);
+
 /* Shift the time index of logical entries [slot_lo, slot_hi) by delta
  * (clamped at 0 when clamp0 != 0) and re-rotate their stored keys' time band
  * in place by the actual change.  Logical order: sink oldest..newest, then

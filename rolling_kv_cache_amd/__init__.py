@@ -3,7 +3,7 @@
 Thin ctypes binding over ``libkvc.so`` (C ABI in ``include/kvc.h``).  PyTorch
 only provides device memory and the stream; every step of the cache runs in
 the library's HIP kernels.  Importing this package fails loudly when the
-library has not been built (``python -m rolling_kv_cache_amd.build``).
+library has not been built (``python rolling_kv_cache_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ KVC_MAX_Q_FRAMES = 32
 
 # Every symbol include/kvc.h declares.
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
-            "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_compact", "kvc_sink_push", "kvc_info",
+            "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_compact", "kvc_sink_push", "kvc_info",
             "kvc_slot_times", "kvc_export", "kvc_export_tables", "kvc_last_error")
 
 
@@ -47,7 +47,7 @@ class _Info(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rolling_kv_cache_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python rolling_kv_cache_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, u32, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
     p32, p64, pf = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_float)
@@ -59,6 +59,7 @@ def _load():
         "kvc_set_stream": (ctypes.c_int, [vp, vp]),
         "kvc_append": (ctypes.c_int, [vp, vp, vp, i32, i32, u32]),
         "kvc_attend": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+        "kvc_attend_blockcausal": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
         "kvc_retime": (ctypes.c_int, [vp, i32, i32, i32, i32]),
         "kvc_score_scratch_bytes": (sz, [vp, i32]),
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
@@ -165,6 +166,15 @@ class KVCache:
             out = torch.empty_like(q)
         _check(lib.kvc_attend(self._h, self._tensor(q, F, "q"), F, KVC_T_NEWEST if t_index is None else int(t_index),
                               self._tensor(out, F, "out")))
+        return out
+
+    def attend_block_causal(self, q, t_index, block_frames: int, out=None):
+        """Block-causal attention of a whole clip held by this cache from its first frame."""
+        F = self._frames_of(q)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib.kvc_attend_blockcausal(self._h, self._tensor(q, F, "q"), F, int(t_index), int(block_frames),
+                                          self._tensor(out, F, "out")))
         return out
 
     def retime(self, delta: int, clamp0: bool = False, lo: int = 0, hi=None):

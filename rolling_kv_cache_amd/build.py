@@ -1,6 +1,6 @@
 """Build libkvc.so (HIP for gfx950) and the host-only ring planner library, in-tree.
 
-    python -m rolling_kv_cache_amd.build
+    python rolling_kv_cache_amd/build.py
 
 Always recompiles.  Objects go to <repo>/_build (ignored by git); the shared
 libraries land next to this file so they travel with the source tree.

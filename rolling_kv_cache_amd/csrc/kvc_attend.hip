@@ -399,7 +399,12 @@ __device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* l
 }
 
 // With only_flagged set, blocks whose flag is 0 exit at once (the recompute
-// pass behind the fixed-reference kernel).
+// pass behind the fixed-reference kernel).  CAUSAL: block-causal attention of
+// a clip -- query row r sees the logical key prefix of length
+// min(n, (r / causal_block + 1) * causal_block); a workgroup loops only over
+// the tiles its longest prefix needs, rows whose prefix ends inside a tile mask
+// the rest per lane, and workgroups with the longest prefixes start first.
+template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles, const int32_t* only_flagged) {
   __shared__ u32x4_t lks[2][kKTileP];
@@ -409,14 +414,36 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   if (lin >= total) return;
   if (only_flagged != nullptr && only_flagged[lin] == 0) return;
   const int h = lin / mblocks;
-  const int mb = lin - h * mblocks;
+  const int mb = CAUSAL ? mblocks - 1 - (lin - h * mblocks) : lin - h * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
   const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
-  const int last = ntiles - 1;
+  int nt = ntiles, lim = 0, lim_lo = 0;
+  if (CAUSAL) {
+    const int cb = a.causal_block, nall = a.keys.n[0] + a.keys.n[1];
+    auto limit = [&](int r) { return min(nall, (r / cb + 1) * cb); };
+    const int r0 = mb * 256, r1 = min(a.Lq, r0 + 256) - 1;
+    lim_lo = limit(r0);
+    lim = limit(min(qrow, a.Lq - 1));
+    const int lim_hi = limit(r1), n0 = a.keys.n[0];
+    nt = lim_hi <= n0 ? (lim_hi + kBN - 1) / kBN : ntile0 + (lim_hi - n0 + kBN - 1) / kBN;
+  }
+  const int last = nt - 1;
+  // mask tile t: slots past the region's valid prefix, and (causal) keys past this row's prefix
+  auto mask = [&](f32x16_t* s, int t) {
+    const int nv = ts.valid(t);
+    if (CAUSAL) {
+      const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
+      if (lb + kBN > lim_lo) {
+        mask_tile(s, min(nv, lim - lb), hl);
+        return;
+      }
+    }
+    mask_tile(s, nv, hl);
+  };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
 
   Stage5 st;
@@ -448,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
       sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
     }
   }
-  mask_tile(sa, ts.valid(0), hl);
+  mask(sa, 0);
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
@@ -465,17 +492,17 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     }
     lsum = lsum * alpha + psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
-    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    mask(snext, min(t + 1, last));
     store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
 
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  for (; t + 1 < nt; t += 2) {
     step(t, sa, sb);
     step(t + 1, sb, sa);
   }
-  if (t < ntiles) step(t, sa, sb);
+  if (t < nt) step(t, sa, sb);
   store_out(a, o, lsum, qrow, h, hl);
 }
 
@@ -828,7 +855,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
 
 template <int VAR>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int bm = (VAR == 2 || VAR == 4) ? 256 : kBM;
+  const int bm = (VAR == 2 || VAR == 4 || VAR == 5) ? 256 : kBM;
   const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
@@ -849,13 +876,16 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     nt = ntile1;
   }
   if (VAR == 2)
-    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt,
-                       (const int32_t*)nullptr);
+    hipLaunchKernelGGL(attend_v5_kernel<false>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
+                       nt, (const int32_t*)nullptr);
+  else if (VAR == 5)
+    hipLaunchKernelGGL(attend_v5_kernel<true>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
+                       nt, (const int32_t*)nullptr);
   else if (VAR == 4) {
     hipLaunchKernelGGL(attend_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_v5_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt,
-                       (const int32_t*)b.flags);
+    hipLaunchKernelGGL(attend_v5_kernel<false>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
+                       nt, (const int32_t*)b.flags);
   }
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
@@ -867,6 +897,7 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
 // KVC_ATTEND_VARIANT=v5 (running maximum, 8 waves) or v3 (4 waves, two
 // workgroups per CU) selects another kernel for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
+  if (a.causal_block > 0) return attend_launch<5>(a, s);
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
   if (v && std::string(v) == "v3") return attend_launch<0>(a, s);
   if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2>(a, s);

@@ -120,6 +120,7 @@ struct AttendArgs {
   Tables tab;
   float scale;                            // 1/sqrt(D)
   int32_t* flags;                         // workspace: one recompute flag per 256-query attention block
+  int32_t causal_block;                   // > 0: query row r sees the logical key prefix min(n, (r/cb+1)*cb)
 };
 
 struct ScoreArgs {

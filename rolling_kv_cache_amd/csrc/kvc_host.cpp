@@ -352,8 +352,8 @@ kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_fram
   return KVC_OK;
 }
 
-kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out) {
-  if (kvc_status s = check(h)) return s;
+static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out,
+                              int32_t causal_block) {
   if (!q || !out) return fail(KVC_EINVAL, "q/out null");
   if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
   if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "attend on an empty cache");
@@ -374,9 +374,25 @@ kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t
   a.tab = h->tab;
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
   a.flags = h->att_flags;
+  a.causal_block = causal_block;
   const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
   hipError_t e = kvc::launch_attend(a, h->stream, force_general);
   return device_result(h, e, "attend");
+}
+
+kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out) {
+  if (kvc_status s = check(h)) return s;
+  return attend_impl(h, q, q_frames, q_t_index, out, 0);
+}
+
+kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index,
+                                  int32_t block_frames, void* out) {
+  if (kvc_status s = check(h)) return s;
+  if (block_frames < 1 || block_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "block_frames out of range");
+  // key prefixes are taken in logical order, which must coincide with slot order
+  if (h->st.hs != 0 || h->st.hw != 0)
+    return fail(KVC_EUNSUPPORTED, "block-causal attention needs an unrolled cache (sink and window heads at 0)");
+  return attend_impl(h, q, q_frames, q_t_index, out, block_frames * h->S);
 }
 
 kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi) {

@@ -567,9 +567,13 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
   float o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) o[d] = 0.f;
+  // block-causal: this row sees the first lim entries in logical order (sink region first)
+  const int nall = a.keys.n[0] + a.keys.n[1];
+  const int lim = a.causal_block > 0 ? min(nall, (i / a.causal_block + 1) * a.causal_block) : nall;
   for (int r = 0; r < 2; ++r) {
     const T* vbase = (const T*)a.keys.v[r];
-    for (int j = 0; j < a.keys.n[r]; ++j) {
+    const int nr = min(a.keys.n[r], lim - (r == 0 ? 0 : a.keys.n[0]));
+    for (int j = 0; j < nr; ++j) {
       const float s = key_dot<T, D>(qv, a.keys, r, h, j, g) * a.scale;
       const float mn = fmaxf(m, s);
       const float alpha = expf(m - mn);

@@ -92,3 +92,28 @@ def test_c5a_infinity_rope():
 @pytest.mark.timeout(900)
 def test_c5b_deep_forcing():
     _run_config("c5b", full_rows_at=(7,), compact=True, sample_rows=256)
+
+
+@pytest.mark.timeout(900)
+def test_c2_clip_block_causal():
+    """The Wan-1.3B 21-frame clip (32760 query rows, 12 heads) attended block-causally in blocks of 3 frames
+    over the cache that holds it: 512 sampled rows plus the first and last row of every block."""
+    from oracle import OracleCache
+    w = WORKLOADS["c2"]
+    S = w.frame_seqlen
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, S, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(w.n_chunks):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), w.chunk_start_frame(i))
+        oc.append(k, v, w.chunk_frames[i], w.chunk_start_frame(i))
+    F = w.total_frames
+    (q,) = chunk_inputs(w, 99, tensors=(0,), frames=F)
+    with Timer("c2 clip block-causal"):
+        out = gc.attend_block_causal(dev(q, w), 0, 3).float().cpu().numpy()
+    rng = np.random.default_rng(4321)
+    cb = 3 * S
+    edges = np.concatenate([np.arange(0, F * S, cb), np.arange(cb - 1, F * S, cb)])
+    rows = np.unique(np.concatenate([rng.choice(F * S, size=512, replace=False), edges]))
+    mx, rr = check_attention(out[rows], oc.attend_block_causal(q, F, 0, 3, rows=rows), "c2 clip block-causal")
+    log(f"c2 clip block-causal: max_abs {mx:.3e} rel_rms {rr:.3e} on {rows.shape[0]} rows")

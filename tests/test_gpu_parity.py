@@ -221,3 +221,67 @@ def test_compact_validation():
             gc.compact(keep)
     gc.compact(list(range(32)) + [40, 70, 71, 127])
     assert gc.info()["n_valid"] == 36
+
+
+# ---------------------------------------------------------------- block-causal attention of a whole clip
+def _clip(w, frames, chunk=2):
+    """Cache (GPU and oracle) holding `frames` frames appended chunk by chunk from time 0, plus the clip's
+    queries."""
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    f = 0
+    i = 0
+    while f < frames:
+        n = min(chunk, frames - f)
+        _, k, v = chunk_inputs(w, i, frames=n)
+        gc.append(dev(k, w), dev(v, w), f)
+        oc.append(k, v, n, f)
+        f += n
+        i += 1
+    (q,) = chunk_inputs(w, 99, tensors=(0,), frames=frames)
+    return gc, oc, q
+
+
+@pytest.mark.parametrize("general", [False, True])
+@pytest.mark.parametrize("sink,block", [(0, 2), (1, 3), (1, 8), (0, 1)])
+def test_block_causal_small(general, sink, block):
+    """207-token frames (a block boundary every 207*block rows, never on a 64-key or 256-row tile edge), a
+    sink region or none, a last block cut short (8 frames in blocks of 3), one block (full attention) and
+    frame-wise causality (block 1)."""
+    w = Workload("bc", 210, 2, 128, "bf16", 9, 23, sink, 8 - sink, (2,) * 4)
+    gc, oc, q = _clip(w, 8)
+    if general:
+        os.environ["KVC_ATTEND_GENERAL"] = "1"
+    try:
+        out = gc.attend_block_causal(dev(q, w), 0, block).float().cpu().numpy()
+    finally:
+        os.environ.pop("KVC_ATTEND_GENERAL", None)
+    check_attention(out, oc.attend_block_causal(q, 8, 0, block), f"block-causal sink {sink} block {block}")
+    if block >= 8:
+        check_attention(out, gc.attend(dev(q, w), 0).float().cpu().numpy(), "one block == attend")
+
+
+def test_block_causal_partial_cache_and_time_offset():
+    """The clip's queries see only what the cache holds (6 of 8 frames cached), rotated from t0 = 5."""
+    w = Workload("bcp", 211, 2, 128, "bf16", 9, 23, 0, 8, (2,) * 3)
+    gc, oc, _ = _clip(w, 6)
+    (q,) = chunk_inputs(w, 98, tensors=(0,), frames=8)
+    out = gc.attend_block_causal(dev(q, w), 5, 3).float().cpu().numpy()
+    check_attention(out, oc.attend_block_causal(q, 8, 5, 3), "block-causal partial cache")
+
+
+def test_block_causal_errors():
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("bce", 212, 2, 128, "bf16", 4, 8, 1, 3, (1,) * 6)
+    gc, _, q = _clip(w, 4, chunk=1)
+    qd = dev(q, w)
+    for bad in (0, 33):
+        with pytest.raises(KVCError) as e:
+            gc.attend_block_causal(qd, 0, bad)
+        assert e.value.code == 1
+    gc.attend_block_causal(qd, 0, 2)                              # sink full, window full, heads at 0
+    _, k, v = chunk_inputs(w, 50, frames=1)
+    gc.append(dev(k, w), dev(v, w), 4)                            # evicts: the window head moves
+    with pytest.raises(KVCError) as e:
+        gc.attend_block_causal(qd, 0, 2)
+    assert e.value.code == 5
