@@ -18,7 +18,7 @@ references.  Sources it follows (cited by page and section throughout):
   current block's queries attend to cached history plus the new block.
 * rCM length-extrapolation article (dpshk.com/news/6097349): Rolling Sink bank,
   Infinity-RoPE shift/clamp/flush/cut, Deep-Forcing scoring and compaction,
-  in-place time re-rotation.
+  in-place time re-rotation, Relax Forcing frame selection.
 * Rolling Sink paper summary (paper.rainbus.top/paper/2602.07775), "method step
   details": Cat(x[0,S), x[i-(K-S), i)), sliding indices, Roll with
   forward/reverse alternation.
@@ -36,11 +36,13 @@ from .cache import OracleCache, OracleError
 from .attention import attention_f32, attention_f64, attention_loops_f64
 from .score import attention_mass_scores
 from .policies import (SlidingWindowRun, RollingSinkRun, InfinityRopeRun, DeepForcingRun,
-                       roll_index, make_run)
+                       RelaxForcingRun, roll_index, make_run)
+from .relax import relax_frame_scores, top_frames
 
 __all__ = [
     "round_to_bf16", "bf16_ulp", "band_split", "inv_freq", "cos_sin_table", "token_positions",
     "rotate_f32", "rotate_f64", "OracleCache", "OracleError", "attention_f32", "attention_f64",
     "attention_loops_f64", "attention_mass_scores", "SlidingWindowRun", "RollingSinkRun",
-    "InfinityRopeRun", "DeepForcingRun", "roll_index", "make_run",
+    "InfinityRopeRun", "DeepForcingRun", "RelaxForcingRun", "roll_index", "make_run",
+    "relax_frame_scores", "top_frames",
 ]

@@ -36,6 +36,7 @@ from .bf16 import round_to_bf16
 from .rope import band_split, rotate_f32, token_positions
 from .attention import attention_f32, attention_f64
 from .score import attention_mass_scores
+from .relax import relax_frame_scores
 
 
 class OracleError(ValueError):
@@ -243,6 +244,18 @@ class OracleCache:
             n_vis = min(self.n, int(b + 1) * block_frames * self.S)
             out[sel] = fn(qh[rows[sel]], self.K[:n_vis], self.V[:n_vis])
         return out
+
+    def relax_scores(self, tail_frames, weight=0.5):
+        """Relax Forcing scores of the History candidates: the whole frames between the sink and the
+        last tail_frames frames (which form the Tail).  The cache must hold whole frames."""
+        S = self.S
+        if self.n % S or self.n_sink % S:
+            raise OracleError("relax scores need whole frames")
+        first = self.n_sink // S
+        n_cand = self.n // S - tail_frames - first
+        if tail_frames < 1 or n_cand < 1:
+            raise OracleError("relax scores need a tail and at least one candidate")
+        return relax_frame_scores(self.K, S, first, n_cand, tail_frames, weight)
 
     def score(self, q_win, frames, t_frames, f64=False):
         """Per-entry attention mass of the query window, summed over heads and query rows."""

@@ -17,6 +17,9 @@ performs chunk i's cache operations and returns its attention output.
 * DeepForcingRun -- Deep Forcing (rCM article, strategy 4): keep Deep Sink +
   Top-C tokens by attention score + Recent Tail, compact, then close the time
   holes of the sink and compressed regions in place.
+* RelaxForcingRun -- Relax Forcing (rCM article, strategy 5): the same Sink +
+  kept history + Tail shape, with whole History frames chosen by cosine
+  alignment with the Tail plus a complement bonus (see relax.py).
 
 Readings (the pages leave these open): a block is one chunk of 3 frames; for
 Rolling Sink the segment of Roll read at step i starts at i-K, so at i = K the
@@ -32,6 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .cache import OracleCache
+from .relax import top_frames
 
 
 def roll_index(n: int, K: int) -> int:
@@ -143,13 +147,64 @@ class DeepForcingRun:
             if keep_override is not None:
                 keep = np.asarray(keep_override, dtype=np.int64)
             c.compact(keep)
-            n_comp = keep.shape[0] - c.S_tok - self.R
-            comp = (c.S_tok, c.S_tok + n_comp)
-            tail = (comp[1], c.n)
-            d_c = (int(c.t[tail[0]:tail[1]].min()) - 1) - int(c.t[comp[0]:comp[1]].max())
-            c.retime(d_c, False, comp[0], comp[1])
-            d_s = (int(c.t[comp[0]:comp[1]].min()) - 1) - int(c.t[0:c.S_tok].max())
-            c.retime(d_s, False, 0, c.S_tok)
+            d_c, d_s = _close_gaps(c, keep.shape[0] - c.S_tok - self.R)
+            self.last.update({"d_c": d_c, "d_s": d_s})
+        c.append(k, v, F, t0)
+        return c.attend(q, F, t0, rows=rows, f64=f64)
+
+
+def _close_gaps(c, n_comp):
+    """After compaction to sink + n_comp compressed entries + tail: shift the compressed region so it ends
+    one frame before the tail starts, then the sink so it ends one frame before the compressed region
+    starts (one time delta per region, no clamp)."""
+    comp = (c.S_tok, c.S_tok + n_comp)
+    d_c = (int(c.t[comp[1]:c.n].min()) - 1) - int(c.t[comp[0]:comp[1]].max())
+    c.retime(d_c, False, comp[0], comp[1])
+    d_s = (int(c.t[comp[0]:comp[1]].min()) - 1) - int(c.t[0:c.S_tok].max())
+    c.retime(d_s, False, 0, c.S_tok)
+    return d_c, d_s
+
+
+class RelaxForcingRun:
+    """Relax Forcing (rCM article, strategy 5): Sink + History + Tail.  On the same trigger as Deep
+    Forcing (the next chunk does not fit), the History candidates -- whole frames between the sink and
+    the Tail (the last recent_frames frames) -- are scored by cosine alignment with the Tail plus the
+    complement bonus (relax_frame_scores), the Top-K frames are kept whole, the cache is compacted and
+    the time gaps are closed as for Deep Forcing."""
+
+    def __init__(self, w, top_frames=4, recent_frames=2, weight=0.5):
+        self.w = w
+        self.K = top_frames
+        self.Rf = recent_frames
+        self.R = recent_frames * w.frame_seqlen
+        self.weight = weight
+        self.cache = _cache_for(w)
+        self.last = {}
+
+    def needs_compaction(self, i):
+        return self.cache.n + self.w.chunk_frames[i] * self.w.frame_seqlen > self.cache.C_tok
+
+    def select(self, scores):
+        c = self.cache
+        S = self.w.frame_seqlen
+        frames = c.n_sink // S + top_frames(scores, self.K)
+        hist = (frames[:, None] * S + np.arange(S)[None, :]).reshape(-1)
+        return np.concatenate([np.arange(c.n_sink), hist, np.arange(c.n - self.R, c.n)]).astype(np.int64)
+
+    def step(self, i, q, k, v, keep_override=None, rows=None, f64=False, **_):
+        c = self.cache
+        w = self.w
+        F = w.chunk_frames[i]
+        t0 = w.chunk_start_frame(i)
+        self.last = {}
+        if self.needs_compaction(i):
+            scores = c.relax_scores(self.Rf, self.weight)
+            keep = self.select(scores)
+            self.last = {"scores": scores, "keep": keep}
+            if keep_override is not None:
+                keep = np.asarray(keep_override, dtype=np.int64)
+            c.compact(keep)
+            d_c, d_s = _close_gaps(c, keep.shape[0] - c.S_tok - self.R)
             self.last.update({"d_c": d_c, "d_s": d_s})
         c.append(k, v, F, t0)
         return c.attend(q, F, t0, rows=rows, f64=f64)
@@ -157,5 +212,5 @@ class DeepForcingRun:
 
 def make_run(w):
     """Run of a workload by name prefix; anything else is a plain sliding window / global cache."""
-    return {"c4": RollingSinkRun, "c5a": InfinityRopeRun, "c5b": DeepForcingRun}.get(
+    return {"c4": RollingSinkRun, "c5a": InfinityRopeRun, "c5b": DeepForcingRun, "c5c": RelaxForcingRun}.get(
         w.name.split("_")[0], SlidingWindowRun)(w)

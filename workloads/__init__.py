@@ -81,6 +81,8 @@ WORKLOADS = {
                     cut_chunks=(7, 20, 34)),
     # Deep-Forcing token compaction on the same shape, absolute times
     "c5b": Workload("c5b", 5, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,)),
+    # Relax Forcing frame selection on the same shape (sink 3 + History 4 + Tail 2 frames kept)
+    "c5c": Workload("c5c", 6, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,)),
 }
 
 
