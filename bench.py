@@ -229,10 +229,11 @@ def main():
 
 
 def sink_push_and_compact(dev, stream, flush, ev):
-    """The two remaining data-movement kernels at their workloads' shapes, MALL flushed before each sample:
+    """The remaining data-movement kernels at their workloads' shapes, MALL flushed before each sample:
     a Rolling-Sink push of one 3-frame bank block (12 heads x 1560-token frames, 15 sink + 6 window frames,
     18-frame bank) and a Deep-Forcing compaction keeping the 3-frame sink plus 9360 of 28080 window entries
-    (12 heads, 3 sink + 18 window frames).  Bytes = read + write of K and V for every moved entry."""
+    (12 heads, 3 sink + 18 window frames); bytes = read + write of K and V for every moved entry.  Then the
+    Relax Forcing frame scores of the full cache of that shape; bytes = the keys read."""
     import numpy as np
     import torch
     import rolling_kv_cache_amd as kvc
@@ -289,6 +290,20 @@ def sink_push_and_compact(dev, stream, flush, ev):
     byt = 4.0 * (len(keep) - ns) * H * D * 2
     out["compact_us_cold"] = round(us, 2)
     out["compact_GBps_cold"] = round(byt / (us * 1e-6) / 1e9, 1)
+
+    # Relax Forcing scores on the full 3 + 18-frame cache (same shape, c5c): 16 candidate frames and a
+    # 2-frame Tail, i.e. the keys of 18 frames read once (frame sums), then the Gram matrix and the scores
+    sc = torch.empty(64, dtype=torch.float32, device=dev)
+
+    def relax(i, timed):
+        if not timed:
+            fill()
+        else:
+            c5.relax_scores(2, 0.5, out=sc)
+    us = cold(relax)
+    byt = 18.0 * S * H * D * 2
+    out["relax_scores_us_cold"] = round(us, 2)
+    out["relax_scores_GBps_cold"] = round(byt / (us * 1e-6) / 1e9, 1)
     return out
 
 

@@ -177,6 +177,30 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
                      void* scratch, size_t scratch_bytes);
 
+/* Device scratch bytes kvc_relax_scores needs (depends only on the cache
+ * geometry). */
+size_t kvc_relax_scratch_bytes(kvc_handle h);
+
+/* Relax Forcing frame scores (rCM length-extrapolation article, strategy 5:
+ * the cache is Sink + History + Tail; History frames are ranked by
+ * score = weight * alignment + (1 - weight) * complement and the Top-K kept).
+ * The cache must hold whole frames: frame f is logical entries [f * S,
+ * (f + 1) * S).  The Tail is the last tail_frames frames; the candidates are
+ * the n_cand = n_valid / S - sink_filled / S - tail_frames frames between the
+ * sink and the Tail.  With x_f the sum of frame f's stored keys over its
+ * tokens (flattened over heads and dims) and x_T the sum over the Tail's:
+ *   alignment(f)  = cos(x_f, x_T)
+ *   complement(f) = 1 - mean over the other candidates g of cos(x_f, x_g)
+ *                   (1 when f is the only candidate)
+ * with cos = 0 when either vector is zero.  scores: device float[n_cand], in
+ * candidate order; scratch: device, 256-byte aligned, >=
+ * kvc_relax_scratch_bytes.  EINVAL if a frame is partial, tail_frames < 1,
+ * no candidate is left, weight is outside [0, 1] or a pointer is null;
+ * ENOMEM if the scratch is too small; EUNSUPPORTED for more than 64 frames
+ * (candidates + Tail) in one call.  The cache state is not changed. */
+kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
+                            size_t scratch_bytes);
+
 /* Keep exactly the logical entries keep_idx[0..n_keep) (host int32, sorted,
  * unique, in [0, n_valid), containing every sink entry), packed in that
  * order; window entries are gathered into the other window buffer.  Requires

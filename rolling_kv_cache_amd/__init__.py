@@ -26,7 +26,8 @@ KVC_MAX_Q_FRAMES = 32
 
 # Every symbol include/kvc.h declares.
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
-            "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_compact", "kvc_sink_push", "kvc_info",
+            "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
+            "kvc_relax_scores", "kvc_compact", "kvc_sink_push", "kvc_info",
             "kvc_slot_times", "kvc_export", "kvc_export_tables", "kvc_last_error")
 
 
@@ -63,6 +64,8 @@ def _load():
         "kvc_retime": (ctypes.c_int, [vp, i32, i32, i32, i32]),
         "kvc_score_scratch_bytes": (sz, [vp, i32]),
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
+        "kvc_relax_scratch_bytes": (sz, [vp]),
+        "kvc_relax_scores": (ctypes.c_int, [vp, i32, ctypes.c_float, vp, vp, sz]),
         "kvc_compact": (ctypes.c_int, [vp, p32, i32]),
         "kvc_sink_push": (ctypes.c_int, [vp, i32, i32, i32]),
         "kvc_info": (ctypes.c_int, [vp, ctypes.POINTER(_Info)]),
@@ -123,6 +126,7 @@ class KVCache:
                               ctypes.c_void_p(self._stream.cuda_stream), ctypes.byref(h)))
         self._h = h
         self._score_scratch = None
+        self._relax_scratch = None
 
     def close(self):
         if getattr(self, "_h", None):
@@ -198,6 +202,23 @@ class KVCache:
         _check(lib.kvc_score(self._h, self._tensor(q_win, F, "q_win"), F,
                              q_t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.c_void_p(out.data_ptr()),
                              ctypes.c_void_p(self._score_scratch.data_ptr() + off), need))
+        return out
+
+    def relax_scores(self, tail_frames: int, weight: float = 0.5, out=None):
+        """Relax Forcing scores of the whole frames between the sink and the last tail_frames frames."""
+        info = self.info()
+        n_cand = max(1, info["n_valid"] // self.S - info["sink_filled"] // self.S - int(tail_frames))
+        need = int(lib.kvc_relax_scratch_bytes(self._h))
+        if self._relax_scratch is None or self._relax_scratch.numel() < need + 256:
+            self._relax_scratch = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+        off = (-self._relax_scratch.data_ptr()) % 256
+        if out is None:
+            out = torch.empty(n_cand, dtype=torch.float32, device=self.device)
+        elif (out.device.type != "cuda" or out.dtype != torch.float32 or not out.is_contiguous()
+              or out.numel() < n_cand):
+            raise ValueError("out must be a contiguous float32 CUDA tensor of at least n_cand elements")
+        _check(lib.kvc_relax_scores(self._h, int(tail_frames), float(weight), ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(self._relax_scratch.data_ptr() + off), need))
         return out
 
     def compact(self, keep_idx):

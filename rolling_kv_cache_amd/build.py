@@ -28,7 +28,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-fno-gpu-rdc", "-I" + INC, "-I" + CSRC]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INC, "-I" + CSRC]
 
-HIP_SOURCES = ["kvc_kernels.hip", "kvc_attend.hip"]
+HIP_SOURCES = ["kvc_kernels.hip", "kvc_attend.hip", "kvc_relax.hip"]
 HOST_SOURCES = ["kvc_host.cpp"]
 
 

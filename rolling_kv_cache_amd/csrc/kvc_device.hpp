@@ -139,4 +139,21 @@ struct ScoreArgs {
   float scale;
 };
 
+struct RelaxArgs {
+  KeyRegions keys;                        // ka / kb / cap of the sink and current window
+  int32_t ns, hs, S_tok, nw, hw, W_tok;   // logical -> physical map
+  int32_t first;                          // logical frame of candidate 0
+  int32_t n_cand, n_tail;                 // candidates, then the Tail frames right after them
+  int32_t nsl;                            // token slices per frame
+  float* part;                            // scratch: key sums [n_cand + n_tail][nsl][H * D]
+  float* xsum;                            // scratch: frame key sums [n_cand + n_tail][H * D]
+  float* gram;                            // scratch: [n_cand + n_tail]^2, upper triangle <x_i, x_j>
+  float* scores;                          // out: [n_cand]
+  float weight;
+  Geo geo;
+};
+
+constexpr int kRelaxSlice = 256;          // tokens per frame-sum workgroup
+constexpr int kRelaxMaxFrames = 64;       // candidates + Tail frames per relax call (Gram matrix in LDS)
+
 }  // namespace kvc

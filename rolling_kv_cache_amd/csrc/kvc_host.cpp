@@ -469,6 +469,54 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   return device_result(h, e, "score");
 }
 
+static int32_t relax_slices(kvc_handle h) { return (h->S + kvc::kRelaxSlice - 1) / kvc::kRelaxSlice; }
+
+size_t kvc_relax_scratch_bytes(kvc_handle h) {
+  if (!h) return 0;
+  const size_t nf = (size_t)(h->st.S_tok + h->st.W_tok) / h->S;   // at most this many whole frames
+  return align_up(nf * relax_slices(h) * h->H * h->D * 4) + align_up(nf * h->H * h->D * 4) +
+         align_up((size_t)kvc::kRelaxMaxFrames * kvc::kRelaxMaxFrames * 4);
+}
+
+kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
+                            size_t scratch_bytes) {
+  if (kvc_status s = check(h)) return s;
+  if (!scores || !scratch) return fail(KVC_EINVAL, "null argument");
+  if (!(weight >= 0.f && weight <= 1.f)) return fail(KVC_EINVAL, "weight outside [0, 1]");
+  if (scratch_bytes < kvc_relax_scratch_bytes(h)) return fail(KVC_ENOMEM, "relax scratch too small");
+  if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
+  const int32_t n = h->st.n_valid(), ns = h->st.ns, S = h->S;
+  if (n % S != 0 || ns % S != 0) return fail(KVC_EINVAL, "relax scores need whole frames in the cache");
+  if (tail_frames < 1) return fail(KVC_EINVAL, "tail_frames must be >= 1");
+  const int32_t n_cand = n / S - ns / S - tail_frames;
+  if (n_cand < 1) return fail(KVC_EINVAL, "no candidate frame between the sink and the tail");
+  if (n_cand + tail_frames > kvc::kRelaxMaxFrames)
+    return fail(KVC_EUNSUPPORTED, "relax scores take at most 64 frames (candidates + tail)");
+  const int32_t CH = h->D * h->geo.esz / 16;
+  if (256 % CH != 0) return fail(KVC_EUNSUPPORTED, "head_dim not supported by the frame sums");
+  kvc::RelaxArgs a{};
+  a.keys = key_regions(h);
+  a.ns = ns;
+  a.hs = h->st.hs;
+  a.S_tok = std::max(1, h->st.S_tok);
+  a.nw = h->st.nw;
+  a.hw = h->st.hw;
+  a.W_tok = h->st.W_tok;
+  a.first = ns / S;
+  a.n_cand = n_cand;
+  a.n_tail = tail_frames;
+  a.nsl = relax_slices(h);
+  const size_t nfc = (size_t)(h->st.S_tok + h->st.W_tok) / S;
+  a.part = (float*)scratch;
+  a.xsum = (float*)((char*)scratch + align_up(nfc * a.nsl * h->H * h->D * 4));
+  a.gram = (float*)((char*)a.xsum + align_up(nfc * h->H * h->D * 4));
+  a.scores = scores;
+  a.weight = weight;
+  a.geo = h->geo;
+  hipError_t e = kvc::launch_relax(a, h->stream);
+  return device_result(h, e, "relax scores");
+}
+
 kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
   if (kvc_status s = check(h)) return s;
   if (!(h->cflags & KVC_CREATE_COMPACT)) return fail(KVC_EUNSUPPORTED, "compact needs KVC_CREATE_COMPACT");

@@ -19,6 +19,8 @@ hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
 // Scores: the matrix-core passes for bf16 with head_dim 128, else the general
 // per-row/per-column path (force_general selects the latter).
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general);
+// frame sums, their Gram matrix, then the Relax Forcing scores
+hipError_t launch_relax(const RelaxArgs& a, hipStream_t s);
 // rows + columns passes over a query window already rotated into qbf
 // ([H][Nq][128] bf16); writes a.m (log2 normaliser per row) and a.part
 hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s);

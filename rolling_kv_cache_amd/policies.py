@@ -23,6 +23,9 @@ A schedule object needs ``chunk_frames`` (frames per chunk, in stream order),
   does not fit, score entries by the attention mass the previous chunk's
   queries give them, keep the sink, the Top-C candidates and the recent tail,
   compact, and close the time gaps of the compressed region and the sink.
+* RelaxForcing -- Relax Forcing (rCM article, strategy 5): the same shape of
+  kept cache, with whole History frames chosen by cosine alignment of their
+  keys with the Tail plus a complement bonus.
 """
 from __future__ import annotations
 
@@ -121,20 +124,63 @@ class DeepForcing:
             keep = self.keep_set(scores, info["n_valid"], sink)
             self.last = {"scores": scores, "keep": keep}
             c.compact(keep)
-            t, _ = c.slot_times()
-            n_comp = keep.shape[0] - sink - self.R
-            lo, hi = sink, sink + n_comp
-            d_c = (int(t[hi:].min()) - 1) - int(t[lo:hi].max())
-            c.retime(d_c, False, lo, hi)
-            t, _ = c.slot_times()
-            d_s = (int(t[lo:hi].min()) - 1) - int(t[:sink].max())
-            c.retime(d_s, False, 0, sink)
+            d_c, d_s = _close_gaps(c, sink, keep.shape[0] - sink - self.R)
             self.last.update({"d_c": d_c, "d_s": d_s})
         t0 = _start_frame(self.sched, i)
         c.append(k, v, t0)
         return c.attend(q, t0)
 
 
+class RelaxForcing:
+    """Relax Forcing (rCM article, strategy 5): on the same trigger as Deep Forcing, score the whole
+    frames between the sink and the Tail (the last recent_frames frames) by cosine alignment with the
+    Tail plus a complement bonus (kvc_relax_scores), keep the Top-K frames whole with the sink and the
+    Tail, compact, and close the time gaps as Deep Forcing does."""
+
+    def __init__(self, cache, sched, top_frames=4, recent_frames=2, weight=0.5):
+        self.cache, self.sched = cache, sched
+        self.K, self.Rf, self.weight = top_frames, recent_frames, weight
+        self.last = {}
+
+    def keep_set(self, scores: np.ndarray, n: int, sink: int) -> np.ndarray:
+        S = self.sched.frame_seqlen
+        order = np.argsort(-scores, kind="stable")            # equal scores keep the lower frame first
+        frames = sink // S + np.sort(order[:self.K])
+        hist = (frames[:, None] * S + np.arange(S)[None, :]).reshape(-1)
+        return np.concatenate([np.arange(sink), hist, np.arange(n - self.Rf * S, n)]).astype(np.int32)
+
+    def step(self, i, q, k, v, **_):
+        c = self.cache
+        S = self.sched.frame_seqlen
+        F = self.sched.chunk_frames[i]
+        info = c.info()
+        self.last = {}
+        if info["n_valid"] + F * S > info["capacity"]:
+            scores = c.relax_scores(self.Rf, self.weight).cpu().numpy().astype(np.float64)
+            sink = info["sink_filled"]
+            keep = self.keep_set(scores, info["n_valid"], sink)
+            self.last = {"scores": scores, "keep": keep}
+            c.compact(keep)
+            d_c, d_s = _close_gaps(c, sink, keep.shape[0] - sink - self.Rf * S)
+            self.last.update({"d_c": d_c, "d_s": d_s})
+        t0 = _start_frame(self.sched, i)
+        c.append(k, v, t0)
+        return c.attend(q, t0)
+
+
+def _close_gaps(c, sink, n_comp):
+    """Shift the compressed region to end one frame before the tail, then the sink to end one frame before
+    the compressed region (one time delta each, no clamp)."""
+    t, _ = c.slot_times()
+    lo, hi = sink, sink + n_comp
+    d_c = (int(t[hi:].min()) - 1) - int(t[lo:hi].max())
+    c.retime(d_c, False, lo, hi)
+    t, _ = c.slot_times()
+    d_s = (int(t[lo:hi].min()) - 1) - int(t[:sink].max())
+    c.retime(d_s, False, 0, sink)
+    return d_c, d_s
+
+
 def driver_for(name: str):
     """Policy of a workload by name prefix; anything else is a plain sliding window / global cache."""
-    return {"c4": RollingSink, "c5a": InfinityRope, "c5b": DeepForcing}.get(name.split("_")[0], SlidingWindow)
+    return {"c4": RollingSink, "c5a": InfinityRope, "c5b": DeepForcing, "c5c": RelaxForcing}.get(name.split("_")[0], SlidingWindow)

@@ -285,3 +285,69 @@ def test_block_causal_errors():
     with pytest.raises(KVCError) as e:
         gc.attend_block_causal(qd, 0, 2)
     assert e.value.code == 5
+
+
+# ---------------------------------------------------------------- Relax Forcing frame scores
+RELAX_TOL = 2e-5        # fp32 sums and cosines against the fp64 oracle (scores lie in [-1, 2])
+
+
+@pytest.mark.parametrize("dtype,grid,D", [("bf16", (9, 60), 128), ("f32", (4, 4), 64), ("bf16", (5, 7), 64)])
+def test_relax_scores_match_oracle(dtype, grid, D):
+    """Frames of 540 tokens (three 256-token slices, the last ragged) or 16 / 35 tokens, a two-frame sink,
+    a window that has wrapped (its ring head is not at slot 0), several weights and tail lengths."""
+    w = Workload("rx", 213, 3, D, dtype, grid[0], grid[1], 2, 7, (1,) * 12)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(12):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), i)
+        oc.append(k, v, 1, i)
+    assert gc.info()["n_valid"] == oc.n
+    for tail, wt in ((2, 0.5), (1, 0.3), (5, 1.0), (3, 0.0)):
+        got = gc.relax_scores(tail, wt).cpu().numpy()
+        ref = oc.relax_scores(tail, wt)
+        assert got.shape == ref.shape
+        err = float(np.max(np.abs(got - ref)))
+        log(f"  relax {dtype} D={D} tail {tail} w {wt}: max err {err:.2e}")
+        assert err <= RELAX_TOL, (tail, wt, err)
+
+
+def test_relax_scores_40_heads_and_frame_limit():
+    """40 heads x 128 dims: the Gram pass takes the 5120-long frame sums in two LDS chunks.  Then a cache
+    of 70 one-frame appends: more than 64 frames in one call is refused."""
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("rx40", 216, 40, 128, "bf16", 4, 8, 1, 8, (1,) * 9)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(9):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), i)
+        oc.append(k, v, 1, i)
+    got = gc.relax_scores(2, 0.5).cpu().numpy()
+    assert np.max(np.abs(got - oc.relax_scores(2, 0.5))) <= RELAX_TOL
+    w = Workload("rxmax", 217, 1, 64, "bf16", 2, 2, 0, 70, (1,) * 70)
+    gc = new_cache(w)
+    for i in range(70):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), i)
+    with pytest.raises(KVCError) as e:
+        gc.relax_scores(7)                                          # 63 candidates + 7 = 70 frames
+    assert e.value.code == 5
+
+
+def test_relax_scores_errors():
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("rxe", 215, 2, 128, "bf16", 4, 8, 1, 5, (1,) * 6)
+    gc = new_cache(w, compact=True)
+    for i in range(6):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), i)
+    gc.relax_scores(2)
+    for tail, wt in ((0, 0.5), (5, 0.5), (6, 0.5), (2, 1.5), (2, -0.1), (2, float("nan"))):
+        with pytest.raises(KVCError) as e:
+            gc.relax_scores(tail, wt)
+        assert e.value.code == 1, (tail, wt)
+    gc.compact(list(range(32)) + list(range(40, 100)))                # leaves a partial frame
+    with pytest.raises(KVCError) as e:
+        gc.relax_scores(1)
+    assert e.value.code == 1
