@@ -45,7 +45,7 @@ class OracleError(ValueError):
 
 class OracleCache:
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
-                 dtype="bf16", bank_frames=0):
+                 dtype="bf16", bank_frames=0, raw_keys=False):
         self.S = frame_seqlen
         self.H = heads
         self.D = head_dim
@@ -55,6 +55,9 @@ class OracleCache:
         self.W_tok = window_frames * frame_seqlen
         self.C_tok = self.S_tok + self.W_tok
         self.bank_tok = bank_frames * frame_seqlen
+        # raw-key mode (MemRoPE, rCM article): keys are kept un-rotated in time and placed at their
+        # current time when attended; a retime then only changes t
+        self.raw_keys = raw_keys
         e = np.zeros((0, heads, head_dim), np.float32)
         self.K, self.V, self.Kraw = e.copy(), e.copy(), e.copy()
         self.t = np.zeros(0, np.int64)
@@ -78,6 +81,20 @@ class OracleCache:
         h = tok // self.grid_w
         w = tok % self.grid_w
         return self._store(rotate_f32(x, t, h, w, bands))
+
+    def _stored_key(self, k, t, tok):
+        """The key as the cache stores it: fully rotated, or (raw-key mode) with only the height and
+        width bands rotated -- those positions never change -- and the time band left raw."""
+        if self.raw_keys:
+            return self._rotate(k, t, tok, bands=(False, True, True))
+        return self._rotate(k, t, tok)
+
+    def attention_keys(self):
+        """Keys as attention sees them: the stored keys, or (raw-key mode) the raw keys freshly rotated at
+        every entry's current time (the plain definition, from Kraw)."""
+        if self.raw_keys:
+            return self._rotate(self.Kraw, self.t, self.tok)
+        return self.K
 
     def _take(self, idx):
         idx = np.asarray(idx, dtype=np.int64)
@@ -103,7 +120,7 @@ class OracleCache:
             raise OracleError("chunk larger than the rolling window")
         t, _, _ = token_positions(N, self.S, self.grid_w, t0)
         tok = np.arange(N, dtype=np.int64) % self.S
-        Kst = self._rotate(k, t, tok)
+        Kst = self._stored_key(k, t, tok)
         if replace_newest:
             if self.newest is None or self.newest[2] != frames:
                 raise OracleError("no newest chunk of that size to replace")
@@ -152,6 +169,9 @@ class OracleCache:
             return
         t_old = self.t[lo:hi]
         t_new = np.maximum(0, t_old + delta) if clamp0 else t_old + delta
+        if self.raw_keys:                       # index only: keys are placed at attention time
+            self.t[lo:hi] = t_new
+            return
         dlt = t_new - t_old
         blk = self.K[lo:hi]
         rot = rotate_f32(blk, dlt, np.zeros_like(dlt), np.zeros_like(dlt), bands=(True, False, False))
@@ -195,7 +215,7 @@ class OracleCache:
         raw = self.bank_K[b0:b0 + N]
         t, _, _ = token_positions(N, self.S, self.grid_w, t0)
         tok = (b0 + np.arange(N, dtype=np.int64)) % self.S
-        new = {"K": self._rotate(raw, t, tok), "V": self.bank_V[b0:b0 + N].copy(), "Kraw": raw.copy(),
+        new = {"K": self._stored_key(raw, t, tok), "V": self.bank_V[b0:b0 + N].copy(), "Kraw": raw.copy(),
                "t": t, "g": b0 + np.arange(N, dtype=np.int64), "tok": tok}
         self._cat([self._entries(N, self.S_tok), new, self._entries(self.S_tok, self.n)])
 
@@ -219,9 +239,10 @@ class OracleCache:
         qh = self.rotate_queries(q, frames, t0)
         if rows is not None:
             qh = qh[np.asarray(rows)]
+        K = self.attention_keys()
         if f64:
-            return attention_f64(qh, self.K, self.V)
-        return attention_f32(qh, self.K, self.V)
+            return attention_f64(qh, K, self.V)
+        return attention_f32(qh, K, self.V)
 
     def attend_block_causal(self, q, frames, t0, block_frames, rows=None, f64=False):
         """Block-causal attention of a whole clip, for a cache that holds the clip from its first frame.
@@ -238,11 +259,12 @@ class OracleCache:
         rows = np.arange(N) if rows is None else np.asarray(rows)
         blk = rows // (block_frames * self.S)
         fn = attention_f64 if f64 else attention_f32
+        K = self.attention_keys()
         out = np.empty((len(rows), self.H, self.D), np.float64 if f64 else np.float32)
         for b in np.unique(blk):
             sel = np.nonzero(blk == b)[0]
             n_vis = min(self.n, int(b + 1) * block_frames * self.S)
-            out[sel] = fn(qh[rows[sel]], self.K[:n_vis], self.V[:n_vis])
+            out[sel] = fn(qh[rows[sel]], K[:n_vis], self.V[:n_vis])
         return out
 
     def relax_scores(self, tail_frames, weight=0.5):
@@ -255,7 +277,7 @@ class OracleCache:
         n_cand = self.n // S - tail_frames - first
         if tail_frames < 1 or n_cand < 1:
             raise OracleError("relax scores need a tail and at least one candidate")
-        return relax_frame_scores(self.K, S, first, n_cand, tail_frames, weight)
+        return relax_frame_scores(self.attention_keys(), S, first, n_cand, tail_frames, weight)
 
     def score(self, q_win, frames, t_frames, f64=False):
         """Per-entry attention mass of the query window, summed over heads and query rows."""
@@ -263,7 +285,7 @@ class OracleCache:
         t = np.repeat(np.asarray(t_frames, np.int64), self.S)
         tok = np.arange(N, dtype=np.int64) % self.S
         qh = self._rotate(np.asarray(q_win, np.float32), t, tok)
-        return attention_mass_scores(qh, self.K, np.float64 if f64 else np.float32)
+        return attention_mass_scores(qh, self.attention_keys(), np.float64 if f64 else np.float32)
 
     def state(self):
         return {"K": self.K, "V": self.V, "t": self.t, "g": self.g, "n_sink": self.n_sink,
