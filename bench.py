@@ -151,6 +151,7 @@ def main():
     extras = sink_push_and_compact(dev, stream, flush, ev)
     extras.update(per_gpu_share(dev, stream, ev, w))
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
+    extras.update(raw_keys_ab(dev, stream, ev, flush, w))
     # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
     cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cy = torch.empty_like(cx)
@@ -365,6 +366,46 @@ def block_causal_clip(dev, stream, ev, w, block_frames=3):
     vis = sum(min(n, (r // cb + 1) * cb) * min(cb, F * S - r) for r in range(0, F * S, cb))
     flop = 4.0 * H * D * vis
     return {"block_causal_clip_ms": round(ms, 4), "block_causal_clip_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+
+def raw_keys_ab(dev, stream, ev, flush, w):
+    """The bench chunk on a raw-key cache (same 40-head, 28080-key shape): attention rotates every key's
+    time band while staging it, and a retime of the whole cache only rewrites 28080 time indices."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import chunk_inputs
+    S, H, D = w.frame_seqlen, w.heads, w.head_dim
+    c = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16, raw_keys=True)
+    q = None
+    for i in range(6):
+        q_, k, v = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, i % 4))
+        c.append(k, v, 3 * i)
+        q = q_
+    out = c.attend(q, 15)
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(10):
+        a, b = ev(), ev()
+        a.record(stream)
+        c.attend(q, 15, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    flop = 4.0 * H * q.shape[0] * c.info()["n_valid"] * D
+    rt = []
+    for i in range(10):
+        flush.sum()
+        a, b = ev(), ev()
+        a.record(stream)
+        c.retime(1 if i % 2 == 0 else -1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            rt.append(a.elapsed_time(b) * 1e3)
+    return {"raw_attend_ms": round(ms, 4), "raw_attend_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "raw_retime_us_cold": round(float(np.mean(rt)), 2)}
 
 
 def vendor_context(dev, stream, H, N, Lk, D):

@@ -69,6 +69,14 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
 #define KVC_APPEND_REPLACE_NEWEST 1u
 /* kvc_create: reserve the second window buffer that kvc_compact gathers into. */
 #define KVC_CREATE_COMPACT 1u
+/* kvc_create: raw-key cache (the MemRoPE variant of the rCM length-extrapolation
+ * article: keys kept un-rotated, placed at attention time).  Keys are stored
+ * with their height and width bands rotated (those positions never change)
+ * and the time band raw; kvc_attend rotates each key's time band at its slot's
+ * current time while staging it, so every attended key equals a fresh
+ * rotation of the raw key and kvc_retime only rewrites time indices.
+ * kvc_score and kvc_relax_scores return KVC_EUNSUPPORTED on such a cache. */
+#define KVC_CREATE_RAW_KEYS 2u
 /* Largest |time index| and |retime delta| (the RoPE time table covers
  * positions -KVC_MAX_POS .. KVC_MAX_POS). */
 #define KVC_MAX_POS 16383

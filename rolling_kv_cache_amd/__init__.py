@@ -21,6 +21,7 @@ KVC_BF16, KVC_F32 = 0, 1
 KVC_T_NEWEST = -(2 ** 31)
 KVC_APPEND_REPLACE_NEWEST = 1
 KVC_CREATE_COMPACT = 1
+KVC_CREATE_RAW_KEYS = 2
 KVC_MAX_POS = 16383
 KVC_MAX_Q_FRAMES = 32
 
@@ -97,22 +98,26 @@ def _dt(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported cache dtype {dtype}")
 
 
+def _create_flags(compact=False, raw_keys=False) -> int:
+    return (KVC_CREATE_COMPACT if compact else 0) | (KVC_CREATE_RAW_KEYS if raw_keys else 0)
+
+
 def workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype=torch.bfloat16,
-                    bank_frames=0, compact=False) -> int:
+                    bank_frames=0, compact=False, raw_keys=False) -> int:
     return int(lib.kvc_workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, _dt(dtype),
-                                       bank_frames, KVC_CREATE_COMPACT if compact else 0))
+                                       bank_frames, _create_flags(compact, raw_keys)))
 
 
 class KVCache:
     """One layer's cache.  Methods mirror the C calls: append, attend, retime, score, compact, sink_push."""
 
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
-                 dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None):
+                 dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False):
         self.S, self.H, self.D = frame_seqlen, heads, head_dim
         self.dtype = dtype
         self.device = torch.device(device)
         nbytes = workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype, bank_frames,
-                                 compact)
+                                 compact, raw_keys)
         if nbytes == 0:
             raise KVCError(KVC_EINVAL, "unsupported geometry")
         self._ws_raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -121,7 +126,7 @@ class KVCache:
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
         _check(lib.kvc_create(sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w, _dt(dtype),
-                              bank_frames, KVC_CREATE_COMPACT if compact else 0,
+                              bank_frames, _create_flags(compact, raw_keys),
                               ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
                               ctypes.c_void_p(self._stream.cuda_stream), ctypes.byref(h)))
         self._h = h

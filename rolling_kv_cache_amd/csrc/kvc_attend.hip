@@ -398,13 +398,123 @@ __device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* l
   }
 }
 
+// Raw-key caches store the key's time band un-rotated (the height and width
+// bands, whose positions never change, are stored rotated), and attention
+// places every key at its slot's current time while staging the tile.  Each
+// pair is rotated by one band only, so rotating the stored time band now gives
+// exactly the key a full rotation of the raw key at that time would give (fp32,
+// no FMA, rounded to nearest even).  The 22 time pairs sit in the first six
+// 16-byte chunks of a key row (the KA plane), so the staging map changes for
+// raw tiles: threads 0..383 (waves 0-5) move KA chunk tid (row tid / 6) and
+// rotate it, plus KB chunk tid; threads 384..511 move KB chunks tid and
+// tid + 128 (KB chunk i: row i / 10, column 6 + i % 10).
+struct RawPtrs {
+  const uint16_t* ka[2];   // region r, head h: key planes, V^T tiles and times (wave-uniform)
+  const uint16_t* kb[2];
+  const uint16_t* v[2];
+  const int32_t* t[2];
+  int o0, o1;              // element offsets of the two chunks in their planes at slot base 0
+  int l0, l1;              // LDS chunk index (row * kKSt + column) of the two chunks
+  int lrow;                // the KA chunk's row in the tile
+  int cpair;               // first pair of the KA chunk (4 * column)
+};
+
+__device__ __forceinline__ RawPtrs raw_ptrs(const KeyRegions& kr, int h, int tid) {
+  RawPtrs p;
+  const bool ka = tid < 384;
+  const int i1 = ka ? tid : tid + 128;
+  p.lrow = tid / 6;
+  p.cpair = 4 * (tid % 6);
+  p.l0 = ka ? p.lrow * kKSt + tid % 6 : (tid / 10) * kKSt + 6 + tid % 10;
+  p.l1 = (i1 / 10) * kKSt + 6 + i1 % 10;
+  p.o0 = tid * 8;
+  p.o1 = i1 * 8;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    p.ka[r] = (const uint16_t*)kr.ka[r] + (int64_t)h * kr.cap[r] * kDA;
+    p.kb[r] = (const uint16_t*)kr.kb[r] + (int64_t)h * kr.cap[r] * kDB;
+    p.v[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile;
+    p.t[r] = kr.t[r];
+  }
+  return p;
+}
+
+struct StageR {
+  u32x4_t k[2];
+  u32x4_t v[2];
+  int t;                   // time of the KA chunk's row
+  float cs[8];             // (cos, sin) of its four pairs at that time
+};
+
+// issue the loads of K tile (rk, bk) and V tile (rv, bv), and the KA row's time
+__device__ __forceinline__ void loadR(StageR& st, const RawPtrs& p, const AttendArgs& a, int tid, int rk, int bk,
+                                      int rv, int bv) {
+  const bool ka = tid < 384;
+  const uint16_t* pa = rk == 0 ? p.ka[0] : p.ka[1];
+  const uint16_t* pb = rk == 0 ? p.kb[0] : p.kb[1];
+  if (ka) {
+    const int slot = bk + p.lrow;
+    st.t = (rk == 0 ? p.t[0] : p.t[1])[slot];
+    if (rk == 0 && slot >= a.mem_lo) st.t = a.mem_t[slot - a.mem_lo >= a.geo.S ? 1 : 0];
+    st.k[0] = *reinterpret_cast<const u32x4_t*>(pa + (bk * kDA + p.o0));
+  } else {
+    st.k[0] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o0));
+  }
+  st.k[1] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o1));
+  const uint16_t* vp = (rv == 0 ? p.v[0] : p.v[1]) + (bv / kTile) * kVTile + tid * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) st.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 4096 * i);
+}
+
+// the (cos, sin) table entries of the KA chunk's time pairs (issued once its t has arrived)
+__device__ __forceinline__ void loadR_table(StageR& st, const RawPtrs& p, const AttendArgs& a, int tid) {
+  if (tid >= 384) return;
+  const float* tp = a.tab.tcs + ((st.t + a.tab.maxpos) * 22 + p.cpair) * 2;
+  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(tp);
+  u32x4_t hi = {__float_as_uint(1.f), 0u, __float_as_uint(1.f), 0u};
+  if (p.cpair < 20) hi = *reinterpret_cast<const u32x4_t*>(tp + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.cs[i] = __uint_as_float(lo[i]);
+    st.cs[4 + i] = __uint_as_float(hi[i]);
+  }
+}
+
+// rotate the KA chunk's time pairs and write the tile into LDS
+__device__ __forceinline__ void storeR(StageR& st, const RawPtrs& p, u32x4_t* lk, u32x4_t* lv, int tid, bool k,
+                                       bool v) {
+  if (k) {
+    if (tid < 384) {
+      u32x4_t x = st.k[0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q >= 2 && p.cpair >= 20) break;            // pairs 22, 23 belong to the height band
+        float x0 = __uint_as_float(x[q] << 16), x1 = __uint_as_float(x[q] & 0xFFFF0000u);
+        rot_pair(x0, x1, st.cs[2 * q], st.cs[2 * q + 1]);
+        const bf16x2_t r = {(__bf16)x0, (__bf16)x1};   // round to nearest even, as the cache rounds
+        x[q] = __builtin_bit_cast(uint32_t, r);
+      }
+      st.k[0] = x;
+    }
+    lk[p.l0] = st.k[0];
+    lk[p.l1] = st.k[1];
+  }
+  if (v) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 512 * i;
+      lv[(ci >> 3) * kVSt + (ci & 7)] = st.v[i];
+    }
+  }
+}
+
 // With only_flagged set, blocks whose flag is 0 exit at once (the recompute
 // pass behind the fixed-reference kernel).  CAUSAL: block-causal attention of
 // a clip -- query row r sees the logical key prefix of length
 // min(n, (r / causal_block + 1) * causal_block); a workgroup loops only over
 // the tiles its longest prefix needs, rows whose prefix ends inside a tile mask
 // the rest per lane, and workgroups with the longest prefixes start first.
-template <bool CAUSAL>
+template <bool CAUSAL, bool RAW>
 __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles, const int32_t* only_flagged) {
   __shared__ u32x4_t lks[2][kKTileP];
@@ -445,16 +555,32 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     mask_tile(s, nv, hl);
   };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+  const RawPtrs rp = raw_ptrs(a.keys, h, tid);
 
   Stage5 st;
-  load5(st, tp, 0, 0, 0, 0);
+  StageR sr;
+  if constexpr (RAW) {
+    loadR(sr, rp, a, tid, 0, 0, 0, 0);
+    loadR_table(sr, rp, a, tid);
+  } else {
+    load5(st, tp, 0, 0, 0, 0);
+  }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-  store5(st, lks[0], lvs[0], tid, true, true);
+  if constexpr (RAW)
+    storeR(sr, rp, lks[0], lvs[0], tid, true, true);
+  else
+    store5(st, lks[0], lvs[0], tid, true, true);
   {
     const int t1 = min(1, last);
-    load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
-    store5(st, lks[1], lvs[1], tid, true, false);
+    if constexpr (RAW) {
+      loadR(sr, rp, a, tid, ts.region(t1), ts.base(t1), 0, 0);
+      loadR_table(sr, rp, a, tid);
+      storeR(sr, rp, lks[1], lvs[1], tid, true, false);
+    } else {
+      load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+      store5(st, lks[1], lvs[1], tid, true, false);
+    }
   }
   f32x16_t o[4];
 #pragma unroll
@@ -479,11 +605,15 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
-    load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    if constexpr (RAW)
+      loadR(sr, rp, a, tid, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    else
+      load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
     bf16x8_t pb[2][2];
     float psum, alpha;
     bool upd;
     qk_and_softmax(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
+    if constexpr (RAW) loadR_table(sr, rp, a, tid);
     if (__ballot(upd) != 0) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -493,7 +623,10 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     lsum = lsum * alpha + psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
     mask(snext, min(t + 1, last));
-    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    if constexpr (RAW)
+      storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    else
+      store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
 
@@ -695,6 +828,7 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
     b.keys.ka[0] = a.keys.ka[1];
     b.keys.kb[0] = a.keys.kb[1];
     b.keys.v[0] = a.keys.v[1];
+    b.keys.t[0] = a.keys.t[1];
     b.keys.cap[0] = a.keys.cap[1];
     b.keys.n[0] = a.keys.n[1];
     b.keys.n[1] = 0;
@@ -774,6 +908,7 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
   }
 }
 
+template <bool RAW>
 __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles) {
   __shared__ u32x4_t lks[2][kKTileP];
@@ -792,17 +927,33 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   const int vbase = l32 * kVSt + hl;
   const int last = ntiles - 1;
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+  const RawPtrs rp = raw_ptrs(a.keys, h, tid);
   if (tid == 0) s_flag = 0;
 
   Stage5 st;
-  load5(st, tp, 0, 0, 0, 0);
+  StageR sr;
+  if constexpr (RAW) {
+    loadR(sr, rp, a, tid, 0, 0, 0, 0);
+    loadR_table(sr, rp, a, tid);
+  } else {
+    load5(st, tp, 0, 0, 0, 0);
+  }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-  store5(st, lks[0], lvs[0], tid, true, true);
+  if constexpr (RAW)
+    storeR(sr, rp, lks[0], lvs[0], tid, true, true);
+  else
+    store5(st, lks[0], lvs[0], tid, true, true);
   {
     const int t1 = min(1, last);
-    load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
-    store5(st, lks[1], lvs[1], tid, true, false);
+    if constexpr (RAW) {
+      loadR(sr, rp, a, tid, ts.region(t1), ts.base(t1), 0, 0);
+      loadR_table(sr, rp, a, tid);
+      storeR(sr, rp, lks[1], lvs[1], tid, true, false);
+    } else {
+      load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+      store5(st, lks[1], lvs[1], tid, true, false);
+    }
   }
   f32x16_t o[4];
 #pragma unroll
@@ -829,15 +980,22 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
-    load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    if constexpr (RAW)
+      loadR(sr, rp, a, tid, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+    else
+      load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
     bf16x8_t pb[2][2];
     float psum;
     qk_and_exp(snext, lks[(t + 1) & 1], qf, kbase, scur, negm, c2, pb, psum);
+    if constexpr (RAW) loadR_table(sr, rp, a, tid);
     pmax = fmaxf(pmax, psum);
     lsum += psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
     mask_tile(snext, ts.valid(min(t + 1, last)), hl);
-    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    if constexpr (RAW)
+      storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    else
+      store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
 
@@ -853,7 +1011,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   store_out(a, o, lsum, qrow, h, hl);
 }
 
-template <int VAR>
+template <int VAR, bool RAW>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int bm = (VAR == 2 || VAR == 4 || VAR == 5) ? 256 : kBM;
   const int mblocks = (a.Lq + bm - 1) / bm;
@@ -865,10 +1023,13 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   AttendArgs b = a;
   int n0 = ntile0, nt = ntile0 + ntile1;
   // a region with no valid keys contributes no tiles; keep region 0 non-empty
+  // (memory tokens live in region 0, so there are none when it is empty)
   if (ntile0 == 0) {
+    b.mem_lo = INT32_MAX;
     b.keys.ka[0] = a.keys.ka[1];
     b.keys.kb[0] = a.keys.kb[1];
     b.keys.v[0] = a.keys.v[1];
+    b.keys.t[0] = a.keys.t[1];
     b.keys.cap[0] = a.keys.cap[1];
     b.keys.n[0] = a.keys.n[1];
     b.keys.n[1] = 0;
@@ -876,16 +1037,17 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     nt = ntile1;
   }
   if (VAR == 2)
-    hipLaunchKernelGGL(attend_v5_kernel<false>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
-                       nt, (const int32_t*)nullptr);
+    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
+                       n0, nt, (const int32_t*)nullptr);
   else if (VAR == 5)
-    hipLaunchKernelGGL(attend_v5_kernel<true>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
-                       nt, (const int32_t*)nullptr);
+    hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
+                       n0, nt, (const int32_t*)nullptr);
   else if (VAR == 4) {
-    hipLaunchKernelGGL(attend_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0, nt);
+    hipLaunchKernelGGL((attend_v5f_kernel<RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
+                       nt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_v5_kernel<false>, dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
-                       nt, (const int32_t*)b.flags);
+    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
+                       n0, nt, (const int32_t*)b.flags);
   }
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
@@ -897,11 +1059,17 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
 // KVC_ATTEND_VARIANT=v5 (running maximum, 8 waves) or v3 (4 waves, two
 // workgroups per CU) selects another kernel for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
-  if (a.causal_block > 0) return attend_launch<5>(a, s);
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
-  if (v && std::string(v) == "v3") return attend_launch<0>(a, s);
-  if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2>(a, s);
-  return attend_launch<4>(a, s);
+  if (a.raw) {
+    // raw-key caches: the 8-wave kernels only (the 4-wave variant has no time-band staging)
+    if (a.causal_block > 0) return attend_launch<5, true>(a, s);
+    if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, true>(a, s);
+    return attend_launch<4, true>(a, s);
+  }
+  if (a.causal_block > 0) return attend_launch<5, false>(a, s);
+  if (v && std::string(v) == "v3") return attend_launch<0, false>(a, s);
+  if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, false>(a, s);
+  return attend_launch<4, false>(a, s);
 }
 
 }  // namespace kvc

@@ -53,6 +53,7 @@ struct SegW {
 };
 
 struct AppendArgs {
+  int32_t time_raw;                       // raw-key cache: the time band is stored un-rotated
   const void* k;
   const void* v;
   int64_t k_tok, k_head, v_tok, v_head;   // element strides of the sources
@@ -80,6 +81,7 @@ struct RetimeArgs {
   RangeW rng[4];
   int32_t nrng;
   int32_t delta, clamp0;
+  int32_t keys;                           // 0: raw-key cache, only t changes
   Geo geo;
   Tables tab;
 };
@@ -106,6 +108,7 @@ struct KeyRegions {
   const void* ka[2];
   const void* kb[2];
   const void* v[2];
+  const int32_t* t[2];                    // time index of every slot
   int32_t cap[2];
   int32_t n[2];                           // valid slots (a prefix of each region)
 };
@@ -121,6 +124,9 @@ struct AttendArgs {
   float scale;                            // 1/sqrt(D)
   int32_t* flags;                         // workspace: one recompute flag per 256-query attention block
   int32_t causal_block;                   // > 0: query row r sees the logical key prefix min(n, (r/cb+1)*cb)
+  int32_t raw;                            // raw-key cache: rotate each key's time band at its slot's t
+  int32_t mem_lo;                         // region-0 slots [mem_lo, mem_lo + 2S): memory tokens ...
+  int32_t mem_t[2];                       // ... placed at times mem_t[0] (first S) and mem_t[1] (next S)
 };
 
 struct ScoreArgs {

@@ -151,11 +151,13 @@ kvc::KeyRegions key_regions(kvc_handle h) {
   k.ka[0] = h->sink.ka;
   k.kb[0] = h->sink.kb;
   k.v[0] = h->sink.v;
+  k.t[0] = h->sink.t;
   k.cap[0] = h->sink.cap;
   k.n[0] = h->st.ns;
   k.ka[1] = w.ka;
   k.kb[1] = w.kb;
   k.v[1] = w.v;
+  k.t[1] = w.t;
   k.cap[1] = w.cap;
   k.n[1] = h->st.nw;
   return k;
@@ -167,6 +169,7 @@ hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, cons
                            int32_t bank_lo, int32_t bank_hi) {
   for (size_t b = 0; b < segs.size(); b += kvc::kMaxSegs) {
     kvc::AppendArgs a{};
+    a.time_raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
     a.k = k;
     a.v = v;
     a.k_tok = k_tok;
@@ -248,7 +251,9 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   Layout L = make_layout(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames, create_flags);
   if (!L.ok) return fail(KVC_EINVAL, "unsupported geometry (head_dim must be 64 or 128; sizes positive)");
   if (grid_w < 1 || frame_seqlen % grid_w != 0) return fail(KVC_EINVAL, "frame_seqlen must be a multiple of grid_w");
-  if (create_flags & ~KVC_CREATE_COMPACT) return fail(KVC_EINVAL, "unknown create flag");
+  if (create_flags & ~(KVC_CREATE_COMPACT | KVC_CREATE_RAW_KEYS)) return fail(KVC_EINVAL, "unknown create flag");
+  if ((create_flags & KVC_CREATE_RAW_KEYS) && !(dt == KVC_BF16 || dt == KVC_F32))
+    return fail(KVC_EINVAL, "raw keys need a bf16 or fp32 cache");
   if (!workspace) return fail(KVC_EINVAL, "workspace is null");
   if ((uintptr_t)workspace % kAlign != 0) return fail(KVC_EINVAL, "workspace must be 256-byte aligned");
   if (ws_bytes < L.total) return fail(KVC_ENOMEM, "workspace smaller than kvc_workspace_bytes()");
@@ -375,6 +380,8 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
   a.flags = h->att_flags;
   a.causal_block = causal_block;
+  a.raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
+  a.mem_lo = INT32_MAX;
   const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
   hipError_t e = kvc::launch_attend(a, h->stream, force_general);
   return device_result(h, e, "attend");
@@ -415,6 +422,7 @@ kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_
   }
   a.delta = delta;
   a.clamp0 = clamp0 != 0;
+  a.keys = (h->cflags & KVC_CREATE_RAW_KEYS) ? 0 : 1;     // raw keys: only the time indices move
   a.geo = h->geo;
   a.tab = h->tab;
   hipError_t e = kvc::launch_retime(a, blocks, h->stream);
@@ -435,6 +443,7 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   if (kvc_status s = check(h)) return s;
   if (!q_win || !q_t || !scores || !scratch) return fail(KVC_EINVAL, "null argument");
   if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
+  if (h->cflags & KVC_CREATE_RAW_KEYS) return fail(KVC_EUNSUPPORTED, "score is not available on a raw-key cache");
   if (scratch_bytes < kvc_score_scratch_bytes(h, q_frames)) return fail(KVC_ENOMEM, "score scratch too small");
   if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
   if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "score on an empty cache");
@@ -482,6 +491,7 @@ kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, flo
                             size_t scratch_bytes) {
   if (kvc_status s = check(h)) return s;
   if (!scores || !scratch) return fail(KVC_EINVAL, "null argument");
+  if (h->cflags & KVC_CREATE_RAW_KEYS) return fail(KVC_EUNSUPPORTED, "relax scores are not available on a raw-key cache");
   if (!(weight >= 0.f && weight <= 1.f)) return fail(KVC_EINVAL, "weight outside [0, 1]");
   if (scratch_bytes < kvc_relax_scratch_bytes(h)) return fail(KVC_ENOMEM, "relax scratch too small");
   if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");

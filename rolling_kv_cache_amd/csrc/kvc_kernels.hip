@@ -38,10 +38,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 // ----------------------------------------------------------------------------
 // append.  One grid, two kinds of 256-thread blocks:
-//   K blocks: one head x (256/CH)*4 consecutive tokens of a segment; lanes run
-//     over the row's 16-byte chunks first, so a wave reads whole 256-byte
-//     source rows and writes consecutive destination rows of that head's key
-//     planes; each thread keeps four chunks in flight.
+//   K blocks: 256/CH consecutive tokens of a segment x up to 20 heads; lanes
+//     run over the row's 16-byte chunks first, so a wave reads whole 256-byte
+//     source rows and writes consecutive destination rows of each head's key
+//     planes; each thread keeps eight chunks (heads) in flight.
 //   V blocks: one 64-slot tile x (256/(8*CH)) heads; thread (group of 8 slots,
 //     chunk) loads eight tokens' chunk, transposes it in registers and writes
 //     eight d-rows of the tile, so eight lanes fill one 128-byte tile row.
@@ -99,8 +99,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int t = a.t0 + f, hp = tok / g.grid_w, wp = tok - hp * g.grid_w;
     const int d0 = c * E;
     float cs[E / 2][2];
+    bool rot[E / 2];
 #pragma unroll
-    for (int q = 0; q < E / 2; ++q) pair_cs(g, a.tab, d0 + 2 * q, t, hp, wp, cs[q][0], cs[q][1]);
+    for (int q = 0; q < E / 2; ++q) {
+      pair_cs(g, a.tab, d0 + 2 * q, t, hp, wp, cs[q][0], cs[q][1]);
+      rot[q] = !(a.time_raw && d0 + 2 * q < g.dt);     // raw-key cache: the time band stays raw
+    }
     const bool bank = src >= a.bank_lo && src < a.bank_hi;
     const T* sp = (const T*)a.k + (int64_t)src * a.k_tok + d0;
     T* dp;
@@ -129,7 +133,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
 #pragma unroll
-        for (int q = 0; q < E / 2; ++q) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
+        for (int q = 0; q < E / 2; ++q)
+          if (rot[q]) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
 #pragma unroll
         for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
         *reinterpret_cast<uint4*>(dp + h * dstride) = x[u].u;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
   }
   __syncthreads();
   const int j = tid / CA, c = tid - (tid / CA) * CA;
-  if (j < ns) {
+  if (j < ns && a.keys) {
     // this chunk's rotation, shared by every head
     float cs[E / 2][2];
     const float* tp = a.tab.tcs + ((size_t)(s_dl[j] + a.tab.maxpos) * (DT / 2)) * 2;
@@ -536,8 +541,11 @@ __device__ __forceinline__ void load_rotated_query(const T* q, int i, int h, int
   }
 }
 
+// q . k_j for slot j of region r.  tr >= -maxpos: a raw-key cache, whose stored
+// time band is first rotated to time tr and rounded, as the cache would store it.
 template <typename T, int D>
-__device__ __forceinline__ float key_dot(const float* qv, const KeyRegions& kr, int r, int h, int j, const Geo& g) {
+__device__ __forceinline__ float key_dot(const float* qv, const KeyRegions& kr, int r, int h, int j, const Geo& g,
+                                         const Tables& tb, int tr) {
   constexpr int E = Elem<T>::E;
   const T* ka = (const T*)kr.ka[r] + ((int64_t)h * kr.cap[r] + j) * g.DA;
   const T* kb = (const T*)kr.kb[r] + ((int64_t)h * kr.cap[r] + j) * g.DB;
@@ -547,8 +555,22 @@ __device__ __forceinline__ float key_dot(const float* qv, const KeyRegions& kr, 
     Vec16<T> x;
     const int d0 = c * E;
     x.u = d0 < g.DA ? *reinterpret_cast<const uint4*>(ka + d0) : *reinterpret_cast<const uint4*>(kb + (d0 - g.DA));
+    float xf[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc = fmaf(qv[d0 + e], Elem<T>::ld(x.e[e]), acc);
+    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x.e[e]);
+    if (tr >= -tb.maxpos && d0 < g.dt) {
+#pragma unroll
+      for (int q = 0; q < E / 2; ++q) {
+        const int d = d0 + 2 * q;
+        if (d >= g.dt) break;
+        const float* cs = tb.tcs + ((size_t)(tr + tb.maxpos) * (g.dt >> 1) + (d >> 1)) * 2;
+        rot_pair(xf[2 * q], xf[2 * q + 1], cs[0], cs[1]);
+        xf[2 * q] = Elem<T>::ld(Elem<T>::st(xf[2 * q]));
+        xf[2 * q + 1] = Elem<T>::ld(Elem<T>::st(xf[2 * q + 1]));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(qv[d0 + e], xf[e], acc);
   }
   return acc;
 }
@@ -574,7 +596,9 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
     const T* vbase = (const T*)a.keys.v[r];
     const int nr = min(a.keys.n[r], lim - (r == 0 ? 0 : a.keys.n[0]));
     for (int j = 0; j < nr; ++j) {
-      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g) * a.scale;
+      int tr = INT32_MIN;
+      if (a.raw) tr = (r == 0 && j >= a.mem_lo) ? a.mem_t[j - a.mem_lo >= g.S ? 1 : 0] : a.keys.t[r][j];
+      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g, a.tab, tr) * a.scale;
       const float mn = fmaxf(m, s);
       const float alpha = expf(m - mn);
       const float p = expf(s - mn);
@@ -649,7 +673,7 @@ __global__ __launch_bounds__(64) void score_rows_kernel(ScoreArgs a) {
   float m = -INFINITY, l = 0.f;
   for (int r = 0; r < 2; ++r)
     for (int j = 0; j < a.keys.n[r]; ++j) {
-      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g) * a.scale;
+      const float s = key_dot<T, D>(qv, a.keys, r, h, j, g, a.tab, INT32_MIN) * a.scale;
       const float mn = fmaxf(m, s);
       l = l * expf(m - mn) + expf(s - mn);
       m = mn;

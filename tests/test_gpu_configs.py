@@ -114,6 +114,13 @@ def test_c5b_deep_forcing():
 
 
 @pytest.mark.timeout(900)
+def test_c5a_raw_keys_infinity_rope():
+    """Infinity-RoPE on a raw-key cache: the per-chunk shifts only move time indices and every attended key is
+    the raw key rotated once at its current time."""
+    _run_config("c5a_raw", full_rows_at=(7,), compact=True, sample_rows=256)
+
+
+@pytest.mark.timeout(900)
 def test_c5c_relax_forcing():
     _run_config("c5c", full_rows_at=(7,), compact=True, sample_rows=256)
 

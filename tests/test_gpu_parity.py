@@ -351,3 +351,60 @@ def test_relax_scores_errors():
     with pytest.raises(KVCError) as e:
         gc.relax_scores(1)
     assert e.value.code == 1
+
+
+# ---------------------------------------------------------------- raw-key caches (time band placed at attention)
+from dataclasses import replace as _replace
+
+
+@pytest.mark.parametrize("general", [False, True])
+def test_raw_keys_sliding_window(general):
+    """Stored keys (time band raw, height/width rotated) bit-exact, attention against the oracle's fresh
+    rotation, on the ragged sink/window workload."""
+    _drive(_replace(SMALL_SW, name="sw_raw", raw_keys=True), general=general)
+
+
+def test_raw_keys_tiny_fp32():
+    _drive(_replace(WORKLOADS["tiny"], name="tiny_raw", raw_keys=True))
+
+
+@pytest.mark.parametrize("variant", ["", "v5"])
+def test_raw_keys_infinity_rope(variant):
+    """Shift with clamp every chunk, flush and cut: index-only retimes, keys rotated at attention."""
+    base = WORKLOADS["c5a"]
+    w = Workload("c5a_small", 206, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
+                 (3,) * 14 + (2,), cut_chunks=(7, 11), raw_keys=True)
+    if variant:
+        os.environ["KVC_ATTEND_VARIANT"] = variant
+    try:
+        _drive(w, compact=True)
+    finally:
+        os.environ.pop("KVC_ATTEND_VARIANT", None)
+
+
+def test_raw_keys_negative_times_and_block_causal():
+    """A shift below time 0 without clamp, then a whole-clip block-causal attend on a raw cache; score and
+    relax scores are refused on such a cache."""
+    from rolling_kv_cache_amd import KVCError
+    w = Workload("rawneg", 218, 2, 128, "bf16", 9, 23, 1, 7, (2,) * 4, raw_keys=True)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                     raw_keys=True)
+    for i in range(4):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    (q,) = chunk_inputs(w, 97, tensors=(0,), frames=8)
+    check_attention(gc.attend_block_causal(dev(q, w), 0, 2).float().cpu().numpy(),
+                    oc.attend_block_causal(q, 8, 0, 2), "raw block-causal")
+    gc.retime(-30)
+    oc.retime(-30, False)
+    assert_state_equal(gc, oc, w, "raw after negative shift")
+    (q2,) = chunk_inputs(w, 96, tensors=(0,), frames=2)
+    check_attention(gc.attend(dev(q2, w), -24).float().cpu().numpy(), oc.attend(q2, 2, -24), "raw negative t")
+    with pytest.raises(KVCError) as e:
+        gc.score(dev(q2, w), [-24, -23])
+    assert e.value.code == 5
+    with pytest.raises(KVCError) as e:
+        gc.relax_scores(2)
+    assert e.value.code == 5
