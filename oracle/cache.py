@@ -45,7 +45,7 @@ class OracleError(ValueError):
 
 class OracleCache:
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
-                 dtype="bf16", bank_frames=0, raw_keys=False):
+                 dtype="bf16", bank_frames=0, raw_keys=False, memory=None):
         self.S = frame_seqlen
         self.H = heads
         self.D = head_dim
@@ -58,6 +58,13 @@ class OracleCache:
         # raw-key mode (MemRoPE, rCM article): keys are kept un-rotated in time and placed at their
         # current time when attended; a retime then only changes t
         self.raw_keys = raw_keys
+        # MemRoPE memory tokens (rCM article): (alpha_long, alpha_short) or None
+        if memory is not None and not raw_keys:
+            raise OracleError("memory tokens need a raw-key cache")
+        self.memory = memory
+        self.mem_k = np.zeros((2, frame_seqlen, heads, head_dim), np.float32)   # EMA state, fp32
+        self.mem_v = np.zeros((2, frame_seqlen, heads, head_dim), np.float32)
+        self.mem_frames = 0                                                     # frames folded so far
         e = np.zeros((0, heads, head_dim), np.float32)
         self.K, self.V, self.Kraw = e.copy(), e.copy(), e.copy()
         self.t = np.zeros(0, np.int64)
@@ -140,6 +147,8 @@ class OracleCache:
         self.n_sink = min(self.S_tok, self.n_sink + N)
         if self.n > self.C_tok:
             n_evict = self.n - self.C_tok
+            if self.memory is not None:
+                self._fold(self.S_tok, n_evict)
             # physical left shift of everything after the sink: window = window[n_evict:]
             sink = self._entries(0, self.S_tok)
             window = self._entries(self.S_tok + n_evict, self.n)
@@ -147,6 +156,43 @@ class OracleCache:
         self.newest = (g0, N, frames)
         self.global_end += N
         self._capture_bank(g0, k, v)
+
+    def _fold(self, lo, n):
+        """MemRoPE: fold the evicted entries [lo, lo + n) -- whole frames, oldest first -- into the long and
+        short memories, M = alpha * M + (1 - alpha) * E per grid position, in fp32 with every product and the
+        sum rounded separately; the first evicted frame initialises both."""
+        if n % self.S or np.any(self.tok[lo:lo + n] != np.arange(n) % self.S):
+            raise OracleError("memory folds whole frames")
+        for f in range(n // self.S):
+            ek = self.K[lo + f * self.S: lo + (f + 1) * self.S]
+            ev = self.V[lo + f * self.S: lo + (f + 1) * self.S]
+            for m, alpha in enumerate(self.memory):
+                if self.mem_frames == 0:
+                    self.mem_k[m] = ek
+                    self.mem_v[m] = ev
+                else:
+                    a = np.float32(alpha)
+                    b = np.float32(1.0) - a
+                    self.mem_k[m] = (a * self.mem_k[m]) + (b * ek)
+                    self.mem_v[m] = (a * self.mem_v[m]) + (b * ev)
+            self.mem_frames += 1
+
+    def memory_entries(self):
+        """The memory tokens as attention sees them (none before the first fold): keys = the state rounded to
+        the cache dtype, i.e. a stored key with its time band raw, placed (time band rotated) just before the
+        oldest window entry -- the long memory at t_w - 2, the short at t_w - 1; values = the state rounded."""
+        if self.memory is None or self.mem_frames == 0:
+            return None
+        t_w = int(self.t[self.n_sink])
+        keys, vals, times = [], [], []
+        zero = np.zeros(self.S, np.int64)
+        for m, dt in ((0, 2), (1, 1)):
+            stored = self._store(self.mem_k[m])
+            tm = np.full(self.S, t_w - dt, np.int64)
+            keys.append(self._store(rotate_f32(stored, tm, zero, zero, bands=(True, False, False))))
+            vals.append(self._store(self.mem_v[m]))
+            times.append(tm)
+        return np.concatenate(keys), np.concatenate(vals), np.concatenate(times)
 
     def _capture_bank(self, g0, k, v):
         if self.bank_tok == 0 or g0 >= self.bank_tok:
@@ -184,6 +230,8 @@ class OracleCache:
     # ------------------------------------------------------------------ compact
     def compact(self, keep_idx):
         """Keep exactly the logical entries keep_idx (sorted, unique, containing the whole sink)."""
+        if self.memory is not None:
+            raise OracleError("compaction is not defined with memory tokens")
         keep = np.asarray(keep_idx, dtype=np.int64)
         if keep.ndim != 1 or keep.shape[0] == 0:
             raise OracleError("keep_idx empty")
@@ -239,10 +287,14 @@ class OracleCache:
         qh = self.rotate_queries(q, frames, t0)
         if rows is not None:
             qh = qh[np.asarray(rows)]
-        K = self.attention_keys()
+        K, V = self.attention_keys(), self.V
+        mem = self.memory_entries()
+        if mem is not None:
+            K = np.concatenate([K, mem[0]])
+            V = np.concatenate([V, mem[1]])
         if f64:
-            return attention_f64(qh, K, self.V)
-        return attention_f32(qh, K, self.V)
+            return attention_f64(qh, K, V)
+        return attention_f32(qh, K, V)
 
     def attend_block_causal(self, q, frames, t0, block_frames, rows=None, f64=False):
         """Block-causal attention of a whole clip, for a cache that holds the clip from its first frame.

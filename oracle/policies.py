@@ -46,7 +46,8 @@ def roll_index(n: int, K: int) -> int:
 
 def _cache_for(w):
     return OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w,
-                       w.dtype, w.bank_frames, raw_keys=getattr(w, "raw_keys", False))
+                       w.dtype, w.bank_frames, raw_keys=getattr(w, "raw_keys", False),
+                       memory=getattr(w, "memory", None))
 
 
 class SlidingWindowRun:

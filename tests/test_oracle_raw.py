@@ -86,3 +86,96 @@ def test_time_band_rotation_of_stored_keys_is_the_full_rotation():
         staged = raw._store(rotate_f32(raw.K, raw.t, zero, zero, bands=(True, False, False)))
         assert np.array_equal(staged, raw.attention_keys())
         assert np.min(raw.t) < 0                     # some entries sit before time 0
+
+
+# ---------------------------------------------------------------- MemRoPE memory tokens
+def _mem_cache(alphas, n_chunks, F=1, S=6, H=2, D=64, sink=1, window=3, seed=5, raw_keys=True):
+    c = OracleCache(sink, window, S, H, D, 3, "bf16", raw_keys=raw_keys, memory=alphas)
+    rng = np.random.default_rng(seed)
+    ks, vs = [], []
+    for j in range(n_chunks):
+        k = round_to_bf16(rng.standard_normal((F * S, H, D)).astype(np.float32))
+        v = round_to_bf16(rng.standard_normal((F * S, H, D)).astype(np.float32))
+        c.append(k, v, F, j * F)
+        ks.append(k)
+        vs.append(v)
+    return c, ks, vs
+
+
+def test_memory_ema_closed_form():
+    """After folding frames E_1..E_n: M = a^(n-1) E_1 + sum_{i>=2} (1-a) a^(n-i) E_i (fp64), within the
+    rounding of n fp32 multiply-adds; memory exists only from the first eviction on."""
+    c, _, _ = _mem_cache((0.9, 0.5), 4)               # capacity 4 frames: nothing evicted yet
+    assert c.mem_frames == 0 and c.memory_entries() is None
+    c, _, _ = _mem_cache((0.9, 0.5), 9)
+    assert c.mem_frames == 5
+    # the evicted frames are the window's frames 1..5 in order (frame 0 is the sink); their stored keys
+    ref = OracleCache(1, 8, 6, 2, 64, 3, "bf16", raw_keys=True)
+    rng = np.random.default_rng(5)
+    for j in range(9):
+        k = round_to_bf16(rng.standard_normal((6, 2, 64)).astype(np.float32))
+        v = round_to_bf16(rng.standard_normal((6, 2, 64)).astype(np.float32))
+        ref.append(k, v, 1, j)
+    Ek = [ref.K[6 * f:6 * (f + 1)].astype(np.float64) for f in range(1, 6)]
+    Ev = [ref.V[6 * f:6 * (f + 1)].astype(np.float64) for f in range(1, 6)]
+    for m, a in enumerate((0.9, 0.5)):
+        n = len(Ek)
+        mk = a ** (n - 1) * Ek[0] + sum((1 - a) * a ** (n - i) * Ek[i - 1] for i in range(2, n + 1))
+        mv = a ** (n - 1) * Ev[0] + sum((1 - a) * a ** (n - i) * Ev[i - 1] for i in range(2, n + 1))
+        scale = max(np.max(np.abs(mk)), 1.0)
+        assert np.max(np.abs(c.mem_k[m] - mk)) < 8 * n * 2.0 ** -24 * scale * 4
+        assert np.max(np.abs(c.mem_v[m] - mv)) < 8 * n * 2.0 ** -24 * scale * 4
+    assert not np.array_equal(c.mem_k[0], c.mem_k[1])
+
+
+def test_memory_extreme_rates_are_exact():
+    """alpha = 1 keeps the first evicted frame, alpha = 0 the last one, bit for bit."""
+    c, _, _ = _mem_cache((1.0, 0.0), 9)
+    ref = OracleCache(1, 8, 6, 2, 64, 3, "bf16", raw_keys=True)
+    rng = np.random.default_rng(5)
+    for j in range(9):
+        k = round_to_bf16(rng.standard_normal((6, 2, 64)).astype(np.float32))
+        v = round_to_bf16(rng.standard_normal((6, 2, 64)).astype(np.float32))
+        ref.append(k, v, 1, j)
+    assert np.array_equal(c.mem_k[0], ref.K[6:12]) and np.array_equal(c.mem_v[0], ref.V[6:12])
+    assert np.array_equal(c.mem_k[1], ref.K[30:36]) and np.array_equal(c.mem_v[1], ref.V[30:36])
+
+
+def test_memory_placement():
+    """With alpha_short = 0 the short memory is the last evicted frame, and it is placed at t_w - 1, the time
+    that frame had: its attended keys equal that frame's keys in a plain rotated cache with a larger window.
+    With alpha_long = 1 the long memory is the first evicted frame, placed at t_w - 2: its keys equal that raw
+    frame rotated freshly at t_w - 2."""
+    c, ks, vs = _mem_cache((1.0, 0.0), 9)
+    big = OracleCache(1, 8, 6, 2, 64, 3, "bf16")
+    for j in range(9):
+        big.append(ks[j], vs[j], 1, j)
+    K, V, T = c.memory_entries()
+    t_w = int(c.t[c.n_sink])
+    assert t_w == 6 and np.all(T[:6] == 4) and np.all(T[6:] == 5)
+    assert np.array_equal(K[6:], big.K[30:36]) and np.array_equal(V[6:], big.V[30:36])
+    at = OracleCache(0, 1, 6, 2, 64, 3, "bf16")
+    at.append(ks[1], vs[1], 1, t_w - 2)
+    assert np.array_equal(K[:6], at.K) and np.array_equal(V[:6], at.V)
+
+
+def test_memory_follows_uniform_shift():
+    """A uniform retime of every entry moves the memory with the window (it is placed relative to the oldest
+    window entry), so attention with queries shifted alike changes only by rounding."""
+    c, _, _ = _mem_cache((0.9, 0.5), 9)
+    rng = np.random.default_rng(9)
+    q = round_to_bf16(rng.standard_normal((6, 2, 64)).astype(np.float32))
+    a = c.attend(q, 1, 8, f64=True)
+    c.retime(37, False)
+    b = c.attend(q, 1, 45, f64=True)
+    assert np.max(np.abs(a - b)) < 2e-2 and np.sqrt(np.mean((a - b) ** 2)) < 3e-3
+
+
+def test_memory_needs_raw_keys_and_refuses_compaction():
+    from oracle import OracleError
+    import pytest as _pt
+    with _pt.raises(OracleError):
+        OracleCache(1, 3, 6, 2, 64, 3, "bf16", memory=(0.9, 0.5))
+    c, _, _ = _mem_cache((0.9, 0.5), 6)
+    with _pt.raises(OracleError):
+        c.compact(np.arange(c.n))

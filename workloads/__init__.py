@@ -44,6 +44,8 @@ class Workload:
     cut_chunks: tuple = field(default_factory=tuple)
     # raw-key cache (keys kept un-rotated in time, placed at attention time)
     raw_keys: bool = False
+    # MemRoPE memory tokens (alpha_long, alpha_short) on a raw-key cache, or None
+    memory: tuple | None = None
 
     @property
     def frame_seqlen(self) -> int:
@@ -85,6 +87,9 @@ WORKLOADS = {
     "c5b": Workload("c5b", 5, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,)),
     # Relax Forcing frame selection on the same shape (sink 3 + History 4 + Tail 2 frames kept)
     "c5c": Workload("c5c", 6, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,)),
+    # MemRoPE: sliding window + sink on a raw-key cache whose evicted frames fold into long/short
+    # EMA memory tokens (rates 0.9 / 0.5)
+    "c6": Workload("c6", 7, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,), raw_keys=True, memory=(0.9, 0.5)),
     # Infinity-RoPE on a raw-key cache: every per-chunk shift is an index update
     "c5a_raw": Workload("c5a_raw", 4, 12, 128, "bf16", 30, 52, 3, 18, (3,) * 46 + (2,),
                         cut_chunks=(7, 20, 34), raw_keys=True),
@@ -120,4 +125,4 @@ def small_variant(w: Workload, heads: int | None = None, grid=None, n_chunks: in
     cf = w.chunk_frames if n_chunks is None else w.chunk_frames[:n_chunks]
     return Workload(w.name + "_small", w.cfg_id + 100, heads or w.heads, w.head_dim, w.dtype,
                     gh, gw, w.sink_frames, w.window_frames, tuple(cf), w.bank_frames,
-                    tuple(c for c in w.cut_chunks if c < len(cf)), w.raw_keys)
+                    tuple(c for c in w.cut_chunks if c < len(cf)), w.raw_keys, w.memory)
