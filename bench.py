@@ -152,6 +152,7 @@ def main():
     extras.update(per_gpu_share(dev, stream, ev, w))
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
     extras.update(raw_keys_ab(dev, stream, ev, flush, w))
+    extras.update(memrope_chunk(dev, stream, ev, flush, WORKLOADS["c6"]))
     # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
     cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cy = torch.empty_like(cx)
@@ -406,6 +407,53 @@ def raw_keys_ab(dev, stream, ev, flush, w):
             rt.append(a.elapsed_time(b) * 1e3)
     return {"raw_attend_ms": round(ms, 4), "raw_attend_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
             "raw_retime_us_cold": round(float(np.mean(rt)), 2)}
+
+
+def memrope_chunk(dev, stream, ev, flush, w):
+    """MemRoPE at its workload's shape (12 heads, 3 sink + 18 window frames, raw keys, memories at rates
+    0.9 / 0.5), MALL flushed: an append that evicts 3 frames (their fold into both memories, then the write)
+    next to the same append on a raw-key cache without memory; and the chunk's attention over sink + 2
+    memory frames + window (35880 keys)."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import chunk_inputs
+    S, H, D = w.frame_seqlen, w.heads, w.head_dim
+    chunks = [tuple(torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, c)) for c in range(4)]
+    out = {}
+    for tag, mem in (("memory", w.memory), ("plain", None)):
+        c = kvc.KVCache(w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16, raw_keys=True,
+                        memory=mem)
+        for i in range(8):
+            c.append(chunks[i % 4][1], chunks[i % 4][2], 3 * i)
+        ts = []
+        for i in range(10):
+            flush.sum()
+            a, b = ev(), ev()
+            a.record(stream)
+            c.append(chunks[i % 4][1], chunks[i % 4][2], 24 + 3 * i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(a.elapsed_time(b) * 1e3)
+        out[f"memrope_append_{tag}_us_cold"] = round(float(np.mean(ts)), 2)
+        if mem is not None:
+            q = chunks[0][0]
+            o = c.attend(q, 54)
+            tt = []
+            for i in range(8):
+                a, b = ev(), ev()
+                a.record(stream)
+                c.attend(q, 54, out=o)
+                b.record(stream)
+                torch.cuda.synchronize()
+                tt.append(a.elapsed_time(b))
+            ms = float(np.median(tt))
+            nk = c.info()["n_valid"] + 2 * S
+            out["memrope_attend_ms"] = round(ms, 4)
+            out["memrope_attend_tflops"] = round(4.0 * H * q.shape[0] * nk * D / (ms * 1e-3) / 1e12, 1)
+        del c
+    return out
 
 
 def vendor_context(dev, stream, H, N, Lk, D):

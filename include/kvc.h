@@ -77,6 +77,19 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
  * rotation of the raw key and kvc_retime only rewrites time indices.
  * kvc_score and kvc_relax_scores return KVC_EUNSUPPORTED on such a cache. */
 #define KVC_CREATE_RAW_KEYS 2u
+/* kvc_create: MemRoPE memory tokens (rCM length-extrapolation article: evicted
+ * frames are compressed into long- and short-term EMA memories instead of
+ * dropped); needs KVC_CREATE_RAW_KEYS.  Two memory frames (long, short), one
+ * token per grid position, live in 2 * frame_seqlen extra sink-region slots.
+ * Every frame a kvc_append evicts (whole frames, oldest first) updates both,
+ * per position, as M = a*M + (1-a)*E over the stored keys and the values, in
+ * fp32 with the products and the sum rounded separately; the first evicted
+ * frame initialises them (rates: kvc_set_memory_rates, default 0.9 / 0.5).
+ * Once a frame has been folded, kvc_attend also attends to the memories,
+ * rounded to the cache dtype and placed just before the oldest window entry
+ * (long at t_w - 2, short at t_w - 1).  kvc_compact, kvc_sink_push and
+ * block-causal attention return KVC_EUNSUPPORTED on such a cache. */
+#define KVC_CREATE_MEMORY 4u
 /* Largest |time index| and |retime delta| (the RoPE time table covers
  * positions -KVC_MAX_POS .. KVC_MAX_POS). */
 #define KVC_MAX_POS 16383
@@ -184,6 +197,18 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);
  * logical order; scratch: device, >= kvc_score_scratch_bytes. */
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
                      void* scratch, size_t scratch_bytes);
+
+/* Memory-token rates (KVC_CREATE_MEMORY caches): alpha_long for the long
+ * memory, alpha_short for the short one, each in [0, 1]; they apply to the
+ * frames folded from the next eviction on.  EUNSUPPORTED without memory. */
+kvc_status kvc_set_memory_rates(kvc_handle h, float alpha_long, float alpha_short);
+
+/* Copy the memory tokens out (for inspection; synchronizes the stream):
+ * k, v: device, [2 * frame_seqlen, heads, head_dim] in the cache dtype, the
+ * long memory's tokens then the short one's, keys in stored form (height and
+ * width bands rotated, time band raw); *n_folded (host) = frames folded so far
+ * (0: the memories are empty and not attended).  EUNSUPPORTED without memory. */
+kvc_status kvc_export_memory(kvc_handle h, void* k, void* v, int32_t* n_folded);
 
 /* Device scratch bytes kvc_relax_scores needs (depends only on the cache
  * geometry). */

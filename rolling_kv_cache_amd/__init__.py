@@ -22,13 +22,15 @@ KVC_T_NEWEST = -(2 ** 31)
 KVC_APPEND_REPLACE_NEWEST = 1
 KVC_CREATE_COMPACT = 1
 KVC_CREATE_RAW_KEYS = 2
+KVC_CREATE_MEMORY = 4
 KVC_MAX_POS = 16383
 KVC_MAX_Q_FRAMES = 32
 
 # Every symbol include/kvc.h declares.
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
             "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
-            "kvc_relax_scores", "kvc_compact", "kvc_sink_push", "kvc_info",
+            "kvc_relax_scores", "kvc_set_memory_rates", "kvc_export_memory", "kvc_compact", "kvc_sink_push",
+            "kvc_info",
             "kvc_slot_times", "kvc_export", "kvc_export_tables", "kvc_last_error")
 
 
@@ -67,6 +69,8 @@ def _load():
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
         "kvc_relax_scratch_bytes": (sz, [vp]),
         "kvc_relax_scores": (ctypes.c_int, [vp, i32, ctypes.c_float, vp, vp, sz]),
+        "kvc_set_memory_rates": (ctypes.c_int, [vp, ctypes.c_float, ctypes.c_float]),
+        "kvc_export_memory": (ctypes.c_int, [vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]),
         "kvc_compact": (ctypes.c_int, [vp, p32, i32]),
         "kvc_sink_push": (ctypes.c_int, [vp, i32, i32, i32]),
         "kvc_info": (ctypes.c_int, [vp, ctypes.POINTER(_Info)]),
@@ -98,26 +102,29 @@ def _dt(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported cache dtype {dtype}")
 
 
-def _create_flags(compact=False, raw_keys=False) -> int:
-    return (KVC_CREATE_COMPACT if compact else 0) | (KVC_CREATE_RAW_KEYS if raw_keys else 0)
+def _create_flags(compact=False, raw_keys=False, memory=False) -> int:
+    return ((KVC_CREATE_COMPACT if compact else 0) | (KVC_CREATE_RAW_KEYS if raw_keys else 0)
+            | (KVC_CREATE_MEMORY if memory else 0))
 
 
 def workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype=torch.bfloat16,
-                    bank_frames=0, compact=False, raw_keys=False) -> int:
+                    bank_frames=0, compact=False, raw_keys=False, memory=False) -> int:
     return int(lib.kvc_workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, _dt(dtype),
-                                       bank_frames, _create_flags(compact, raw_keys)))
+                                       bank_frames, _create_flags(compact, raw_keys, memory)))
 
 
 class KVCache:
     """One layer's cache.  Methods mirror the C calls: append, attend, retime, score, compact, sink_push."""
 
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
-                 dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False):
+                 dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False,
+                 memory=None):
+        """memory: (alpha_long, alpha_short) for MemRoPE memory tokens on a raw-key cache, or None."""
         self.S, self.H, self.D = frame_seqlen, heads, head_dim
         self.dtype = dtype
         self.device = torch.device(device)
         nbytes = workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype, bank_frames,
-                                 compact, raw_keys)
+                                 compact, raw_keys, memory is not None)
         if nbytes == 0:
             raise KVCError(KVC_EINVAL, "unsupported geometry")
         self._ws_raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -126,10 +133,12 @@ class KVCache:
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
         _check(lib.kvc_create(sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w, _dt(dtype),
-                              bank_frames, _create_flags(compact, raw_keys),
+                              bank_frames, _create_flags(compact, raw_keys, memory is not None),
                               ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
                               ctypes.c_void_p(self._stream.cuda_stream), ctypes.byref(h)))
         self._h = h
+        if memory is not None:
+            _check(lib.kvc_set_memory_rates(h, float(memory[0]), float(memory[1])))
         self._score_scratch = None
         self._relax_scratch = None
 
@@ -225,6 +234,18 @@ class KVCache:
         _check(lib.kvc_relax_scores(self._h, int(tail_frames), float(weight), ctypes.c_void_p(out.data_ptr()),
                                     ctypes.c_void_p(self._relax_scratch.data_ptr() + off), need))
         return out
+
+    def set_memory_rates(self, alpha_long: float, alpha_short: float):
+        _check(lib.kvc_set_memory_rates(self._h, float(alpha_long), float(alpha_short)))
+
+    def export_memory(self):
+        """(k, v, n_folded): the long then the short memory tokens [2S, H, D] (keys in stored form)."""
+        k = torch.empty((2 * self.S, self.H, self.D), dtype=self.dtype, device=self.device)
+        v = torch.empty_like(k)
+        n = ctypes.c_int32()
+        _check(lib.kvc_export_memory(self._h, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                     ctypes.byref(n)))
+        return k, v, int(n.value)
 
     def compact(self, keep_idx):
         keep = np.ascontiguousarray(np.asarray(keep_idx, dtype=np.int32))

@@ -145,6 +145,29 @@ struct ScoreArgs {
   float scale;
 };
 
+// MemRoPE memory tokens: fold the oldest n_frames window frames (about to be
+// evicted) into the long (m = 0) and short (m = 1) EMA memories.
+struct MemFoldArgs {
+  RegionPtrs win;                         // the window region holding the evicted frames
+  RegionPtrs sink;                        // memory slots: sink region slots [mem_lo, mem_lo + 2S)
+  float* state_k;                         // [2][H][S][D] fp32
+  float* state_v;                         // [2][H][D][S] fp32
+  int32_t hw, W_tok;                      // window ring head and size (logical -> physical)
+  int32_t n_frames;                       // frames folded, oldest first
+  int32_t init;                           // 1: the first frame initialises both memories
+  int32_t mem_lo;
+  float alpha[2];
+  Geo geo;
+};
+
+struct MemExportArgs {
+  RegionPtrs sink;
+  int32_t mem_lo;
+  void* k;                                // [2S][H][D] stored-form keys (long, then short)
+  void* v;
+  Geo geo;
+};
+
 struct RelaxArgs {
   KeyRegions keys;                        // ka / kb / cap of the sink and current window
   int32_t ns, hs, S_tok, nw, hw, W_tok;   // logical -> physical map

@@ -40,6 +40,7 @@ struct Layout {
   int32_t D = 0, DA = 0, DB = 0, dt = 0, bw = 0, esz = 0;
   RegionLayout sink{}, win[2]{};
   size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, att_flags = 0, total = 0;
+  size_t mem_k = 0, mem_v = 0;
 };
 
 Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_t H, int32_t D, kvc_dtype dt,
@@ -53,7 +54,8 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   if (s_tok + w_tok > (1 << 26) || b_tok > (1 << 26) || H > 4096) return L;
   L.S_tok = (int32_t)s_tok;
   L.W_tok = (int32_t)w_tok;
-  L.SP = round64(L.S_tok);
+  // memory tokens (MemRoPE) live in 2S extra sink-region slots after the sink
+  L.SP = round64(L.S_tok + ((cflags & KVC_CREATE_MEMORY) ? 2 * S : 0));
   L.WP = round64(L.W_tok);
   L.bank_tok = (int32_t)b_tok;
   L.D = D;
@@ -89,6 +91,10 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   L.keep = take((size_t)L.WP * 4);
   // one recompute flag per 256-query attention block of the largest query chunk
   L.att_flags = take((size_t)H * (((size_t)KVC_MAX_Q_FRAMES * S + 255) / 256) * 4);
+  if (cflags & KVC_CREATE_MEMORY) {
+    L.mem_k = take((size_t)2 * H * S * D * 4);
+    L.mem_v = take((size_t)2 * H * S * D * 4);
+  }
   L.total = off;
   L.ok = true;
   return L;
@@ -115,6 +121,8 @@ struct kvc_cache {
   hipStream_t stream;
   kvc::RingState st;
   bool poisoned;
+  float mem_alpha[2];
+  int32_t mem_frames;       // frames folded into the memories so far
 };
 
 namespace {
@@ -251,7 +259,10 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   Layout L = make_layout(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames, create_flags);
   if (!L.ok) return fail(KVC_EINVAL, "unsupported geometry (head_dim must be 64 or 128; sizes positive)");
   if (grid_w < 1 || frame_seqlen % grid_w != 0) return fail(KVC_EINVAL, "frame_seqlen must be a multiple of grid_w");
-  if (create_flags & ~(KVC_CREATE_COMPACT | KVC_CREATE_RAW_KEYS)) return fail(KVC_EINVAL, "unknown create flag");
+  if (create_flags & ~(KVC_CREATE_COMPACT | KVC_CREATE_RAW_KEYS | KVC_CREATE_MEMORY))
+    return fail(KVC_EINVAL, "unknown create flag");
+  if ((create_flags & KVC_CREATE_MEMORY) && !(create_flags & KVC_CREATE_RAW_KEYS))
+    return fail(KVC_EINVAL, "memory tokens need KVC_CREATE_RAW_KEYS");
   if ((create_flags & KVC_CREATE_RAW_KEYS) && !(dt == KVC_BF16 || dt == KVC_F32))
     return fail(KVC_EINVAL, "raw keys need a bf16 or fp32 cache");
   if (!workspace) return fail(KVC_EINVAL, "workspace is null");
@@ -285,6 +296,9 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->att_flags = (int32_t*)(h->ws + L.att_flags);
   h->keep_pinned = nullptr;
   h->keep_pending = false;
+  h->mem_alpha[0] = 0.9f;
+  h->mem_alpha[1] = 0.5f;
+  h->mem_frames = 0;
   h->st.init(frame_seqlen, L.S_tok, L.W_tok);
   hipError_t e = hipSuccess;
   if (create_flags & KVC_CREATE_COMPACT) {
@@ -350,9 +364,30 @@ kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_fram
   int32_t bank_lo = 0, bank_hi = 0;
   if (h->L.bank_tok > 0 && g0 < h->L.bank_tok) bank_hi = (int32_t)std::min<int64_t>(N, h->L.bank_tok - g0);
   const int64_t HD = (int64_t)h->H * h->D;
+  // MemRoPE: the frames this append evicts (the oldest window entries) fold into the memories first
+  const int32_t evicted = replace ? 0 : h->st.n_valid() + N - nx.n_valid();
+  hipError_t e = hipSuccess;
+  if ((h->cflags & KVC_CREATE_MEMORY) && evicted > 0) {
+    if (evicted % h->S != 0 || h->st.ns != h->L.S_tok) return fail(KVC_ESTATE, "memory folds whole frames");
+    kvc::MemFoldArgs m{};
+    m.win = cur_win(h);
+    m.sink = h->sink;
+    m.state_k = (float*)(h->ws + h->L.mem_k);
+    m.state_v = (float*)(h->ws + h->L.mem_v);
+    m.hw = h->st.hw;
+    m.W_tok = h->st.W_tok;
+    m.n_frames = evicted / h->S;
+    m.init = h->mem_frames == 0 ? 1 : 0;
+    m.mem_lo = h->L.S_tok;
+    m.alpha[0] = h->mem_alpha[0];
+    m.alpha[1] = h->mem_alpha[1];
+    m.geo = h->geo;
+    e = kvc::launch_mem_fold(m, h->stream);
+  }
   // the window region read by the kernel must be the post-plan buffer (unchanged by append)
-  hipError_t e = launch_segments(h, segs, k, v, HD, h->D, HD, h->D, t_index, g0, bank_lo, bank_hi);
+  if (e == hipSuccess) e = launch_segments(h, segs, k, v, HD, h->D, HD, h->D, t_index, g0, bank_lo, bank_hi);
   if (kvc_status s = device_result(h, e, "append")) return s;
+  if (h->cflags & KVC_CREATE_MEMORY) h->mem_frames += evicted / h->S;
   h->st = std::move(nx);
   return KVC_OK;
 }
@@ -382,6 +417,16 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
   a.causal_block = causal_block;
   a.raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
   a.mem_lo = INT32_MAX;
+  if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0) {
+    // the memories sit right before the oldest window entry: long at t_w - 2, short at t_w - 1
+    if (causal_block > 0) return fail(KVC_EUNSUPPORTED, "block-causal attention with memory tokens");
+    const int32_t t_w = h->st.t_at(kvc::kWin, h->st.hw);
+    if (t_w - 2 < -KVC_MAX_POS) return fail(KVC_EINVAL, "memory time out of range");
+    a.mem_lo = h->L.S_tok;
+    a.mem_t[0] = t_w - 2;
+    a.mem_t[1] = t_w - 1;
+    a.keys.n[0] = h->L.S_tok + 2 * h->S;
+  }
   const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
   hipError_t e = kvc::launch_attend(a, h->stream, force_general);
   return device_result(h, e, "attend");
@@ -527,8 +572,36 @@ kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, flo
   return device_result(h, e, "relax scores");
 }
 
+kvc_status kvc_set_memory_rates(kvc_handle h, float alpha_long, float alpha_short) {
+  if (kvc_status s = check(h)) return s;
+  if (!(h->cflags & KVC_CREATE_MEMORY)) return fail(KVC_EUNSUPPORTED, "no memory tokens (KVC_CREATE_MEMORY)");
+  if (!(alpha_long >= 0.f && alpha_long <= 1.f && alpha_short >= 0.f && alpha_short <= 1.f))
+    return fail(KVC_EINVAL, "memory rates outside [0, 1]");
+  h->mem_alpha[0] = alpha_long;
+  h->mem_alpha[1] = alpha_short;
+  return KVC_OK;
+}
+
+kvc_status kvc_export_memory(kvc_handle h, void* k, void* v, int32_t* n_folded) {
+  if (kvc_status s = check(h)) return s;
+  if (!(h->cflags & KVC_CREATE_MEMORY)) return fail(KVC_EUNSUPPORTED, "no memory tokens (KVC_CREATE_MEMORY)");
+  if (!k || !v || !n_folded) return fail(KVC_EINVAL, "null argument");
+  kvc::MemExportArgs m{};
+  m.sink = h->sink;
+  m.mem_lo = h->L.S_tok;
+  m.k = k;
+  m.v = v;
+  m.geo = h->geo;
+  hipError_t e = kvc::launch_mem_export(m, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (kvc_status s = device_result(h, e, "export memory")) return s;
+  *n_folded = h->mem_frames;
+  return KVC_OK;
+}
+
 kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
   if (kvc_status s = check(h)) return s;
+  if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "compact is not available with memory tokens");
   if (!(h->cflags & KVC_CREATE_COMPACT)) return fail(KVC_EUNSUPPORTED, "compact needs KVC_CREATE_COMPACT");
   kvc::RingState nx = h->st;
   std::vector<int32_t> src;
@@ -565,6 +638,7 @@ kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
 
 kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int32_t t_index) {
   if (kvc_status s = check(h)) return s;
+  if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "sink push is not available with memory tokens");
   if (h->L.bank_tok == 0) return fail(KVC_ESTATE, "no bank (bank_frames was 0)");
   if (h->st.global_end < h->L.bank_tok) return fail(KVC_ESTATE, "bank not complete yet");
   if (bank_frame < 0 || n_frames < 1 || (int64_t)(bank_frame + n_frames) * h->S > h->L.bank_tok)

@@ -765,3 +765,152 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general) {
 }
 
 }  // namespace kvc
+
+namespace kvc {
+
+// ----------------------------------------------------------------------------
+// MemRoPE memory fold.  Key blocks: thread (head, grid position p, 16-byte
+// chunk c of the key row) walks the evicted frames oldest first, reading the
+// chunk of the token at position p (consecutive threads read consecutive
+// chunks and rows), and keeps both memories' fp32 state for its E dims in
+// registers.  Value blocks: thread (head, dim d, position p) does the same on
+// the tile-transposed values (consecutive p are consecutive slots).  Each
+// update is M = a*M + (1-a)*E with the products and the sum rounded
+// separately; the state is written back and the memory slots get it rounded to
+// the cache dtype.
+template <typename T>
+__device__ __forceinline__ float ema(float m, float e, float a, float b) {
+#pragma clang fp contract(off)
+  const float x = a * m;
+  const float y = b * e;
+  return x + y;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
+  constexpr int E = Elem<T>::E, CH = D / E;
+  const Geo& g = a.geo;
+  const float al[2] = {a.alpha[0], a.alpha[1]};
+  const float be[2] = {1.f - a.alpha[0], 1.f - a.alpha[1]};
+  if ((int)blockIdx.x < nkb) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int c = (int)(id % CH);
+    const int64_t hp = id / CH;
+    if (hp >= (int64_t)g.H * g.S) return;
+    const int p = (int)(hp % g.S), h = (int)(hp / g.S);
+    const int d0 = c * E;
+    float st[2][E];
+    for (int f = 0; f < a.n_frames; ++f) {
+      const int slot = (a.hw + f * g.S + p) % a.W_tok;
+      const T* src = d0 < g.DA ? (const T*)a.win.ka + ((int64_t)h * a.win.cap + slot) * g.DA + d0
+                               : (const T*)a.win.kb + ((int64_t)h * a.win.cap + slot) * g.DB + (d0 - g.DA);
+      Vec16<T> x;
+      x.u = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (f == 0) {
+          if (a.init) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) st[m][e] = Elem<T>::ld(x.e[e]);
+            continue;
+          }
+          const float* sp = a.state_k + (((int64_t)m * g.H + h) * g.S + p) * D + d0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) st[m][e] = sp[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) st[m][e] = ema<T>(st[m][e], Elem<T>::ld(x.e[e]), al[m], be[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float* sp = a.state_k + (((int64_t)m * g.H + h) * g.S + p) * D + d0;
+      Vec16<T> y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        sp[e] = st[m][e];
+        y.e[e] = Elem<T>::st(st[m][e]);
+      }
+      const int slot = a.mem_lo + m * g.S + p;
+      T* dst = d0 < g.DA ? (T*)a.sink.ka + ((int64_t)h * a.sink.cap + slot) * g.DA + d0
+                         : (T*)a.sink.kb + ((int64_t)h * a.sink.cap + slot) * g.DB + (d0 - g.DA);
+      *reinterpret_cast<uint4*>(dst) = y.u;
+    }
+    return;
+  }
+  const int64_t id = (int64_t)(blockIdx.x - nkb) * 256 + threadIdx.x;
+  const int p = (int)(id % g.S);
+  const int64_t hd = id / g.S;
+  if (hd >= (int64_t)g.H * D) return;
+  const int d = (int)(hd % D), h = (int)(hd / D);
+  float st[2];
+  for (int f = 0; f < a.n_frames; ++f) {
+    const int slot = (a.hw + f * g.S + p) % a.W_tok;
+    const float e = Elem<T>::ld(((const T*)a.win.v)[v_index(h, a.win.cap, D, slot, d)]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (f == 0) {
+        if (a.init) {
+          st[m] = e;
+          continue;
+        }
+        st[m] = a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p];
+      }
+      st[m] = ema<T>(st[m], e, al[m], be[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p] = st[m];
+    ((T*)a.sink.v)[v_index(h, a.sink.cap, D, a.mem_lo + m * g.S + p, d)] = Elem<T>::st(st[m]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void mem_export_kernel(MemExportArgs a) {
+  const Geo& g = a.geo;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)2 * g.S * g.H * D) return;
+  const int d = (int)(id % D);
+  const int64_t jh = id / D;
+  const int h = (int)(jh % g.H), j = (int)(jh / g.H);
+  const int slot = a.mem_lo + j;
+  const T kv = d < g.DA ? ((const T*)a.sink.ka)[((int64_t)h * a.sink.cap + slot) * g.DA + d]
+                        : ((const T*)a.sink.kb)[((int64_t)h * a.sink.cap + slot) * g.DB + (d - g.DA)];
+  ((T*)a.k)[id] = kv;
+  ((T*)a.v)[id] = ((const T*)a.sink.v)[v_index(h, a.sink.cap, D, slot, d)];
+}
+
+template <typename T, int D>
+static hipError_t mem_fold_launch(const MemFoldArgs& a, hipStream_t s) {
+  constexpr int CH = D / Elem<T>::E;
+  const int64_t nk = (int64_t)a.geo.H * a.geo.S * CH, nv = (int64_t)a.geo.H * D * a.geo.S;
+  const int nkb = (int)((nk + 255) / 256), nvb = (int)((nv + 255) / 256);
+  hipLaunchKernelGGL((mem_fold_kernel<T, D>), dim3(nkb + nvb), dim3(256), 0, s, a, nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_mem_fold(const MemFoldArgs& a, hipStream_t s) {
+  if (a.n_frames <= 0) return hipSuccess;
+  if (a.geo.esz == 2) return a.geo.D == 128 ? mem_fold_launch<uint16_t, 128>(a, s) : mem_fold_launch<uint16_t, 64>(a, s);
+  return a.geo.D == 128 ? mem_fold_launch<float, 128>(a, s) : mem_fold_launch<float, 64>(a, s);
+}
+
+hipError_t launch_mem_export(const MemExportArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)2 * a.geo.S * a.geo.H * a.geo.D;
+  const unsigned b = (unsigned)((n + 255) / 256);
+  if (a.geo.esz == 2) {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((mem_export_kernel<uint16_t, 128>), dim3(b), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((mem_export_kernel<uint16_t, 64>), dim3(b), dim3(256), 0, s, a);
+  } else {
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL((mem_export_kernel<float, 128>), dim3(b), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((mem_export_kernel<float, 64>), dim3(b), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

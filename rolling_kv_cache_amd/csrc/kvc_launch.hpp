@@ -19,6 +19,9 @@ hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
 // Scores: the matrix-core passes for bf16 with head_dim 128, else the general
 // per-row/per-column path (force_general selects the latter).
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general);
+// MemRoPE: fold evicted frames into the EMA memories; copy the memory slots out
+hipError_t launch_mem_fold(const MemFoldArgs& a, hipStream_t s);
+hipError_t launch_mem_export(const MemExportArgs& a, hipStream_t s);
 // frame sums, their Gram matrix, then the Relax Forcing scores
 hipError_t launch_relax(const RelaxArgs& a, hipStream_t s);
 // rows + columns passes over a query window already rotated into qbf

@@ -26,7 +26,8 @@ def dev(x: np.ndarray, w) -> torch.Tensor:
 def new_cache(w, compact=False):
     from rolling_kv_cache_amd import KVCache
     return KVCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w,
-                   dtype=torch_dtype(w), bank_frames=w.bank_frames, compact=compact, raw_keys=w.raw_keys)
+                   dtype=torch_dtype(w), bank_frames=w.bank_frames, compact=compact, raw_keys=w.raw_keys,
+                   memory=w.memory)
 
 
 def bits(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -50,6 +50,15 @@ def _run_config(name, full_rows_at=(), every=1, compact=False, sample_rows=512):
             got = out if rows is None else out[rows]
             stats.append(check_attention(got, ref, f"{name} chunk {i}"))
             q_prev, q_prev_d = q, qd
+    if w.memory is not None:
+        from gpu_util import bits, gpu_bits
+        k, v, n = gc.export_memory()
+        c = run.cache
+        assert n == c.mem_frames > 0
+        assert np.array_equal(gpu_bits(k), bits(np.concatenate([c._store(c.mem_k[0]), c._store(c.mem_k[1])]),
+                                                w.dtype))
+        assert np.array_equal(gpu_bits(v), bits(np.concatenate([c._store(c.mem_v[0]), c._store(c.mem_v[1])]),
+                                                w.dtype))
     mx = max(s[0] for s in stats)
     rr = max(s[1] for s in stats)
     log(f"{name}: worst max_abs {mx:.3e} worst rel_rms {rr:.3e} over {len(stats)} chunks")
@@ -118,6 +127,13 @@ def test_c5a_raw_keys_infinity_rope():
     """Infinity-RoPE on a raw-key cache: the per-chunk shifts only move time indices and every attended key is
     the raw key rotated once at its current time."""
     _run_config("c5a_raw", full_rows_at=(7,), compact=True, sample_rows=256)
+
+
+@pytest.mark.timeout(900)
+def test_c6_memrope_memory_tokens():
+    """MemRoPE on the 12-head 3 + 18-frame shape: from chunk 7 on every chunk folds 3 evicted frames into the
+    long/short memories, which attention sees beside the sink and window; memory state bit-exact at the end."""
+    _run_config("c6", full_rows_at=(7,), sample_rows=256)
 
 
 @pytest.mark.timeout(900)

@@ -408,3 +408,82 @@ def test_raw_keys_negative_times_and_block_causal():
     with pytest.raises(KVCError) as e:
         gc.relax_scores(2)
     assert e.value.code == 5
+
+
+# ---------------------------------------------------------------- MemRoPE memory tokens
+def _check_memory(gc, oc, w, tag):
+    from gpu_util import bits
+    k, v, n = gc.export_memory()
+    assert n == oc.mem_frames, (tag, n, oc.mem_frames)
+    if n == 0:
+        return
+    ko = np.concatenate([oc._store(oc.mem_k[0]), oc._store(oc.mem_k[1])])
+    vo = np.concatenate([oc._store(oc.mem_v[0]), oc._store(oc.mem_v[1])])
+    assert np.array_equal(gpu_bits(k), bits(ko, w.dtype)), f"{tag}: memory keys differ"
+    assert np.array_equal(gpu_bits(v), bits(vo, w.dtype)), f"{tag}: memory values differ"
+
+
+def _drive_memory(w, general=False):
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                     raw_keys=True, memory=w.memory)
+    for i in range(w.n_chunks):
+        q, k, v = chunk_inputs(w, i)
+        t0 = w.chunk_start_frame(i)
+        gc.append(dev(k, w), dev(v, w), t0)
+        oc.append(k, v, w.chunk_frames[i], t0)
+        if general:
+            os.environ["KVC_ATTEND_GENERAL"] = "1"
+        try:
+            out = gc.attend(dev(q, w), t0).float().cpu().numpy()
+        finally:
+            os.environ.pop("KVC_ATTEND_GENERAL", None)
+        assert_state_equal(gc, oc, w, f"{w.name} chunk {i}")
+        _check_memory(gc, oc, w, f"{w.name} chunk {i}")
+        check_attention(out, oc.attend(q, w.chunk_frames[i], t0, f64=w.dtype == "f32"), f"{w.name} chunk {i}")
+    assert oc.mem_frames > 0
+    return gc, oc
+
+
+MEM_SMALL = _replace(SMALL_SW, name="mem_small", raw_keys=True, memory=(0.9, 0.5))
+
+
+@pytest.mark.parametrize("general", [False, True])
+def test_memory_tokens_small(general):
+    """Memory state bit-exact and attention (sink + memories + window) after every chunk, with 60-token
+    frames whose memory slots straddle 64-slot tiles."""
+    _drive_memory(MEM_SMALL, general=general)
+
+
+def test_memory_tokens_tiny_fp32_and_extreme_rates():
+    _drive_memory(_replace(WORKLOADS["tiny"], name="tiny_mem", raw_keys=True, memory=(0.7, 0.2)))
+    _drive_memory(_replace(MEM_SMALL, name="mem_extreme", memory=(1.0, 0.0)))
+
+
+def test_memory_tokens_errors():
+    from rolling_kv_cache_amd import KVCError, KVCache
+    w = MEM_SMALL
+    with pytest.raises(KVCError) as e:
+        KVCache(2, 6, w.frame_seqlen, 3, 128, w.grid_w, memory=(0.9, 0.5))     # memory without raw keys
+    assert e.value.code == 1
+    gc, _ = _drive_memory(_replace(MEM_SMALL, chunk_frames=(3, 3, 3)))
+    for rates in ((1.5, 0.5), (0.5, -0.1), (float("nan"), 0.5)):
+        with pytest.raises(KVCError) as e:
+            gc.set_memory_rates(*rates)
+        assert e.value.code == 1
+    q, _, _ = chunk_inputs(w, 0, frames=2)
+    with pytest.raises(KVCError) as e:
+        gc.attend_block_causal(dev(q, w), 0, 1)
+    assert e.value.code == 5
+    cc = new_cache(_replace(MEM_SMALL, name="mem_c"), compact=True)
+    for i in range(3):
+        _, k, v = chunk_inputs(w, i, frames=3)
+        cc.append(dev(k, w), dev(v, w), 3 * i)
+    with pytest.raises(KVCError) as e:
+        cc.compact(list(range(cc.info()["n_valid"])))
+    assert e.value.code == 5
+    plain = new_cache(_replace(SMALL_SW, name="plain"))
+    for call in (plain.export_memory, lambda: plain.set_memory_rates(0.5, 0.5)):
+        with pytest.raises(KVCError) as e:
+            call()
+        assert e.value.code == 5
