@@ -281,13 +281,21 @@ class OracleCache:
         g0 = self.newest[0]
         return int(self.t[np.nonzero(self.g == g0)[0][0]])
 
-    def attend(self, q, frames, t0=None, rows=None, f64=False):
-        """softmax(q_hat K^T / sqrt(D)) V over every valid entry, no mask; q rotated at t0."""
+    def attend(self, q, frames, t0=None, rows=None, f64=False, max_keys=None):
+        """softmax(q_hat K^T / sqrt(D)) V over every valid entry, no mask; q rotated at t0.
+
+        max_keys (LingBot-World 2.0 article, max_attention_size: queries read only the last
+        max_attention_size positions of the cache buffer, whose order is sink first, then the window
+        oldest to newest): attend to the last max_keys entries in logical order only."""
         t0 = self.newest_time() if t0 is None else t0
         qh = self.rotate_queries(q, frames, t0)
         if rows is not None:
             qh = qh[np.asarray(rows)]
         K, V = self.attention_keys(), self.V
+        if max_keys is not None and max_keys < self.n:
+            if max_keys < 1 or self.memory is not None:
+                raise OracleError("max_keys")
+            K, V = K[self.n - max_keys:], V[self.n - max_keys:]
         mem = self.memory_entries()
         if mem is not None:
             K = np.concatenate([K, mem[0]])

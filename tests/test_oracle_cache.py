@@ -244,3 +244,32 @@ def test_block_causal_one_block_is_full_attention():
     a = oc.attend_block_causal(q, 4, 0, 4, f64=True)
     b = oc.attend(q, 4, 0, f64=True)
     assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- max_attention_size (attention over the newest entries)
+def test_max_keys_limits_attention_to_the_newest_entries():
+    """A limit at or above n_valid changes nothing; a limit equal to the newest chunk's size equals a cache
+    holding only that chunk; a limit inside the sink drops the oldest sink entries; brute-force mask."""
+    S, H, D = 8, 2, 16
+    oc = OracleCache(2, 5, S, H, D, 4, "f32")
+    ks, vs = [], []
+    for f in range(9):
+        k = gen(31, f, 1, S, H, D, "f32")
+        v = gen(31, f, 2, S, H, D, "f32")
+        oc.append(k, v, 1, f)
+        ks.append(k)
+        vs.append(v)
+    q = gen(31, 99, 0, S, H, D, "f32")
+    full = oc.attend(q, 1, 8, f64=True)
+    assert np.array_equal(oc.attend(q, 1, 8, f64=True, max_keys=oc.n), full)
+    assert np.array_equal(oc.attend(q, 1, 8, f64=True, max_keys=10 * oc.n), full)
+    only = OracleCache(0, 1, S, H, D, 4, "f32")
+    only.append(ks[8], vs[8], 1, 8)
+    assert np.allclose(oc.attend(q, 1, 8, f64=True, max_keys=S), only.attend(q, 1, 8, f64=True),
+                       rtol=0, atol=1e-13)
+    qh = oc.rotate_queries(q, 1, 8).astype(np.float64)
+    for m in (3, 13, 45, 50):
+        got = oc.attend(q, 1, 8, f64=True, max_keys=m)
+        vis = list(range(oc.n - m, oc.n))
+        ref = attention_loops_f64(qh.tolist(), oc.K[vis].tolist(), oc.V[vis].tolist())
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), m
