@@ -198,6 +198,16 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
                      void* scratch, size_t scratch_bytes);
 
+/* Limit what kvc_attend reads to the newest max_keys valid entries in logical
+ * order (LingBot-World 2.0 article, max_attention_size: queries read only the
+ * last max_attention_size positions of the cache buffer, sink first), i.e. the
+ * oldest entries -- the sink first once the limit is below the window's
+ * length -- drop out of attention without leaving the cache.  0 (the default)
+ * = no limit.  EINVAL if max_keys < 0.  A limited attend returns
+ * KVC_EUNSUPPORTED when the visible entries span a Rolling-Sink sink that has
+ * rolled, with memory tokens, or for block-causal attention. */
+kvc_status kvc_set_attention_limit(kvc_handle h, int32_t max_keys);
+
 /* Memory-token rates (KVC_CREATE_MEMORY caches): alpha_long for the long
  * memory, alpha_short for the short one, each in [0, 1]; they apply to the
  * frames folded from the next eviction on.  EUNSUPPORTED without memory. */

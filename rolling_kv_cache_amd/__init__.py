@@ -29,7 +29,8 @@ KVC_MAX_Q_FRAMES = 32
 # Every symbol include/kvc.h declares.
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
             "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
-            "kvc_relax_scores", "kvc_set_memory_rates", "kvc_export_memory", "kvc_compact", "kvc_sink_push",
+            "kvc_relax_scores", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
+            "kvc_compact", "kvc_sink_push",
             "kvc_info",
             "kvc_slot_times", "kvc_export", "kvc_export_tables", "kvc_last_error")
 
@@ -69,6 +70,7 @@ def _load():
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
         "kvc_relax_scratch_bytes": (sz, [vp]),
         "kvc_relax_scores": (ctypes.c_int, [vp, i32, ctypes.c_float, vp, vp, sz]),
+        "kvc_set_attention_limit": (ctypes.c_int, [vp, i32]),
         "kvc_set_memory_rates": (ctypes.c_int, [vp, ctypes.c_float, ctypes.c_float]),
         "kvc_export_memory": (ctypes.c_int, [vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]),
         "kvc_compact": (ctypes.c_int, [vp, p32, i32]),
@@ -234,6 +236,10 @@ class KVCache:
         _check(lib.kvc_relax_scores(self._h, int(tail_frames), float(weight), ctypes.c_void_p(out.data_ptr()),
                                     ctypes.c_void_p(self._relax_scratch.data_ptr() + off), need))
         return out
+
+    def set_attention_limit(self, max_keys: int):
+        """Attend only to the newest max_keys entries (0: no limit)."""
+        _check(lib.kvc_set_attention_limit(self._h, int(max_keys)))
 
     def set_memory_rates(self, alpha_long: float, alpha_short: float):
         _check(lib.kvc_set_memory_rates(self._h, float(alpha_long), float(alpha_short)))

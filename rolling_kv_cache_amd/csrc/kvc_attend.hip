@@ -134,14 +134,16 @@ __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, in
   }
 }
 
-__device__ __forceinline__ void mask_tile(f32x16_t* s, int nv, int hl) {
-  if (nv >= kBN) return;
+// keys of the tile outside [lead, nv) get -inf (lead > 0 only in the first tile
+// of a range that starts inside a tile)
+__device__ __forceinline__ void mask_tile(f32x16_t* s, int lead, int nv, int hl) {
+  if (nv >= kBN && lead <= 0) return;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kb * 32 + perm_row((i >> 2) * 8 + hl * 4 + (i & 3));
-      if (key >= nv) s[kb][i] = -INFINITY;
+      if (key >= nv || key < lead) s[kb][i] = -INFINITY;
     }
 }
 
@@ -163,13 +165,28 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o
     }
 }
 
+// Key tiles in visiting order: the tiles covering region 0's visible slots
+// [lo0, n0), then region 1's.  base = first slot of the tile (64-aligned),
+// valid = slots of the tile before the range end, lead = slots of the tile
+// before the range start (> 0 only in a range's first tile).
 struct TileSeq {
   int ntile0, ntiles;
-  int n0, n1;
+  int t00, t01;            // first tile of each range
+  int lo0, lo1, n0, n1;
   __device__ __forceinline__ int region(int it) const { return it < ntile0 ? 0 : 1; }
-  __device__ __forceinline__ int base(int it) const { return (it < ntile0 ? it : it - ntile0) * kBN; }
+  __device__ __forceinline__ int base(int it) const { return (it < ntile0 ? t00 + it : t01 + it - ntile0) * kBN; }
   __device__ __forceinline__ int valid(int it) const { return (it < ntile0 ? n0 : n1) - base(it); }
+  __device__ __forceinline__ int lead(int it) const { return (it < ntile0 ? lo0 : lo1) - base(it); }
 };
+
+__device__ __forceinline__ TileSeq tile_seq(const KeyRegions& k, int ntile0, int ntiles) {
+  return TileSeq{ntile0, ntiles, k.lo[0] / kBN, k.lo[1] / kBN, k.lo[0], k.lo[1], k.n[0], k.n[1]};
+}
+
+// tiles covering region r's visible slots
+__host__ __device__ __forceinline__ int range_tiles(const KeyRegions& k, int r) {
+  return k.n[r] > k.lo[r] ? (k.n[r] + kBN - 1) / kBN - k.lo[r] / kBN : 0;
+}
 
 // ---------------------------------------------------------------------------
 // Interleaved pipeline (v3).  LDS rows are padded by one 16-byte chunk (K rows
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * kBM + wave * 32 + l32;
-  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
 
@@ -298,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
 
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
   TileRegs tr;
-  // K(0), V(0) -> buffer 0; K(1) -> buffer 1
-  tile_load(tr, tp, 0, 0);
+  // K(0), V(0) -> buffer 0; K(1) -> buffer 1 (tile 0 starts at slot 0 unless attention is limited)
+  tile_load(tr, tp, ts.region(0), ts.base(0));
   tile_store_padded(tr, lks[0], lvs[0], tid);
   {
     const int t1 = min(1, last);
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
         sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
       }
     }
-    mask_tile(sa, ts.valid(0), hl);
+    mask_tile(sa, ts.lead(0), ts.valid(0), hl);
   }
 
   // one pipeline step: scur holds S^T(t); computes S^T(t+1) into snext
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
     }
     lsum = lsum * alpha + psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
-    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    mask_tile(snext, ts.lead(min(t + 1, last)), ts.valid(min(t + 1, last)), hl);
     tile_store_padded(tr, lks[t & 1], lvs[(t + 1) & 1], tid);
     __syncthreads();
   };
@@ -528,7 +545,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
   int nt = ntiles, lim = 0, lim_lo = 0;
@@ -548,11 +565,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     if (CAUSAL) {
       const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
       if (lb + kBN > lim_lo) {
-        mask_tile(s, min(nv, lim - lb), hl);
+        mask_tile(s, 0, min(nv, lim - lb), hl);
         return;
       }
     }
-    mask_tile(s, nv, hl);
+    mask_tile(s, ts.lead(t), nv, hl);
   };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
   const RawPtrs rp = raw_ptrs(a.keys, h, tid);
@@ -560,10 +577,10 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   Stage5 st;
   StageR sr;
   if constexpr (RAW) {
-    loadR(sr, rp, a, tid, 0, 0, 0, 0);
+    loadR(sr, rp, a, tid, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
     loadR_table(sr, rp, a, tid);
   } else {
-    load5(st, tp, 0, 0, 0, 0);
+    load5(st, tp, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
   }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
@@ -677,12 +694,12 @@ __global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a, co
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * kBM + wave * 32 + l32;
-  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
   const int kbase = perm_row(l32) * kKSt + hl;
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
 
   TileRegs tr;
-  tile_load_k(tr, tp, 0, 0);
+  tile_load_k(tr, tp, ts.region(0), ts.base(0));
   bf16x8_t qf[8];
   {
     const uint16_t* qp = qbf + ((int64_t)h * a.Nq + min(qrow, a.Nq - 1)) * 128 + hl * 8;
@@ -707,7 +724,7 @@ __global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a, co
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]),
                                                          qf[ks], sc[kb], 0, 0, 0);
     }
-    mask_tile(sc, ts.valid(t), hl);
+    mask_tile(sc, ts.lead(t), ts.valid(t), hl);
     float mt = sc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -820,8 +837,8 @@ __global__ __launch_bounds__(256, 2) void score_cols_mfma_kernel(ScoreArgs a, co
 
 hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s) {
   const int mblocks = (a.Nq + kBM - 1) / kBM;
-  const int ntile0 = (a.keys.n[0] + kBN - 1) / kBN;
-  const int ntile1 = (a.keys.n[1] + kBN - 1) / kBN;
+  const int ntile0 = range_tiles(a.keys, 0);
+  const int ntile1 = range_tiles(a.keys, 1);
   ScoreArgs b = a;
   int n0 = ntile0, nt = ntile0 + ntile1;
   if (ntile0 == 0) {   // keep region 0 non-empty for the tile sequence
@@ -830,7 +847,9 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
     b.keys.v[0] = a.keys.v[1];
     b.keys.t[0] = a.keys.t[1];
     b.keys.cap[0] = a.keys.cap[1];
+    b.keys.lo[0] = a.keys.lo[1];
     b.keys.n[0] = a.keys.n[1];
+    b.keys.lo[1] = 0;
     b.keys.n[1] = 0;
     n0 = ntile1;
     nt = ntile1;
@@ -922,7 +941,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  const TileSeq ts{ntile0, ntiles, a.keys.n[0], a.keys.n[1]};
+  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
   const int last = ntiles - 1;
@@ -933,10 +952,10 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   Stage5 st;
   StageR sr;
   if constexpr (RAW) {
-    loadR(sr, rp, a, tid, 0, 0, 0, 0);
+    loadR(sr, rp, a, tid, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
     loadR_table(sr, rp, a, tid);
   } else {
-    load5(st, tp, 0, 0, 0, 0);
+    load5(st, tp, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
   }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
@@ -974,7 +993,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
       sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
     }
   }
-  mask_tile(sa, ts.valid(0), hl);
+  mask_tile(sa, ts.lead(0), ts.valid(0), hl);
   // tile 0 holds at least one valid key, so the reference is finite
   const float negm = -tile_max(sa, c2);
 
@@ -991,7 +1010,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     pmax = fmaxf(pmax, psum);
     lsum += psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
-    mask_tile(snext, ts.valid(min(t + 1, last)), hl);
+    mask_tile(snext, ts.lead(min(t + 1, last)), ts.valid(min(t + 1, last)), hl);
     if constexpr (RAW)
       storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     else
@@ -1017,8 +1036,8 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
-  const int ntile0 = (a.keys.n[0] + kBN - 1) / kBN;
-  const int ntile1 = (a.keys.n[1] + kBN - 1) / kBN;
+  const int ntile0 = range_tiles(a.keys, 0);
+  const int ntile1 = range_tiles(a.keys, 1);
   if (total == 0 || ntile0 + ntile1 == 0) return hipSuccess;
   AttendArgs b = a;
   int n0 = ntile0, nt = ntile0 + ntile1;
@@ -1031,7 +1050,9 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     b.keys.v[0] = a.keys.v[1];
     b.keys.t[0] = a.keys.t[1];
     b.keys.cap[0] = a.keys.cap[1];
+    b.keys.lo[0] = a.keys.lo[1];
     b.keys.n[0] = a.keys.n[1];
+    b.keys.lo[1] = 0;
     b.keys.n[1] = 0;
     n0 = ntile1;
     nt = ntile1;

@@ -110,7 +110,8 @@ struct KeyRegions {
   const void* v[2];
   const int32_t* t[2];                    // time index of every slot
   int32_t cap[2];
-  int32_t n[2];                           // valid slots (a prefix of each region)
+  int32_t lo[2];                          // visible slots of region r: [lo[r], n[r]) (lo is 0 unless
+  int32_t n[2];                           // attention is limited to the newest entries)
 };
 
 struct AttendArgs {

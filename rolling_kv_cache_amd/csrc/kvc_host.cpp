@@ -123,6 +123,7 @@ struct kvc_cache {
   bool poisoned;
   float mem_alpha[2];
   int32_t mem_frames;       // frames folded into the memories so far
+  int32_t max_keys;         // > 0: attention reads only the newest max_keys entries
 };
 
 namespace {
@@ -154,7 +155,7 @@ kvc_status device_result(kvc_handle h, hipError_t e, const char* what) {
 const kvc::RegionPtrs& cur_win(kvc_handle h) { return h->win[h->st.win_buf]; }
 
 kvc::KeyRegions key_regions(kvc_handle h) {
-  kvc::KeyRegions k;
+  kvc::KeyRegions k{};
   const kvc::RegionPtrs& w = cur_win(h);
   k.ka[0] = h->sink.ka;
   k.kb[0] = h->sink.kb;
@@ -296,6 +297,7 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->att_flags = (int32_t*)(h->ws + L.att_flags);
   h->keep_pinned = nullptr;
   h->keep_pending = false;
+  h->max_keys = 0;
   h->mem_alpha[0] = 0.9f;
   h->mem_alpha[1] = 0.5f;
   h->mem_frames = 0;
@@ -417,7 +419,51 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
   a.causal_block = causal_block;
   a.raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
   a.mem_lo = INT32_MAX;
-  if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0) {
+  const int32_t n_valid = h->st.n_valid();
+  if (h->max_keys > 0 && h->max_keys < n_valid) {
+    // only the newest max_keys entries in logical order: at most two physical ranges (a window suffix
+    // that wraps, or a sink tail plus the whole window) when the sink ring has not rolled
+    if (causal_block > 0) return fail(KVC_EUNSUPPORTED, "block-causal attention with an attention limit");
+    if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0)
+      return fail(KVC_EUNSUPPORTED, "memory tokens with an attention limit");
+    // per region: the whole valid prefix when all of it is visible (key order does not matter),
+    // else the physical ranges of its visible logical suffix
+    const int32_t lo = n_valid - h->max_keys, ns = h->st.ns;
+    std::vector<kvc::Range> rs;
+    if (lo < ns) {
+      if (lo == 0)
+        rs.push_back({kvc::kSink, 0, ns});
+      else
+        for (const kvc::Range& r : h->st.ranges(lo, ns)) rs.push_back(r);
+    }
+    if (n_valid > std::max(lo, ns)) {
+      if (lo <= ns)
+        rs.push_back({kvc::kWin, 0, h->st.nw});
+      else
+        for (const kvc::Range& r : h->st.ranges(lo, n_valid)) rs.push_back(r);
+    }
+    if (rs.size() > 2) return fail(KVC_EUNSUPPORTED, "attention limit over a rolled sink");
+    kvc::KeyRegions k{};
+    for (size_t i = 0; i < rs.size(); ++i) {
+      const kvc::RegionPtrs& R = rs[i].region == kvc::kSink ? h->sink : cur_win(h);
+      k.ka[i] = R.ka;
+      k.kb[i] = R.kb;
+      k.v[i] = R.v;
+      k.t[i] = R.t;
+      k.cap[i] = R.cap;
+      k.lo[i] = rs[i].lo;
+      k.n[i] = rs[i].lo + rs[i].n;
+    }
+    if (rs.size() == 1) {             // an empty second range over the same buffer
+      k.ka[1] = k.ka[0];
+      k.kb[1] = k.kb[0];
+      k.v[1] = k.v[0];
+      k.t[1] = k.t[0];
+      k.cap[1] = k.cap[0];
+    }
+    a.keys = k;
+  }
+  if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0 && !(h->max_keys > 0 && h->max_keys < n_valid)) {
     // the memories sit right before the oldest window entry: long at t_w - 2, short at t_w - 1
     if (causal_block > 0) return fail(KVC_EUNSUPPORTED, "block-causal attention with memory tokens");
     const int32_t t_w = h->st.t_at(kvc::kWin, h->st.hw);
@@ -570,6 +616,13 @@ kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, flo
   a.geo = h->geo;
   hipError_t e = kvc::launch_relax(a, h->stream);
   return device_result(h, e, "relax scores");
+}
+
+kvc_status kvc_set_attention_limit(kvc_handle h, int32_t max_keys) {
+  if (kvc_status s = check(h)) return s;
+  if (max_keys < 0) return fail(KVC_EINVAL, "max_keys must be >= 0");
+  h->max_keys = max_keys;
+  return KVC_OK;
 }
 
 kvc_status kvc_set_memory_rates(kvc_handle h, float alpha_long, float alpha_short) {

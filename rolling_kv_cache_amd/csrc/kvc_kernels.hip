@@ -595,7 +595,7 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
   for (int r = 0; r < 2; ++r) {
     const T* vbase = (const T*)a.keys.v[r];
     const int nr = min(a.keys.n[r], lim - (r == 0 ? 0 : a.keys.n[0]));
-    for (int j = 0; j < nr; ++j) {
+    for (int j = a.keys.lo[r]; j < nr; ++j) {
       int tr = INT32_MIN;
       if (a.raw) tr = (r == 0 && j >= a.mem_lo) ? a.mem_t[j - a.mem_lo >= g.S ? 1 : 0] : a.keys.t[r][j];
       const float s = key_dot<T, D>(qv, a.keys, r, h, j, g, a.tab, tr) * a.scale;

@@ -487,3 +487,74 @@ def test_memory_tokens_errors():
         with pytest.raises(KVCError) as e:
             call()
         assert e.value.code == 5
+
+
+# ---------------------------------------------------------------- attention limited to the newest entries
+@pytest.mark.parametrize("general,raw", [(False, False), (True, False), (False, True)])
+def test_attention_limit(general, raw):
+    """After every chunk of the ragged sink/window workload, attention over the newest m entries for m = all,
+    one chunk, a window suffix that wraps the ring, and the sink's last 37 entries plus the whole window
+    (ranges that start inside a 64-slot tile)."""
+    w = _replace(SMALL_SW, name="lim", raw_keys=raw)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                     raw_keys=raw)
+    S = w.frame_seqlen
+    for i in range(w.n_chunks):
+        q, k, v = chunk_inputs(w, i)
+        t0 = w.chunk_start_frame(i)
+        F = w.chunk_frames[i]
+        gc.append(dev(k, w), dev(v, w), t0)
+        oc.append(k, v, F, t0)
+        n = oc.n
+        nw = n - oc.n_sink
+        for m in sorted({n, F * S, max(1, nw - 37), min(n, nw + 37), 1}):
+            gc.set_attention_limit(m)
+            if general:
+                os.environ["KVC_ATTEND_GENERAL"] = "1"
+            try:
+                out = gc.attend(dev(q, w), t0).float().cpu().numpy()
+            finally:
+                os.environ.pop("KVC_ATTEND_GENERAL", None)
+            check_attention(out, oc.attend(q, F, t0, max_keys=m), f"chunk {i} limit {m}")
+        gc.set_attention_limit(0)
+
+
+def test_attention_limit_refusals():
+    from rolling_kv_cache_amd import KVCError
+    w = SMALL_SW
+    gc = new_cache(w)
+    with pytest.raises(KVCError) as e:
+        gc.set_attention_limit(-1)
+    assert e.value.code == 1
+    for i in range(4):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), w.chunk_start_frame(i))
+    gc.set_attention_limit(100)
+    (q,) = chunk_inputs(w, 95, tensors=(0,), frames=2)
+    with pytest.raises(KVCError) as e:
+        gc.attend_block_causal(dev(q, w), 0, 1)
+    assert e.value.code == 5
+    # a Rolling-Sink sink that has rolled: the visible tail of the sink is two slot ranges plus the window
+    base = WORKLOADS["c4"]
+    rw = Workload("c4_lim", 220, 2, 128, "bf16", 4, 8, 3, 2, (1,) * 8, bank_frames=4)
+    rc = new_cache(rw)
+    for i in range(6):
+        _, k, v = chunk_inputs(rw, i)
+        rc.append(dev(k, rw), dev(v, rw), i)
+    rc.sink_push(0, 1, 6)
+    n = rc.info()["n_valid"]
+    rc.set_attention_limit(n - 5)
+    (q,) = chunk_inputs(rw, 94, tensors=(0,), frames=1)
+    with pytest.raises(KVCError) as e:
+        rc.attend(dev(q, rw), 7)
+    assert e.value.code == 5
+    m = new_cache(_replace(MEM_SMALL, name="mem_lim"))
+    for i in range(4):
+        _, k, v = chunk_inputs(w, i, frames=3)
+        m.append(dev(k, w), dev(v, w), 3 * i)
+    m.set_attention_limit(50)
+    (q,) = chunk_inputs(w, 93, tensors=(0,), frames=1)
+    with pytest.raises(KVCError) as e:
+        m.attend(dev(q, w), 12)
+    assert e.value.code == 5
