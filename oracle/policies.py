@@ -211,6 +211,25 @@ class RelaxForcingRun:
         return c.attend(q, F, t0, rows=rows, f64=f64)
 
 
+class DenoiseLoopRun:
+    """Chunk-wise denoising over a cache per layer (Causal-Forcing article, section 4, block-wise denoising;
+    LingBot-World 2.0 article: after each block's sampling steps a clean pass at t = 0 writes the block's
+    KV).  Per chunk and layer: step 0 writes the chunk's frames (rolling the window), steps 1..steps-1 and
+    the commit pass re-write the same frames in place (no new content, no roll), and every pass attends.
+    The plain sliding-window schedule; the chunk is written at its absolute start frame."""
+
+    def __init__(self, w, layers, steps=4):
+        self.w, self.L, self.steps = w, layers, steps
+        self.caches = [_cache_for(w) for _ in range(layers)]
+
+    def step(self, i, layer, s, q, k, v, rows=None, f64=False):
+        c = self.caches[layer]
+        F = self.w.chunk_frames[i]
+        t0 = self.w.chunk_start_frame(i)
+        c.append(k, v, F, t0, replace_newest=s > 0)
+        return c.attend(q, F, t0, rows=rows, f64=f64)
+
+
 def make_run(w):
     """Run of a workload by name prefix; anything else is a plain sliding window / global cache."""
     return {"c4": RollingSinkRun, "c5a": InfinityRopeRun, "c5b": DeepForcingRun, "c5c": RelaxForcingRun}.get(

@@ -261,3 +261,28 @@ def test_deep_forcing_keep_set_and_gap_closing():
             assert c.t[:3 * S].max() == comp_t.min() - 1
         assert c.n <= c.C_tok
     assert compactions == 3        # chunks 7, 11, 15
+
+
+# ---------------------------------------------------------------- denoise loop over layers
+def test_denoise_loop_state_equals_commit_only_run():
+    """After each chunk's four sampling passes and the commit, a layer's cache equals a plain sliding-window
+    cache that received only the commit passes (the re-writes leave no trace but the last one), and the
+    layers stay independent."""
+    from oracle import DenoiseLoopRun
+    from workloads import denoise_inputs
+    w = Workload("dn_small", 107, 2, 64, "bf16", 2, 3, 1, 4, (1, 2, 2, 2, 1, 2))
+    run = DenoiseLoopRun(w, layers=2)
+    plain = [OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+             for _ in range(2)]
+    for i in range(w.n_chunks):
+        for s in range(5):
+            for layer in range(2):
+                q, k, v = denoise_inputs(w, i, s, layer)
+                run.step(i, layer, s, q, k, v)
+        for layer in range(2):
+            _, k, v = denoise_inputs(w, i, 4, layer)
+            plain[layer].append(k, v, w.chunk_frames[i], w.chunk_start_frame(i))
+            a, b = run.caches[layer], plain[layer]
+            for name in ("K", "V", "t", "g"):
+                assert np.array_equal(getattr(a, name), getattr(b, name)), (i, layer, name)
+    assert not np.array_equal(run.caches[0].K, run.caches[1].K)

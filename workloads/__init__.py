@@ -126,3 +126,14 @@ def small_variant(w: Workload, heads: int | None = None, grid=None, n_chunks: in
     return Workload(w.name + "_small", w.cfg_id + 100, heads or w.heads, w.head_dim, w.dtype,
                     gh, gw, w.sink_frames, w.window_frames, tuple(cf), w.bank_frames,
                     tuple(c for c in w.cut_chunks if c < len(cf)), w.raw_keys, w.memory)
+
+
+DENOISE_STEPS = 4        # the 4-step distilled models' timesteps, then one commit pass at t = 0
+
+
+def denoise_inputs(w: Workload, chunk: int, step: int, layer: int = 0, frames=None):
+    """q/k/v of one denoising step (0..DENOISE_STEPS-1, then DENOISE_STEPS = the clean commit pass) of one
+    layer for chunk `chunk`: a seeded stream of its own per (layer, chunk, step)."""
+    n = (w.chunk_frames[chunk] if frames is None else frames) * w.frame_seqlen
+    sub = 1_000_000 + (layer * 10_000 + chunk) * 8 + step
+    return tuple(gen(w.cfg_id, sub, tid, n, w.heads, w.head_dim, w.dtype) for tid in (TENSOR_Q, TENSOR_K, TENSOR_V))
