@@ -136,6 +136,23 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
                       int32_t bank_frames, uint32_t create_flags, void* workspace, size_t ws_bytes,
                       void* hip_stream, kvc_handle* out);
 
+/* Layer groups: one cache per transformer layer, all over one workspace of
+ * n_layers identical per-layer layouts (layer l at workspace + l *
+ * kvc_workspace_bytes(...)), so that the cache operations every layer makes
+ * alike between chunks -- retime, compact, sink push -- run as ONE launch over
+ * the layers (the *_layers calls below).  Appends and attends stay per layer
+ * (a layer's keys and queries exist only inside its own forward pass).
+ * kvc_create_group fills out[0 .. n_layers-1] with handles made as by
+ * kvc_create (same arguments for every layer, same stream); on failure none
+ * is left created.  Each handle is destroyed with kvc_destroy. */
+size_t kvc_group_workspace_bytes(int32_t n_layers, int32_t sink_frames, int32_t window_frames,
+                                 int32_t frame_seqlen, int32_t heads, int32_t head_dim, kvc_dtype dt,
+                                 int32_t bank_frames, uint32_t create_flags);
+kvc_status kvc_create_group(int32_t n_layers, int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,
+                            int32_t heads, int32_t head_dim, int32_t grid_w, kvc_dtype dt, int32_t bank_frames,
+                            uint32_t create_flags, void* workspace, size_t ws_bytes, void* hip_stream,
+                            kvc_handle* out);
+
 /* Free host state; the workspace stays the caller's. */
 kvc_status kvc_destroy(kvc_handle h);
 
@@ -185,6 +202,18 @@ kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames,
  * window oldest..newest.  EINVAL if the range is outside [0, n_valid) or a
  * resulting |time| exceeds KVC_MAX_POS. */
 kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi);
+
+/* kvc_retime / kvc_compact / kvc_sink_push over n_layers layers in one launch:
+ * layers[0 .. n_layers-1] must be consecutive members of one kvc_create_group
+ * group (layer index increasing by one), on the same stream and in the same
+ * cache state (as they are when every layer received the same calls); EINVAL
+ * otherwise, ESTATE if the states differ.  The result on every layer is what
+ * the single-layer call would give.  A HIP failure poisons all of them. */
+kvc_status kvc_retime_layers(const kvc_handle* layers, int32_t n_layers, int32_t delta, int32_t clamp0,
+                             int32_t slot_lo, int32_t slot_hi);
+kvc_status kvc_compact_layers(const kvc_handle* layers, int32_t n_layers, const int32_t* keep_idx, int32_t n_keep);
+kvc_status kvc_sink_push_layers(const kvc_handle* layers, int32_t n_layers, int32_t bank_frame, int32_t n_frames,
+                                int32_t t_index);
 
 /* Device scratch bytes kvc_score needs for q_frames query frames. */
 size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);

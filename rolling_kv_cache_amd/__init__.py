@@ -30,7 +30,8 @@ KVC_MAX_Q_FRAMES = 32
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
             "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
             "kvc_relax_scores", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
-            "kvc_compact", "kvc_sink_push",
+            "kvc_compact", "kvc_sink_push", "kvc_group_workspace_bytes", "kvc_create_group", "kvc_retime_layers",
+            "kvc_compact_layers", "kvc_sink_push_layers",
             "kvc_info",
             "kvc_slot_times", "kvc_export", "kvc_export_tables", "kvc_last_error")
 
@@ -61,6 +62,12 @@ def _load():
         "kvc_create": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32, u32, vp, sz, vp,
                                       ctypes.POINTER(vp)]),
         "kvc_destroy": (ctypes.c_int, [vp]),
+        "kvc_group_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32, u32]),
+        "kvc_create_group": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, i32, u32, vp, sz, vp,
+                                            ctypes.POINTER(vp)]),
+        "kvc_retime_layers": (ctypes.c_int, [ctypes.POINTER(vp), i32, i32, i32, i32, i32]),
+        "kvc_compact_layers": (ctypes.c_int, [ctypes.POINTER(vp), i32, p32, i32]),
+        "kvc_sink_push_layers": (ctypes.c_int, [ctypes.POINTER(vp), i32, i32, i32, i32]),
         "kvc_set_stream": (ctypes.c_int, [vp, vp]),
         "kvc_append": (ctypes.c_int, [vp, vp, vp, i32, i32, u32]),
         "kvc_attend": (ctypes.c_int, [vp, vp, i32, i32, vp]),
@@ -120,11 +127,20 @@ class KVCache:
 
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
                  dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False,
-                 memory=None):
+                 memory=None, _handle=None, _workspace=None):
         """memory: (alpha_long, alpha_short) for MemRoPE memory tokens on a raw-key cache, or None."""
         self.S, self.H, self.D = frame_seqlen, heads, head_dim
         self.dtype = dtype
         self.device = torch.device(device)
+        if _handle is not None:                 # a member of a layer group (create_group)
+            self._ws_raw = _workspace
+            self._stream = stream
+            self._h = _handle
+            if memory is not None:
+                _check(lib.kvc_set_memory_rates(self._h, float(memory[0]), float(memory[1])))
+            self._score_scratch = None
+            self._relax_scratch = None
+            return
         nbytes = workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype, bank_frames,
                                  compact, raw_keys, memory is not None)
         if nbytes == 0:
@@ -291,4 +307,50 @@ class KVCache:
         return out
 
 
-__all__ = ["KVCache", "KVCError", "lib", "workspace_bytes", "EXPORTED", "LIB_PATH"]
+def create_group(n_layers, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
+                 dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False,
+                 memory=None):
+    """n_layers caches over one workspace (kvc_create_group): per-layer append/attend as usual, and the
+    layer-uniform operations batched with retime_layers / compact_layers / sink_push_layers."""
+    device = torch.device(device)
+    flags = _create_flags(compact, raw_keys, memory is not None)
+    nbytes = int(lib.kvc_group_workspace_bytes(n_layers, sink_frames, window_frames, frame_seqlen, heads, head_dim,
+                                               _dt(dtype), bank_frames, flags))
+    if nbytes == 0:
+        raise KVCError(KVC_EINVAL, "unsupported geometry")
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    stream = stream if stream is not None else torch.cuda.current_stream(device)
+    hs = (ctypes.c_void_p * n_layers)()
+    _check(lib.kvc_create_group(n_layers, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
+                                _dt(dtype), bank_frames, flags, ctypes.c_void_p(raw.data_ptr() + off), nbytes,
+                                ctypes.c_void_p(stream.cuda_stream), hs))
+    return [KVCache(sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w, dtype, bank_frames, compact,
+                    device, stream, raw_keys, memory, _handle=ctypes.c_void_p(hs[i]), _workspace=raw)
+            for i in range(n_layers)]
+
+
+def _handles(caches):
+    arr = (ctypes.c_void_p * len(caches))()
+    for i, c in enumerate(caches):
+        arr[i] = c._h.value if isinstance(c._h, ctypes.c_void_p) else c._h
+    return arr
+
+
+def retime_layers(caches, delta: int, clamp0: bool = False, lo: int = 0, hi=None):
+    hi = caches[0].info()["n_valid"] if hi is None else hi
+    _check(lib.kvc_retime_layers(_handles(caches), len(caches), int(delta), 1 if clamp0 else 0, int(lo), int(hi)))
+
+
+def compact_layers(caches, keep_idx):
+    keep = np.ascontiguousarray(np.asarray(keep_idx, dtype=np.int32))
+    _check(lib.kvc_compact_layers(_handles(caches), len(caches), keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  int(keep.shape[0])))
+
+
+def sink_push_layers(caches, bank_frame: int, n_frames: int, t_index: int):
+    _check(lib.kvc_sink_push_layers(_handles(caches), len(caches), int(bank_frame), int(n_frames), int(t_index)))
+
+
+__all__ = ["KVCache", "KVCError", "lib", "workspace_bytes", "EXPORTED", "LIB_PATH", "create_group", "retime_layers",
+           "compact_layers", "sink_push_layers"]

@@ -82,6 +82,16 @@ __device__ __forceinline__ void rotate_run(float* x, const Geo& g, const Tables&
   }
 }
 
+// The same region in the workspace `off` bytes further on (layer batching).
+__device__ __forceinline__ RegionPtrs layer_region(RegionPtrs r, int64_t off) {
+  r.ka = (char*)r.ka + off;
+  r.kb = (char*)r.kb + off;
+  r.v = (char*)r.v + off;
+  r.t = (int32_t*)((char*)r.t + off);
+  r.g = (int64_t*)((char*)r.g + off);
+  return r;
+}
+
 // Index of the V element (head h, slot j, dim d) in the tile-transposed layout.
 __device__ __forceinline__ size_t v_index(int h, int cap, int D, int j, int d) {
   return (((size_t)h * (cap / kTile) + (j / kTile)) * D + d) * kTile + (j % kTile);

@@ -52,7 +52,13 @@ struct SegW {
   int32_t kb0, vb0;    // first K-part / V-part block of this segment
 };
 
+// Layer batching: a launch with gridDim.y = L works on L caches whose
+// workspaces sit layer_stride bytes apart (identical layouts); every pointer
+// into a workspace is layer 0's, offset by blockIdx.y * layer_stride.
 struct AppendArgs {
+  int32_t layers;                         // gridDim.y (0 or 1: one layer)
+  int64_t layer_stride;                   // bytes between the layers' workspaces (0: one layer)
+  int64_t src_stride;                     // bytes between the layers' sources (the bank: layer_stride)
   int32_t time_raw;                       // raw-key cache: the time band is stored un-rotated
   const void* k;
   const void* v;
@@ -77,6 +83,8 @@ struct RangeW {
 };
 
 struct RetimeArgs {
+  int32_t layers;
+  int64_t layer_stride;
   RegionPtrs reg[2];
   RangeW rng[4];
   int32_t nrng;
@@ -87,6 +95,8 @@ struct RetimeArgs {
 };
 
 struct CompactArgs {
+  int32_t layers;
+  int64_t layer_stride;
   RegionPtrs src, dst;
   const int32_t* idx;                     // source slot of each destination slot
   int32_t n;

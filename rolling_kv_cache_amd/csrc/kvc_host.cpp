@@ -124,6 +124,9 @@ struct kvc_cache {
   float mem_alpha[2];
   int32_t mem_frames;       // frames folded into the memories so far
   int32_t max_keys;         // > 0: attention reads only the newest max_keys entries
+  const void* group;        // layer group (kvc_create_group): shared tag, layer index, stride
+  int32_t layer;
+  int64_t layer_stride;
 };
 
 namespace {
@@ -175,9 +178,13 @@ kvc::KeyRegions key_regions(kvc_handle h) {
 // Launch the append kernel over a list of segments (in batches of kMaxSegs).
 hipError_t launch_segments(kvc_handle h, const std::vector<kvc::Seg>& segs, const void* k, const void* v,
                            int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head, int32_t t0, int64_t g0,
-                           int32_t bank_lo, int32_t bank_hi) {
+                           int32_t bank_lo, int32_t bank_hi, int32_t layers = 1, int64_t layer_stride = 0,
+                           int64_t src_stride = 0) {
   for (size_t b = 0; b < segs.size(); b += kvc::kMaxSegs) {
     kvc::AppendArgs a{};
+    a.layers = layers;
+    a.layer_stride = layer_stride;
+    a.src_stride = src_stride;
     a.time_raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
     a.k = k;
     a.v = v;
@@ -242,6 +249,33 @@ void build_tables(int32_t D, int32_t S, int32_t grid_w, std::vector<float>* tt, 
     }
 }
 
+bool same_ring(const kvc::RingState& a, const kvc::RingState& b) {
+  return a.ns == b.ns && a.hs == b.hs && a.nw == b.nw && a.hw == b.hw && a.win_buf == b.win_buf &&
+         a.global_end == b.global_end && a.newest_valid == b.newest_valid && a.newest_frames == b.newest_frames &&
+         a.t_sink == b.t_sink && a.t_win == b.t_win && a.g_sink == b.g_sink && a.g_win == b.g_win;
+}
+
+// A batched call takes consecutive layers of one group, all in the same state and on the same stream; a
+// single-layer call is the set {h}.
+kvc_status check_layers(const kvc_handle* hs, int32_t n) {
+  if (!hs || n < 1) return fail(KVC_EINVAL, "empty layer set");
+  for (int32_t i = 0; i < n; ++i)
+    if (kvc_status s = check(hs[i])) return s;
+  for (int32_t i = 1; i < n; ++i) {
+    if (!hs[0]->group || hs[i]->group != hs[0]->group || hs[i]->layer != hs[0]->layer + i)
+      return fail(KVC_EINVAL, "layers must be consecutive members of one kvc_create_group group");
+    if (hs[i]->stream != hs[0]->stream) return fail(KVC_EINVAL, "layers must share a stream");
+    if (!same_ring(hs[i]->st, hs[0]->st)) return fail(KVC_ESTATE, "layers are not in the same cache state");
+  }
+  return KVC_OK;
+}
+
+kvc_status device_result_layers(const kvc_handle* hs, int32_t n, hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVC_OK;
+  for (int32_t i = 0; i < n; ++i) hs[i]->poisoned = true;
+  return fail(KVC_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,6 +332,9 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->keep_pinned = nullptr;
   h->keep_pending = false;
   h->max_keys = 0;
+  h->group = nullptr;
+  h->layer = 0;
+  h->layer_stride = 0;
   h->mem_alpha[0] = 0.9f;
   h->mem_alpha[1] = 0.5f;
   h->mem_frames = 0;
@@ -331,6 +368,43 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
     return fail(KVC_EDEVICE, std::string("create: ") + hipGetErrorString(e));
   }
   *out = h;
+  return KVC_OK;
+}
+
+size_t kvc_group_workspace_bytes(int32_t n_layers, int32_t sink_frames, int32_t window_frames,
+                                 int32_t frame_seqlen, int32_t heads, int32_t head_dim, kvc_dtype dt,
+                                 int32_t bank_frames, uint32_t create_flags) {
+  if (n_layers < 1) return 0;
+  const size_t one = kvc_workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames,
+                                         create_flags);
+  return one * (size_t)n_layers;
+}
+
+kvc_status kvc_create_group(int32_t n_layers, int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,
+                            int32_t heads, int32_t head_dim, int32_t grid_w, kvc_dtype dt, int32_t bank_frames,
+                            uint32_t create_flags, void* workspace, size_t ws_bytes, void* hip_stream,
+                            kvc_handle* out) {
+  if (!out || n_layers < 1) return fail(KVC_EINVAL, "out is null or n_layers < 1");
+  const size_t one = kvc_workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames,
+                                         create_flags);
+  if (one == 0) return fail(KVC_EINVAL, "unsupported geometry");
+  if (ws_bytes < one * (size_t)n_layers) return fail(KVC_ENOMEM, "workspace smaller than kvc_group_workspace_bytes()");
+  for (int32_t l = 0; l < n_layers; ++l) out[l] = nullptr;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    kvc_status s = kvc_create(sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w, dt, bank_frames,
+                              create_flags, (char*)workspace + one * l, one, hip_stream, &out[l]);
+    if (s != KVC_OK) {
+      const std::string msg = g_err;
+      for (int32_t j = 0; j < l; ++j) {
+        kvc_destroy(out[j]);
+        out[j] = nullptr;
+      }
+      return fail(s, msg);
+    }
+    out[l]->group = workspace;
+    out[l]->layer = l;
+    out[l]->layer_stride = (int64_t)one;
+  }
   return KVC_OK;
 }
 
@@ -493,13 +567,17 @@ kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames,
   return attend_impl(h, q, q_frames, q_t_index, out, block_frames * h->S);
 }
 
-kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi) {
-  if (kvc_status s = check(h)) return s;
+static kvc_status retime_layers(const kvc_handle* hs, int32_t nl, int32_t delta, int32_t clamp0, int32_t slot_lo,
+                                int32_t slot_hi) {
+  if (kvc_status s = check_layers(hs, nl)) return s;
+  kvc_handle h = hs[0];
   kvc::RingState nx = h->st;
   std::vector<kvc::Range> rs;
   std::string err;
   if (!kvc::plan_retime(nx, delta, clamp0 != 0, slot_lo, slot_hi, &rs, &err)) return fail(KVC_EINVAL, err);
   kvc::RetimeArgs a{};
+  a.layers = nl;
+  a.layer_stride = h->layer_stride;
   a.reg[0] = h->sink;
   a.reg[1] = cur_win(h);
   int32_t blocks = 0;
@@ -517,9 +595,18 @@ kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_
   a.geo = h->geo;
   a.tab = h->tab;
   hipError_t e = kvc::launch_retime(a, blocks, h->stream);
-  if (kvc_status s = device_result(h, e, "retime")) return s;
-  h->st = std::move(nx);
+  if (kvc_status s = device_result_layers(hs, nl, e, "retime")) return s;
+  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
   return KVC_OK;
+}
+
+kvc_status kvc_retime(kvc_handle h, int32_t delta, int32_t clamp0, int32_t slot_lo, int32_t slot_hi) {
+  return retime_layers(&h, 1, delta, clamp0, slot_lo, slot_hi);
+}
+
+kvc_status kvc_retime_layers(const kvc_handle* layers, int32_t n_layers, int32_t delta, int32_t clamp0,
+                             int32_t slot_lo, int32_t slot_hi) {
+  return retime_layers(layers, n_layers, delta, clamp0, slot_lo, slot_hi);
 }
 
 size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames) {
@@ -652,8 +739,9 @@ kvc_status kvc_export_memory(kvc_handle h, void* k, void* v, int32_t* n_folded) 
   return KVC_OK;
 }
 
-kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
-  if (kvc_status s = check(h)) return s;
+static kvc_status compact_layers(const kvc_handle* hs, int32_t nl, const int32_t* keep_idx, int32_t n_keep) {
+  if (kvc_status s = check_layers(hs, nl)) return s;
+  kvc_handle h = hs[0];
   if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "compact is not available with memory tokens");
   if (!(h->cflags & KVC_CREATE_COMPACT)) return fail(KVC_EUNSUPPORTED, "compact needs KVC_CREATE_COMPACT");
   kvc::RingState nx = h->st;
@@ -662,6 +750,7 @@ kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
   if (!kvc::plan_compact(nx, keep_idx, n_keep, &src, &err)) return fail(KVC_EINVAL, err);
   hipError_t e = hipSuccess;
   if (!src.empty()) {
+    // the source slots go up once, into the first layer's workspace, and serve every layer
     if (h->keep_pending) {
       e = hipEventSynchronize(h->keep_evt);
       h->keep_pending = false;
@@ -676,6 +765,8 @@ kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
     }
     if (e == hipSuccess) {
       kvc::CompactArgs a{};
+      a.layers = nl;
+      a.layer_stride = h->layer_stride;
       a.src = h->win[h->st.win_buf];
       a.dst = h->win[h->st.win_buf ^ 1];
       a.idx = h->keep_dev;
@@ -684,13 +775,23 @@ kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
       e = kvc::launch_compact(a, h->stream);
     }
   }
-  if (kvc_status s = device_result(h, e, "compact")) return s;
-  h->st = std::move(nx);
+  if (kvc_status s = device_result_layers(hs, nl, e, "compact")) return s;
+  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
   return KVC_OK;
 }
 
-kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int32_t t_index) {
-  if (kvc_status s = check(h)) return s;
+kvc_status kvc_compact(kvc_handle h, const int32_t* keep_idx, int32_t n_keep) {
+  return compact_layers(&h, 1, keep_idx, n_keep);
+}
+
+kvc_status kvc_compact_layers(const kvc_handle* layers, int32_t n_layers, const int32_t* keep_idx, int32_t n_keep) {
+  return compact_layers(layers, n_layers, keep_idx, n_keep);
+}
+
+static kvc_status sink_push_layers(const kvc_handle* hs, int32_t nl, int32_t bank_frame, int32_t n_frames,
+                                   int32_t t_index) {
+  if (kvc_status s = check_layers(hs, nl)) return s;
+  kvc_handle h = hs[0];
   if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "sink push is not available with memory tokens");
   if (h->L.bank_tok == 0) return fail(KVC_ESTATE, "no bank (bank_frames was 0)");
   if (h->st.global_end < h->L.bank_tok) return fail(KVC_ESTATE, "bank not complete yet");
@@ -706,10 +807,21 @@ kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int
   const char* bk = (const char*)h->bank_k + (size_t)b0 * D * h->geo.esz;
   const char* bv = (const char*)h->bank_v + (size_t)b0 * D * h->geo.esz;
   const int64_t head = (int64_t)h->L.bank_tok * D;
-  hipError_t e = launch_segments(h, segs, bk, bv, D, head, D, head, t_index, b0, 0, 0);
-  if (kvc_status s = device_result(h, e, "sink_push")) return s;
-  h->st = std::move(nx);
+  // the bank is in each layer's workspace: sources move with the layer too
+  hipError_t e = launch_segments(h, segs, bk, bv, D, head, D, head, t_index, b0, 0, 0, nl, h->layer_stride,
+                                 h->layer_stride);
+  if (kvc_status s = device_result_layers(hs, nl, e, "sink_push")) return s;
+  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
   return KVC_OK;
+}
+
+kvc_status kvc_sink_push(kvc_handle h, int32_t bank_frame, int32_t n_frames, int32_t t_index) {
+  return sink_push_layers(&h, 1, bank_frame, n_frames, t_index);
+}
+
+kvc_status kvc_sink_push_layers(const kvc_handle* layers, int32_t n_layers, int32_t bank_frame, int32_t n_frames,
+                                int32_t t_index) {
+  return sink_push_layers(layers, n_layers, bank_frame, n_frames, t_index);
 }
 
 kvc_status kvc_info(kvc_handle h, kvc_info_t* out) {

@@ -85,6 +85,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const Geo& g = a.geo;
   const int tid = threadIdx.x;
   int b = blockIdx.x;
+  if (blockIdx.y > 0) {
+    const int64_t off = (int64_t)blockIdx.y * a.layer_stride, soff = (int64_t)blockIdx.y * a.src_stride;
+    a.reg[0] = layer_region(a.reg[0], off);
+    a.reg[1] = layer_region(a.reg[1], off);
+    a.bank_k = (char*)a.bank_k + off;
+    a.bank_v = (char*)a.bank_v + off;
+    a.k = (const char*)a.k + soff;
+    a.v = (const char*)a.v + soff;
+  }
   if (b < a.nkb) {
     const SegW sg = pick_seg_k<T>(a, b);
     const RegionPtrs R = sg.region == 0 ? a.reg[0] : a.reg[1];
@@ -228,7 +237,8 @@ static hipError_t append_launch(AppendArgs a, hipStream_t s) {
   append_blocks<T, D>(a);
   const int blocks = a.nkb + a.nvb;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks), dim3(256), 0, s, a);
+  const unsigned layers = a.layers > 1 ? (unsigned)a.layers : 1u;
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks, layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -267,7 +277,7 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
     if (i < a.nrng && b >= a.rng[i].blk0) rg = a.rng[i];
   const int s0 = rg.lo + (b - rg.blk0) * 32;
   const int ns = min(32, rg.lo + rg.n - s0);
-  const RegionPtrs R = rg.region == 0 ? a.reg[0] : a.reg[1];
+  const RegionPtrs R = layer_region(rg.region == 0 ? a.reg[0] : a.reg[1], (int64_t)blockIdx.y * a.layer_stride);
   __shared__ int s_dl[32];
   __shared__ int s_tn[32];
   const int tid = threadIdx.x;
@@ -317,34 +327,35 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
 
 hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
+  const dim3 grid(nblocks, a.layers > 1 ? (unsigned)a.layers : 1u);
   if (a.geo.esz == 2) {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), dim3(nblocks), dim3(RetimeShape<uint16_t, 128>::THREADS), 0,
-                         s, a);
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), grid, dim3(RetimeShape<uint16_t, 128>::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), dim3(nblocks), dim3(RetimeShape<uint16_t, 64>::THREADS), 0, s,
-                         a);
+      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), grid, dim3(RetimeShape<uint16_t, 64>::THREADS), 0, s, a);
   } else {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<float, 128>), dim3(nblocks), dim3(RetimeShape<float, 128>::THREADS), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<float, 128>), grid, dim3(RetimeShape<float, 128>::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((retime_kernel<float, 64>), dim3(nblocks), dim3(RetimeShape<float, 64>::THREADS), 0, s, a);
+      hipLaunchKernelGGL((retime_kernel<float, 64>), grid, dim3(RetimeShape<float, 64>::THREADS), 0, s, a);
   }
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
 // compact: destination slot j <- source slot idx[j] (the two window buffers;
-// idx sorted and unique).  Two block kinds in one launch:
+// idx unique, increasing except once where the kept logical entries cross the
+// window ring's wrap).  Two block kinds in one launch:
 //  * key blocks: KS destination slots x all heads; thread (slot, chunk) copies
 //    that 16-byte chunk of the slot's key row for every head (eight heads in
 //    flight) and, for chunk 0, the slot's t and g;
 //  * value blocks: one destination V^T tile (64 slots) of one head.  A slot's
 //    value is a column of a V^T tile (one element per 128-byte row), so the
 //    block brings whole source tiles into LDS -- only those holding kept
-//    entries, in order -- gathers the columns there, and writes the
-//    destination tile as full rows.  Since idx is sorted, each source tile is
-//    read by at most two destination tiles.
+//    entries, once per run of consecutive entries in the same tile -- gathers
+//    the columns there, and writes the destination tile as full rows.  A
+//    source tile is read by a few destination tiles at most (two, plus one
+//    more at the ring's wrap).
 template <typename T, int D>
 struct CompactShape {
   static constexpr int E = Elem<T>::E;
@@ -357,6 +368,10 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   using Sh = CompactShape<T, D>;
   constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, HU = 8;
   const Geo& g = a.geo;
+  if (blockIdx.y > 0) {
+    a.src = layer_region(a.src, (int64_t)blockIdx.y * a.layer_stride);
+    a.dst = layer_region(a.dst, (int64_t)blockIdx.y * a.layer_stride);
+  }
   const int tid = threadIdx.x;
   int b = blockIdx.x;
   if (b < a.nk) {
@@ -410,10 +425,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   const T* vsrc = (const T*)a.src.v + (size_t)h * (a.src.cap / kTile) * TE;
   T* sdst = (T*)s_dst;
   const T* ssrc = (const T*)s_src;
-  int st = s_idx[0] / kTile;
-  const int st_last = s_idx[nn - 1] / kTile;
-  while (true) {
-    // stage source tile st
+  // Source tiles in the order the kept entries visit them, one per run of consecutive entries in the same
+  // tile.  Sorted logical indices give increasing slots except where the window ring wraps, so a tile
+  // can come back once (staged again; its entries are copied again, unchanged).
+  for (int q = 0; q < nn;) {
+    const int st = s_idx[q] / kTile;
+    int qe = q + 1;
+    while (qe < nn && s_idx[qe] / kTile == st) ++qe;
     const uint4* tp = reinterpret_cast<const uint4*>(vsrc + (size_t)st * TE);
 #pragma unroll
     for (int i = 0; i < PER; ++i) s_src[tid + 256 * i] = tp[tid + 256 * i];
@@ -426,17 +444,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
       for (int d = tid / kTile; d < D; d += 256 / kTile) sdst[d * kTile + jj] = ssrc[d * kTile + col];
     }
     __syncthreads();
-    if (st >= st_last) break;
-    // next source tile holding a kept entry
-    int nxt = INT32_MAX;
-    for (int q = 0; q < nn; ++q) {
-      const int tq = s_idx[q] / kTile;
-      if (tq > st) {
-        nxt = tq;
-        break;
-      }
-    }
-    st = nxt;
+    q = qe;
   }
   // the destination tile as full rows (slots past n in a partial tile hold
   // stale data; they are outside the valid prefix and never read)
@@ -452,7 +460,8 @@ static hipError_t compact_launch(CompactArgs a, hipStream_t s) {
   a.nt = 0;
   const int64_t blocks = a.nk + a.nv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((compact_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const unsigned layers = a.layers > 1 ? (unsigned)a.layers : 1u;
+  hipLaunchKernelGGL((compact_kernel<T, D>), dim3((unsigned)blocks, layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -168,6 +168,22 @@ class RelaxForcing:
         return c.attend(q, t0)
 
 
+class DenoiseLoop:
+    """Chunk-wise denoising over one cache per layer (Causal-Forcing article, section 4; LingBot-World 2.0
+    article): for each chunk, pass 0 writes the chunk's frames (rolling the window), passes 1..steps-1 and
+    the clean commit pass at t = 0 re-write them in place (KVC_APPEND_REPLACE_NEWEST), and each pass
+    attends.  Inside a pass the layers run in order, each with its own q/k/v."""
+
+    def __init__(self, caches, sched, steps=4):
+        self.caches, self.sched, self.steps = caches, sched, steps
+
+    def pass_layer(self, i, layer, s, q, k, v):
+        c = self.caches[layer]
+        t0 = _start_frame(self.sched, i)
+        c.append(k, v, t0, replace_newest=s > 0)
+        return c.attend(q, t0)
+
+
 def _close_gaps(c, sink, n_comp):
     """Shift the compressed region to end one frame before the tail, then the sink to end one frame before
     the compressed region (one time delta each, no clamp)."""

@@ -558,3 +558,106 @@ def test_attention_limit_refusals():
     with pytest.raises(KVCError) as e:
         m.attend(dev(q, w), 12)
     assert e.value.code == 5
+
+
+# ---------------------------------------------------------------- layer groups and the denoise loop
+def _group(w, n, compact=False):
+    from rolling_kv_cache_amd import create_group
+    return create_group(n, w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w,
+                        dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, bank_frames=w.bank_frames,
+                        compact=compact, raw_keys=w.raw_keys)
+
+
+def test_denoise_loop_over_a_layer_group():
+    """Three layers over one workspace: per chunk four sampling passes and the commit (pass 0 writes, the
+    rest re-write in place), each layer attending with its own q/k/v; after every second chunk one batched
+    retime of all layers (alternately a shift of +2 and a clamped shift of -3).  Every pass's attention and
+    every layer's cache state against the oracle."""
+    from oracle import DenoiseLoopRun
+    from rolling_kv_cache_amd import retime_layers
+    from rolling_kv_cache_amd.policies import DenoiseLoop
+    from workloads import denoise_inputs
+    w = SMALL_SW
+    L = 3
+    caches = _group(w, L)
+    loop = DenoiseLoop(caches, w)
+    run = DenoiseLoopRun(w, L)
+    for i in range(w.n_chunks):
+        for s in range(5):
+            for layer in range(L):
+                q, k, v = denoise_inputs(w, i, s, layer)
+                out = loop.pass_layer(i, layer, s, dev(q, w), dev(k, w), dev(v, w)).float().cpu().numpy()
+                check_attention(out, run.step(i, layer, s, q, k, v), f"chunk {i} pass {s} layer {layer}")
+        if i % 2 == 1:
+            delta, clamp = (2, False) if i % 4 == 1 else (-3, True)
+            retime_layers(caches, delta, clamp)
+            for c in run.caches:
+                c.retime(delta, clamp)
+        for layer in range(L):
+            assert_state_equal(caches[layer], run.caches[layer], w, f"chunk {i} layer {layer}")
+
+
+def test_layer_batched_sink_push_and_compact():
+    """Rolling-Sink pushes and a Deep-Forcing-style compaction as single launches over two layers, each
+    layer's state against the oracle."""
+    from rolling_kv_cache_amd import compact_layers, sink_push_layers
+    base = WORKLOADS["c4"]
+    w = Workload("grp", 221, 2, 128, "bf16", 4, 8, 3, 4, (1,) * 12, bank_frames=6)
+    caches = _group(w, 2, compact=True)
+    oc = [OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                      w.bank_frames) for _ in range(2)]
+    for i in range(8):
+        for layer in range(2):
+            _, k, v = chunk_inputs(w, 10 * layer + i, frames=1)
+            caches[layer].append(dev(k, w), dev(v, w), i)
+            oc[layer].append(k, v, 1, i)
+    sink_push_layers(caches, 2, 1, 8)
+    sink_push_layers(caches, 4, 2, 9)
+    for c in oc:
+        c.sink_push(2, 1, 8)
+        c.sink_push(4, 2, 9)
+    n = oc[0].n
+    keep = np.concatenate([np.arange(oc[0].n_sink), oc[0].n_sink + np.arange(0, n - oc[0].n_sink, 3)])
+    compact_layers(caches, keep)
+    for c in oc:
+        c.compact(keep)
+    for layer in range(2):
+        assert_state_equal(caches[layer], oc[layer], w, f"layer {layer}")
+
+
+def test_layer_batch_refusals():
+    from rolling_kv_cache_amd import KVCError, retime_layers
+    w = SMALL_SW
+    caches = _group(w, 3)
+    other = _group(w, 2)
+    _, k, v = chunk_inputs(w, 0)
+    for c in caches + other:
+        c.append(dev(k, w), dev(v, w), 0)
+    for bad, code in (([caches[0], caches[2]], 1), ([caches[1], caches[0]], 1), ([caches[0], other[1]], 1),
+                      ([new_cache(w), caches[1]], 1)):
+        with pytest.raises(KVCError) as e:
+            retime_layers(bad, 1)
+        assert e.value.code == code
+    caches[1].append(dev(k, w), dev(v, w), 1)                     # layer 1 moves on alone
+    with pytest.raises(KVCError) as e:
+        retime_layers(caches, 1)
+    assert e.value.code == 3
+    retime_layers(caches[:1], 1)                                   # one layer: the plain call
+
+
+def test_compact_across_the_ring_wrap():
+    """Regression: a compaction whose kept window entries cross the ring's wrap (the window has evicted, so
+    its logical start is mid-buffer) -- the source slots of the kept entries fall again after the wrap and
+    every source tile they touch must be gathered."""
+    w = Workload("wrapc", 222, 2, 128, "bf16", 4, 8, 3, 4, (1,) * 8)
+    gc = new_cache(w, compact=True)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(9):
+        _, k, v = chunk_inputs(w, i, frames=1)
+        gc.append(dev(k, w), dev(v, w), i)
+        oc.append(k, v, 1, i)
+    assert gc.info()["window_head"] != 0
+    keep = np.concatenate([np.arange(oc.n_sink), oc.n_sink + np.arange(0, oc.n - oc.n_sink, 3)])
+    gc.compact(keep)
+    oc.compact(keep)
+    assert_state_equal(gc, oc, w, "compaction across the wrap")
