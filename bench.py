@@ -153,6 +153,7 @@ def main():
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
     extras.update(raw_keys_ab(dev, stream, ev, flush, w))
     extras.update(memrope_chunk(dev, stream, ev, flush, WORKLOADS["c6"]))
+    extras.update(layer_group(dev, stream, ev, flush, WORKLOADS["c5a"]))
     # plain device copy of 1 GiB (twice the MALL): the achievable HBM rate on this board
     cx = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cy = torch.empty_like(cx)
@@ -454,6 +455,60 @@ def memrope_chunk(dev, stream, ev, flush, w):
             out["memrope_attend_tflops"] = round(4.0 * H * q.shape[0] * nk * D / (ms * 1e-3) / 1e12, 1)
         del c
     return out
+
+
+def layer_group(dev, stream, ev, flush, w, L=30):
+    """A 30-layer group at the Wan-1.3B shape (12 heads, 3 sink + 18 window frames, full: 32760 entries per
+    layer, 6 GB in all).  MALL flushed: one Infinity-RoPE shift of every layer (clamped, -3 frames) as one
+    launch vs 30 single-layer launches.  Then one chunk of the denoise loop: 4 sampling passes and the commit,
+    each pass appending (pass 0) or re-writing the 3-frame chunk and attending, layer after layer."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from rolling_kv_cache_amd.policies import DenoiseLoop
+    from workloads import chunk_inputs
+    S, H, D = w.frame_seqlen, w.heads, w.head_dim
+    caches = kvc.create_group(L, w.sink_frames, w.window_frames, S, H, D, w.grid_w, torch.bfloat16)
+    chunk = [tuple(torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, c)) for c in range(2)]
+    for i in range(7):
+        for c in caches:
+            c.append(chunk[i % 2][1], chunk[i % 2][2], 3 * i)
+    torch.cuda.synchronize()
+
+    def cold(fn, n=6):
+        ts = []
+        for i in range(n):
+            flush.sum()
+            a, b = ev(), ev()
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 1:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.mean(ts))
+
+    batched = cold(lambda i: kvc.retime_layers(caches, -3 if i % 2 == 0 else 3, i % 2 == 0))
+    single = cold(lambda i: [c.retime(-3 if i % 2 == 0 else 3, i % 2 == 0) for c in caches])
+    loop = DenoiseLoop(caches, w)
+    q, k, v = chunk[0]
+    for c in caches:
+        c.retime(0)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(stream)
+    for s in range(5):
+        for layer in range(L):
+            loop.pass_layer(7, layer, s, q, k, v)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    n = caches[0].info()["n_valid"]
+    flop = 5 * L * 4.0 * H * q.shape[0] * n * D
+    del caches
+    return {"group30_retime_batched_us_cold": round(batched, 1), "group30_retime_per_layer_us_cold": round(single, 1),
+            "denoise_chunk_30_layers_ms": round(ms, 2),
+            "denoise_chunk_attend_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
 
 
 def vendor_context(dev, stream, H, N, Lk, D):
