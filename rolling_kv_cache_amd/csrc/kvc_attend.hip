@@ -927,7 +927,7 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
   }
 }
 
-template <bool RAW>
+template <bool CAUSAL, bool RAW>
 __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles) {
   __shared__ u32x4_t lks[2][kKTileP];
@@ -937,14 +937,36 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   const int lin = (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
   const int h = lin / mblocks;
-  const int mb = lin - h * mblocks;
+  const int mb = CAUSAL ? mblocks - 1 - (lin - h * mblocks) : lin - h * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
   const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
-  const int last = ntiles - 1;
+  // block-causal limits, as in the running-maximum kernel
+  int nt = ntiles, lim = 0, lim_lo = 0;
+  if (CAUSAL) {
+    const int cb = a.causal_block, nall = a.keys.n[0] + a.keys.n[1];
+    auto limit = [&](int r) { return min(nall, (r / cb + 1) * cb); };
+    const int r0 = mb * 256, r1 = min(a.Lq, r0 + 256) - 1;
+    lim_lo = limit(r0);
+    lim = limit(min(qrow, a.Lq - 1));
+    const int lim_hi = limit(r1), n0 = a.keys.n[0];
+    nt = lim_hi <= n0 ? (lim_hi + kBN - 1) / kBN : ntile0 + (lim_hi - n0 + kBN - 1) / kBN;
+  }
+  const int last = nt - 1;
+  auto mask = [&](f32x16_t* s, int t) {
+    const int nv = ts.valid(t);
+    if (CAUSAL) {
+      const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
+      if (lb + kBN > lim_lo) {
+        mask_tile(s, 0, min(nv, lim - lb), hl);
+        return;
+      }
+    }
+    mask_tile(s, ts.lead(t), nv, hl);
+  };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
   const RawPtrs rp = raw_ptrs(a.keys, h, tid);
   if (tid == 0) s_flag = 0;
@@ -993,8 +1015,8 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
       sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
     }
   }
-  mask_tile(sa, ts.lead(0), ts.valid(0), hl);
-  // tile 0 holds at least one valid key, so the reference is finite
+  mask(sa, 0);
+  // tile 0 holds at least one valid key (for every row, also block-causal), so the reference is finite
   const float negm = -tile_max(sa, c2);
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
@@ -1010,7 +1032,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     pmax = fmaxf(pmax, psum);
     lsum += psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
-    mask_tile(snext, ts.lead(min(t + 1, last)), ts.valid(min(t + 1, last)), hl);
+    mask(snext, min(t + 1, last));
     if constexpr (RAW)
       storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     else
@@ -1019,11 +1041,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   };
 
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  for (; t + 1 < nt; t += 2) {
     step(t, sa, sb);
     step(t + 1, sb, sa);
   }
-  if (t < ntiles) step(t, sa, sb);
+  if (t < nt) step(t, sa, sb);
   if (__ballot(!(pmax <= kPLimit)) != 0 && lane == 0) s_flag = 1;
   __syncthreads();
   if (tid == 0) a.flags[lin] = s_flag;
@@ -1032,7 +1054,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
 
 template <int VAR, bool RAW>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int bm = (VAR == 2 || VAR == 4 || VAR == 5) ? 256 : kBM;
+  const int bm = (VAR == 2 || VAR == 4 || VAR == 5 || VAR == 6) ? 256 : kBM;
   const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
@@ -1063,9 +1085,15 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   else if (VAR == 5)
     hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
                        n0, nt, (const int32_t*)nullptr);
-  else if (VAR == 4) {
-    hipLaunchKernelGGL((attend_v5f_kernel<RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
-                       nt);
+  else if (VAR == 6) {       // block-causal: fixed reference, then the flagged blocks with the running maximum
+    hipLaunchKernelGGL((attend_v5f_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
+                       per_xcd, n0, nt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
+                       n0, nt, (const int32_t*)b.flags);
+  } else if (VAR == 4) {
+    hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
+                       per_xcd, n0, nt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
                        n0, nt, (const int32_t*)b.flags);
@@ -1083,11 +1111,13 @@ hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
   if (a.raw) {
     // raw-key caches: the 8-wave kernels only (the 4-wave variant has no time-band staging)
-    if (a.causal_block > 0) return attend_launch<5, true>(a, s);
+    if (a.causal_block > 0) return (a.flags && !(v && std::string(v) == "v5")) ? attend_launch<6, true>(a, s)
+                                                                              : attend_launch<5, true>(a, s);
     if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, true>(a, s);
     return attend_launch<4, true>(a, s);
   }
-  if (a.causal_block > 0) return attend_launch<5, false>(a, s);
+  if (a.causal_block > 0) return (a.flags && !(v && std::string(v) == "v5")) ? attend_launch<6, false>(a, s)
+                                                                            : attend_launch<5, false>(a, s);
   if (v && std::string(v) == "v3") return attend_launch<0, false>(a, s);
   if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, false>(a, s);
   return attend_launch<4, false>(a, s);

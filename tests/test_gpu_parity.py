@@ -661,3 +661,26 @@ def test_compact_across_the_ring_wrap():
     gc.compact(keep)
     oc.compact(keep)
     assert_state_equal(gc, oc, w, "compaction across the wrap")
+
+
+@pytest.mark.parametrize("variant", ["", "v5"])
+def test_block_causal_score_jump(variant):
+    """Block-causal attention where the later blocks' scores exceed the first key tile's by 48-90 in exp2
+    units: the fixed-reference kernel must flag those blocks and the running-maximum pass redo them."""
+    w = Workload("bcjump", 223, 2, 128, "bf16", 9, 23, 0, 6, (2,) * 3)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(3):
+        _, k, v = chunk_inputs(w, i, frames=2)
+        k = (k * (4.0 if i >= 1 else 1.0 / 64)).astype(np.float32)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    (q,) = chunk_inputs(w, 98, tensors=(0,), frames=6)
+    q = (q * 4.0).astype(np.float32)
+    if variant:
+        os.environ["KVC_ATTEND_VARIANT"] = variant
+    try:
+        out = gc.attend_block_causal(dev(q, w), 0, 2).float().cpu().numpy()
+    finally:
+        os.environ.pop("KVC_ATTEND_VARIANT", None)
+    check_attention(out, oc.attend_block_causal(q, 6, 0, 2), f"block-causal score jump {variant or 'default'}")
