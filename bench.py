@@ -312,31 +312,42 @@ def sink_push_and_compact(dev, stream, flush, ev):
 
 def per_gpu_share(dev, stream, ev, w):
     """Attention at one GPU's share of the 40-head layer when heads are split over 8 GPUs: 5 heads, the same
-    4680 queries over 28080 keys (19 query blocks x 5 heads = 95 workgroups for 256 CUs)."""
+    4680 queries over 28080 keys (19 query blocks x 5 heads = 95 workgroups for 256 CUs): split keys (the
+    cache reserves the split buffers), and the unsplit launch for comparison."""
+    import os
     import numpy as np
     import torch
     import rolling_kv_cache_amd as kvc
     from workloads import chunk_inputs
     S, D, Hs = w.frame_seqlen, w.head_dim, 5
-    c = kvc.KVCache(w.sink_frames, w.window_frames, S, Hs, D, w.grid_w, torch.bfloat16)
+    c = kvc.KVCache(w.sink_frames, w.window_frames, S, Hs, D, w.grid_w, torch.bfloat16, split_attend=True)
     q = None
     for i in range(6):
         q_, k, v = (torch.from_numpy(x[:, :Hs].copy()).to(dev, torch.bfloat16) for x in chunk_inputs(w, i))
         c.append(k, v, 3 * i)
         q = q_
-    out = c.attend(q, 15)
-    torch.cuda.synchronize()
-    ts = []
-    for i in range(8):
-        a, b = ev(), ev()
-        a.record(stream)
-        c.attend(q, 15, out=out)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ms = float(np.median(ts))
     flop = 4.0 * Hs * q.shape[0] * c.info()["n_valid"] * D
-    return {"attend_5head_share_ms": round(ms, 4), "attend_5head_share_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    res = {}
+    for tag, env in (("", None), ("_unsplit", "0")):
+        if env is not None:
+            os.environ["KVC_ATTEND_SPLIT"] = env
+        try:
+            out = c.attend(q, 15)
+            torch.cuda.synchronize()
+            ts = []
+            for i in range(8):
+                a, b = ev(), ev()
+                a.record(stream)
+                c.attend(q, 15, out=out)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+        finally:
+            os.environ.pop("KVC_ATTEND_SPLIT", None)
+        ms = float(np.median(ts))
+        res[f"attend_5head_share{tag}_ms"] = round(ms, 4)
+        res[f"attend_5head_share{tag}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    return res
 
 
 def block_causal_clip(dev, stream, ev, w, block_frames=3):

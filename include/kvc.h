@@ -90,6 +90,13 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
  * (long at t_w - 2, short at t_w - 1).  kvc_compact, kvc_sink_push and
  * block-causal attention return KVC_EUNSUPPORTED on such a cache. */
 #define KVC_CREATE_MEMORY 4u
+/* kvc_create: reserve 65 MB of workspace for split-key attention.  When a
+ * kvc_attend call would give fewer 256-query workgroups than the GPU has
+ * compute units (few heads, short chunks: e.g. one GPU's share of a
+ * head-sharded layer), the keys are cut into 2-8 parts that run as separate
+ * workgroups, and a merge pass combines their partial results.  Without the
+ * flag such calls run unsplit. */
+#define KVC_CREATE_SPLIT_ATTEND 8u
 /* Largest |time index| and |retime delta| (the RoPE time table covers
  * positions -KVC_MAX_POS .. KVC_MAX_POS). */
 #define KVC_MAX_POS 16383

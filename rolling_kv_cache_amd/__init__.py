@@ -23,6 +23,7 @@ KVC_APPEND_REPLACE_NEWEST = 1
 KVC_CREATE_COMPACT = 1
 KVC_CREATE_RAW_KEYS = 2
 KVC_CREATE_MEMORY = 4
+KVC_CREATE_SPLIT_ATTEND = 8
 KVC_MAX_POS = 16383
 KVC_MAX_Q_FRAMES = 32
 
@@ -111,15 +112,15 @@ def _dt(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported cache dtype {dtype}")
 
 
-def _create_flags(compact=False, raw_keys=False, memory=False) -> int:
+def _create_flags(compact=False, raw_keys=False, memory=False, split_attend=False) -> int:
     return ((KVC_CREATE_COMPACT if compact else 0) | (KVC_CREATE_RAW_KEYS if raw_keys else 0)
-            | (KVC_CREATE_MEMORY if memory else 0))
+            | (KVC_CREATE_MEMORY if memory else 0) | (KVC_CREATE_SPLIT_ATTEND if split_attend else 0))
 
 
 def workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype=torch.bfloat16,
-                    bank_frames=0, compact=False, raw_keys=False, memory=False) -> int:
+                    bank_frames=0, compact=False, raw_keys=False, memory=False, split_attend=False) -> int:
     return int(lib.kvc_workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, _dt(dtype),
-                                       bank_frames, _create_flags(compact, raw_keys, memory)))
+                                       bank_frames, _create_flags(compact, raw_keys, memory, split_attend)))
 
 
 class KVCache:
@@ -127,7 +128,7 @@ class KVCache:
 
     def __init__(self, sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w,
                  dtype=torch.bfloat16, bank_frames=0, compact=False, device="cuda", stream=None, raw_keys=False,
-                 memory=None, _handle=None, _workspace=None):
+                 memory=None, split_attend=False, _handle=None, _workspace=None):
         """memory: (alpha_long, alpha_short) for MemRoPE memory tokens on a raw-key cache, or None."""
         self.S, self.H, self.D = frame_seqlen, heads, head_dim
         self.dtype = dtype
@@ -142,7 +143,7 @@ class KVCache:
             self._relax_scratch = None
             return
         nbytes = workspace_bytes(sink_frames, window_frames, frame_seqlen, heads, head_dim, dtype, bank_frames,
-                                 compact, raw_keys, memory is not None)
+                                 compact, raw_keys, memory is not None, split_attend)
         if nbytes == 0:
             raise KVCError(KVC_EINVAL, "unsupported geometry")
         self._ws_raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -151,7 +152,7 @@ class KVCache:
         self._stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
         _check(lib.kvc_create(sink_frames, window_frames, frame_seqlen, heads, head_dim, grid_w, _dt(dtype),
-                              bank_frames, _create_flags(compact, raw_keys, memory is not None),
+                              bank_frames, _create_flags(compact, raw_keys, memory is not None, split_attend),
                               ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
                               ctypes.c_void_p(self._stream.cuda_stream), ctypes.byref(h)))
         self._h = h

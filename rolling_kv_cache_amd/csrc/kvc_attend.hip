@@ -37,6 +37,7 @@
 //    blocks of the same head land on the same XCD so they share its L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <string>
@@ -49,6 +50,7 @@ namespace kvc {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // native vector type for 16-byte moves (HIP's uint4 is a class that blocks
 // scalar replacement and lands in private memory)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -147,6 +149,26 @@ __device__ __forceinline__ void mask_tile(f32x16_t* s, int lead, int nv, int hl)
     }
 }
 
+// a split-key part's rows: the unnormalised O, the reference m and the row sum
+__device__ __forceinline__ void store_partial(const AttendArgs& a, const f32x16_t* o, float m, float lsum, int qrow,
+                                              int h, int part, int hl) {
+  const float l = xhalf_sum(lsum);
+  if (qrow >= a.Lq) return;
+  const int64_t r = ((int64_t)part * a.geo.H + h) * a.Lq + qrow;
+  float* op = a.split_o + r * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4_t x = {o[db][gq * 4], o[db][gq * 4 + 1], o[db][gq * 4 + 2], o[db][gq * 4 + 3]};
+      *reinterpret_cast<f32x4_t*>(op + db * 32 + gq * 8 + hl * 4) = x;
+    }
+  if (hl == 0) {
+    a.split_ml[r * 2] = m;
+    a.split_ml[r * 2 + 1] = l;
+  }
+}
+
 __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o, float lsum, int qrow, int h, int hl) {
   const float inv = 1.f / xhalf_sum(lsum);
   if (qrow >= a.Lq) return;
@@ -169,18 +191,23 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o
 // [lo0, n0), then region 1's.  base = first slot of the tile (64-aligned),
 // valid = slots of the tile before the range end, lead = slots of the tile
 // before the range start (> 0 only in a range's first tile).
+// `first` shifts the sequence (a split-key workgroup starts at its part's first tile).
 struct TileSeq {
   int ntile0, ntiles;
   int t00, t01;            // first tile of each range
   int lo0, lo1, n0, n1;
-  __device__ __forceinline__ int region(int it) const { return it < ntile0 ? 0 : 1; }
-  __device__ __forceinline__ int base(int it) const { return (it < ntile0 ? t00 + it : t01 + it - ntile0) * kBN; }
-  __device__ __forceinline__ int valid(int it) const { return (it < ntile0 ? n0 : n1) - base(it); }
-  __device__ __forceinline__ int lead(int it) const { return (it < ntile0 ? lo0 : lo1) - base(it); }
+  int first;
+  __device__ __forceinline__ int region(int it) const { return it + first < ntile0 ? 0 : 1; }
+  __device__ __forceinline__ int base(int it) const {
+    const int jt = it + first;
+    return (jt < ntile0 ? t00 + jt : t01 + jt - ntile0) * kBN;
+  }
+  __device__ __forceinline__ int valid(int it) const { return (it + first < ntile0 ? n0 : n1) - base(it); }
+  __device__ __forceinline__ int lead(int it) const { return (it + first < ntile0 ? lo0 : lo1) - base(it); }
 };
 
 __device__ __forceinline__ TileSeq tile_seq(const KeyRegions& k, int ntile0, int ntiles) {
-  return TileSeq{ntile0, ntiles, k.lo[0] / kBN, k.lo[1] / kBN, k.lo[0], k.lo[1], k.n[0], k.n[1]};
+  return TileSeq{ntile0, ntiles, k.lo[0] / kBN, k.lo[1] / kBN, k.lo[0], k.lo[1], k.n[0], k.n[1], 0};
 }
 
 // tiles covering region r's visible slots
@@ -531,24 +558,33 @@ __device__ __forceinline__ void storeR(StageR& st, const RawPtrs& p, u32x4_t* lk
 // min(n, (r / causal_block + 1) * causal_block); a workgroup loops only over
 // the tiles its longest prefix needs, rows whose prefix ends inside a tile mask
 // the rest per lane, and workgroups with the longest prefixes start first.
+//
+// kparts > 1 (split keys, for launches with fewer workgroups than CUs): the
+// tiles are cut into kparts contiguous parts, workgroup (head, part, query
+// block) runs over its part only and writes its unnormalised O with the row's
+// reference and sum to the split buffers; merge_split_kernel combines them.
 template <bool CAUSAL, bool RAW>
 __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                           int ntile0, int ntiles, const int32_t* only_flagged) {
+                                                           int ntile0, int ntiles, const int32_t* only_flagged,
+                                                           int kparts) {
   __shared__ u32x4_t lks[2][kKTileP];
   __shared__ u32x4_t lvs[2][kVTileP];
   const int wg = blockIdx.x;
   const int lin = (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
   if (only_flagged != nullptr && only_flagged[lin] == 0) return;
-  const int h = lin / mblocks;
-  const int mb = CAUSAL ? mblocks - 1 - (lin - h * mblocks) : lin - h * mblocks;
+  const int hp = lin / mblocks;                         // head * kparts + part
+  const int h = hp / kparts, part = hp - h * kparts;
+  const int mb = CAUSAL ? mblocks - 1 - (lin - hp * mblocks) : lin - hp * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  // balanced parts: [part * ntiles / kparts, (part + 1) * ntiles / kparts), never empty (kparts <= ntiles / 4)
+  ts.first = part * ntiles / kparts;
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
-  int nt = ntiles, lim = 0, lim_lo = 0;
+  int nt = (part + 1) * ntiles / kparts - ts.first, lim = 0, lim_lo = 0;
   if (CAUSAL) {
     const int cb = a.causal_block, nall = a.keys.n[0] + a.keys.n[1];
     auto limit = [&](int r) { return min(nall, (r / cb + 1) * cb); };
@@ -653,7 +689,39 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     step(t + 1, sb, sa);
   }
   if (t < nt) step(t, sa, sb);
-  store_out(a, o, lsum, qrow, h, hl);
+  if (kparts > 1)
+    store_partial(a, o, m, lsum, qrow, h, part, hl);
+  else
+    store_out(a, o, lsum, qrow, h, hl);
+}
+
+// out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s) over the key parts,
+// M = max_s m_s; one thread per (head, row, 4 dims).
+__global__ __launch_bounds__(256) void merge_split_kernel(AttendArgs a, int kparts) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c = (int)(id & 31);
+  const int64_t hr = id >> 5;
+  if (hr >= (int64_t)a.geo.H * a.Lq) return;
+  const int h = (int)(hr / a.Lq), row = (int)(hr - (int64_t)h * a.Lq);
+  float M = -INFINITY;
+  for (int p = 0; p < kparts; ++p) M = fmaxf(M, a.split_ml[(((int64_t)p * a.geo.H + h) * a.Lq + row) * 2]);
+  float l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < kparts; ++p) {
+    const int64_t r = ((int64_t)p * a.geo.H + h) * a.Lq + row;
+    const float w = __builtin_amdgcn_exp2f(a.split_ml[r * 2] - M);
+    l += w * a.split_ml[r * 2 + 1];
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.split_o + r * 128 + c * 4);
+    acc += w * x;
+  }
+  const float inv = 1.f / l;
+  union {
+    uint2 u;
+    __bf16 b[4];
+  } y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y.b[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<uint2*>((uint16_t*)a.out + ((int64_t)row * a.geo.H + h) * 128 + c * 4) = y.u;
 }
 
 // ---------------------------------------------------------------------------
@@ -1052,9 +1120,27 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   store_out(a, o, lsum, qrow, h, hl);
 }
 
+// key parts for a split launch (one workgroup per CU at a time): the count in
+// 2..8 whose workgroups fill the last round of 256 CUs best (ties: fewer
+// parts), with at least four tiles per part and kSplitRows rows of partials
+static int split_parts(int total, int ntiles) {
+  int best = 1;
+  double best_fill = 0.0;
+  for (int kp = 2; kp <= 8; ++kp) {
+    if (kp * 4 > ntiles || (int64_t)kp * total * 256 > kSplitRows) break;
+    const int wgs = kp * total;
+    const double fill = (double)wgs / (256.0 * ((wgs + 255) / 256));
+    if (fill > best_fill + 0.02) {
+      best = kp;
+      best_fill = fill;
+    }
+  }
+  return best;
+}
+
 template <int VAR, bool RAW>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int bm = (VAR == 2 || VAR == 4 || VAR == 5 || VAR == 6) ? 256 : kBM;
+  const int bm = (VAR == 2 || VAR == 4 || VAR == 5 || VAR == 6 || VAR == 7) ? 256 : kBM;
   const int mblocks = (a.Lq + bm - 1) / bm;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
@@ -1079,24 +1165,32 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     n0 = ntile1;
     nt = ntile1;
   }
-  if (VAR == 2)
+  if (VAR == 7) {            // split keys: partials, then the merge
+    const int kp = split_parts(total, nt);
+    const int tot = total * kp, pxcd = (tot + 7) / 8;
+    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * pxcd), dim3(512), 0, s, b, mblocks, tot, pxcd, n0, nt,
+                       (const int32_t*)nullptr, kp);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int64_t threads = (int64_t)a.geo.H * a.Lq * 32;
+    hipLaunchKernelGGL(merge_split_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, b, kp);
+  } else if (VAR == 2)
     hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)nullptr);
+                       n0, nt, (const int32_t*)nullptr, 1);
   else if (VAR == 5)
     hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)nullptr);
+                       n0, nt, (const int32_t*)nullptr, 1);
   else if (VAR == 6) {       // block-causal: fixed reference, then the flagged blocks with the running maximum
     hipLaunchKernelGGL((attend_v5f_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
                        per_xcd, n0, nt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)b.flags);
+                       n0, nt, (const int32_t*)b.flags, 1);
   } else if (VAR == 4) {
     hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
                        per_xcd, n0, nt);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)b.flags);
+                       n0, nt, (const int32_t*)b.flags, 1);
   }
   else
     hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
@@ -1109,6 +1203,15 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
 // workgroups per CU) selects another kernel for A/B timing.
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   const char* v = std::getenv("KVC_ATTEND_VARIANT");
+  // fewer workgroups than CUs: split the keys when the workspace holds the partials
+  // (KVC_ATTEND_SPLIT=0 turns this off for comparisons)
+  if (a.split_o && a.causal_block == 0 && !(std::getenv("KVC_ATTEND_SPLIT") &&
+                                            std::string(std::getenv("KVC_ATTEND_SPLIT")) == "0")) {
+    const int total = (a.Lq + 255) / 256 * a.geo.H;
+    const int kp = split_parts(total, range_tiles(a.keys, 0) + range_tiles(a.keys, 1));
+    if (total < 256 && kp >= 2 && (int64_t)kp * a.geo.H * a.Lq <= kSplitRows)
+      return a.raw ? attend_launch<7, true>(a, s) : attend_launch<7, false>(a, s);
+  }
   if (a.raw) {
     // raw-key caches: the 8-wave kernels only (the 4-wave variant has no time-band staging)
     if (a.causal_block > 0) return (a.flags && !(v && std::string(v) == "v5")) ? attend_launch<6, true>(a, s)

@@ -138,7 +138,11 @@ struct AttendArgs {
   int32_t raw;                            // raw-key cache: rotate each key's time band at its slot's t
   int32_t mem_lo;                         // region-0 slots [mem_lo, mem_lo + 2S): memory tokens ...
   int32_t mem_t[2];                       // ... placed at times mem_t[0] (first S) and mem_t[1] (next S)
+  float* split_o;                         // workspace (KVC_CREATE_SPLIT_ATTEND): per key part, head and row,
+  float* split_ml;                        // the unnormalised O [128] and (reference, row sum); else null
 };
+
+constexpr int kSplitRows = 512 * 256;     // part x head x query rows the split-key buffers hold
 
 struct ScoreArgs {
   const void* q;                          // raw query window [Nq][H][D]

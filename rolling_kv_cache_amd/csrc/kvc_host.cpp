@@ -40,7 +40,7 @@ struct Layout {
   int32_t D = 0, DA = 0, DB = 0, dt = 0, bw = 0, esz = 0;
   RegionLayout sink{}, win[2]{};
   size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, att_flags = 0, total = 0;
-  size_t mem_k = 0, mem_v = 0;
+  size_t mem_k = 0, mem_v = 0, split_o = 0, split_ml = 0;
 };
 
 Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_t H, int32_t D, kvc_dtype dt,
@@ -91,6 +91,10 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   L.keep = take((size_t)L.WP * 4);
   // one recompute flag per 256-query attention block of the largest query chunk
   L.att_flags = take((size_t)H * (((size_t)KVC_MAX_Q_FRAMES * S + 255) / 256) * 4);
+  if (cflags & KVC_CREATE_SPLIT_ATTEND) {
+    L.split_o = take((size_t)kvc::kSplitRows * 128 * 4);
+    L.split_ml = take((size_t)kvc::kSplitRows * 2 * 4);
+  }
   if (cflags & KVC_CREATE_MEMORY) {
     L.mem_k = take((size_t)2 * H * S * D * 4);
     L.mem_v = take((size_t)2 * H * S * D * 4);
@@ -294,7 +298,7 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   Layout L = make_layout(sink_frames, window_frames, frame_seqlen, heads, head_dim, dt, bank_frames, create_flags);
   if (!L.ok) return fail(KVC_EINVAL, "unsupported geometry (head_dim must be 64 or 128; sizes positive)");
   if (grid_w < 1 || frame_seqlen % grid_w != 0) return fail(KVC_EINVAL, "frame_seqlen must be a multiple of grid_w");
-  if (create_flags & ~(KVC_CREATE_COMPACT | KVC_CREATE_RAW_KEYS | KVC_CREATE_MEMORY))
+  if (create_flags & ~(KVC_CREATE_COMPACT | KVC_CREATE_RAW_KEYS | KVC_CREATE_MEMORY | KVC_CREATE_SPLIT_ATTEND))
     return fail(KVC_EINVAL, "unknown create flag");
   if ((create_flags & KVC_CREATE_MEMORY) && !(create_flags & KVC_CREATE_RAW_KEYS))
     return fail(KVC_EINVAL, "memory tokens need KVC_CREATE_RAW_KEYS");
@@ -493,6 +497,10 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
   a.causal_block = causal_block;
   a.raw = (h->cflags & KVC_CREATE_RAW_KEYS) ? 1 : 0;
   a.mem_lo = INT32_MAX;
+  if ((h->cflags & KVC_CREATE_SPLIT_ATTEND) && h->D == 128 && h->geo.esz == 2) {
+    a.split_o = (float*)(h->ws + h->L.split_o);
+    a.split_ml = (float*)(h->ws + h->L.split_ml);
+  }
   const int32_t n_valid = h->st.n_valid();
   if (h->max_keys > 0 && h->max_keys < n_valid) {
     // only the newest max_keys entries in logical order: at most two physical ranges (a window suffix

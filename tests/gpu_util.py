@@ -23,11 +23,11 @@ def dev(x: np.ndarray, w) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=torch_dtype(w))
 
 
-def new_cache(w, compact=False):
+def new_cache(w, compact=False, split=False):
     from rolling_kv_cache_amd import KVCache
     return KVCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w,
                    dtype=torch_dtype(w), bank_frames=w.bank_frames, compact=compact, raw_keys=w.raw_keys,
-                   memory=w.memory)
+                   memory=w.memory, split_attend=split)
 
 
 def bits(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -164,3 +164,35 @@ def test_c2_clip_block_causal():
     rows = np.unique(np.concatenate([rng.choice(F * S, size=512, replace=False), edges]))
     mx, rr = check_attention(out[rows], oc.attend_block_causal(q, F, 0, 3, rows=rows), "c2 clip block-causal")
     log(f"c2 clip block-causal: max_abs {mx:.3e} rel_rms {rr:.3e} on {rows.shape[0]} rows")
+
+
+@pytest.mark.timeout(900)
+def test_head_share_split_keys():
+    """One GPU's share of the 40-head layer (5 heads, 4680 queries over 28080 keys): 95 query workgroups, so
+    the keys are split in 5 parts; 512 sampled rows against the oracle, and the unsplit launch alike."""
+    import os
+    from oracle import OracleCache
+    w = WORKLOADS["c3"]
+    H = 5
+    S = w.frame_seqlen
+    from rolling_kv_cache_amd import KVCache
+    import torch
+    gc = KVCache(w.sink_frames, w.window_frames, S, H, w.head_dim, w.grid_w, torch.bfloat16, split_attend=True)
+    oc = OracleCache(w.sink_frames, w.window_frames, S, H, w.head_dim, w.grid_w, w.dtype)
+    q = None
+    for i in range(6):
+        q, k, v = (x[:, :H].copy() for x in chunk_inputs(w, i))
+        gc.append(dev(k, w), dev(v, w), 3 * i)
+        oc.append(k, v, 3, 3 * i)
+    rows = np.sort(np.random.default_rng(77).choice(q.shape[0], size=512, replace=False))
+    ref = oc.attend(q, 3, 15, rows=rows)
+    with Timer("head share split"):
+        out = gc.attend(dev(q, w), 15).float().cpu().numpy()
+    mx, rr = check_attention(out[rows], ref, "head share split")
+    os.environ["KVC_ATTEND_SPLIT"] = "0"
+    try:
+        out1 = gc.attend(dev(q, w), 15).float().cpu().numpy()
+    finally:
+        os.environ.pop("KVC_ATTEND_SPLIT", None)
+    check_attention(out1[rows], ref, "head share unsplit")
+    log(f"head share split: max_abs {mx:.3e} rel_rms {rr:.3e}")

@@ -13,9 +13,9 @@ from workloads import WORKLOADS, Workload, chunk_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _drive(w, n_chunks=None, full_attention=True, compact=False, general=False):
+def _drive(w, n_chunks=None, full_attention=True, compact=False, general=False, split=False):
     from rolling_kv_cache_amd.policies import driver_for
-    gc = new_cache(w, compact=compact)
+    gc = new_cache(w, compact=compact, split=split)
     drv = driver_for(w.name)(gc, w)
     run = make_run(w)
     q_prev_d = q_prev = None
@@ -684,3 +684,17 @@ def test_block_causal_score_jump(variant):
     finally:
         os.environ.pop("KVC_ATTEND_VARIANT", None)
     check_attention(out, oc.attend_block_causal(q, 6, 0, 2), f"block-causal score jump {variant or 'default'}")
+
+
+# ---------------------------------------------------------------- split-key attention
+@pytest.mark.parametrize("raw", [False, True])
+def test_split_key_attention(raw):
+    """Three heads and chunks of up to 180 queries give a handful of workgroups, so the keys are split in
+    parts (2 to 8 as the cache grows) and merged; ragged tiles, sink/window regions and wrap as before."""
+    _drive(_replace(SMALL_SW, name="split", raw_keys=raw), split=True)
+
+
+def test_split_key_attention_flush_and_retime():
+    base = WORKLOADS["c5a"]
+    _drive(Workload("c5a_split", 224, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
+                    (3,) * 14 + (2,), cut_chunks=(7, 11)), compact=True, split=True)
