@@ -75,7 +75,9 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
  * and the time band raw; kvc_attend rotates each key's time band at its slot's
  * current time while staging it, so every attended key equals a fresh
  * rotation of the raw key and kvc_retime only rewrites time indices.
- * kvc_score and kvc_relax_scores return KVC_EUNSUPPORTED on such a cache. */
+ * kvc_score and kvc_relax_scores see the keys placed the same way (their
+ * scratch then also holds a copy of the keys' time-band plane, rotated to each
+ * slot's current time; the *_scratch_bytes calls include it). */
 #define KVC_CREATE_RAW_KEYS 2u
 /* kvc_create: MemRoPE memory tokens (rCM length-extrapolation article: evicted
  * frames are compressed into long- and short-term EMA memories instead of

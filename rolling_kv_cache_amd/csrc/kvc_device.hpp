@@ -90,6 +90,9 @@ struct RetimeArgs {
   int32_t nrng;
   int32_t delta, clamp0;
   int32_t keys;                           // 0: raw-key cache, only t changes
+  void* out_ka[2];                        // non-null: rotate the stored time band by each slot's own t
+                                          // (a raw-key cache placed at its times) into these KA planes
+                                          // (same layout), leaving the cache and t untouched
   Geo geo;
   Tables tab;
 };

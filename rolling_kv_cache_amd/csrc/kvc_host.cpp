@@ -253,6 +253,38 @@ void build_tables(int32_t D, int32_t S, int32_t grid_w, std::vector<float>* tt, 
     }
 }
 
+// Raw-key caches: scores and Relax scores read the keys as attention sees them, so their scratch gets
+// a copy of the KA planes with each slot's time band rotated to its current time.
+size_t placed_ka_bytes(kvc_handle h) {
+  if (!(h->cflags & KVC_CREATE_RAW_KEYS)) return 0;
+  return align_up((size_t)h->H * h->L.SP * h->L.DA * h->geo.esz) + align_up((size_t)h->H * h->L.WP * h->L.DA * h->geo.esz);
+}
+
+hipError_t launch_placed_ka(kvc_handle h, char* dst, kvc::KeyRegions* keys) {
+  kvc::RetimeArgs a{};
+  a.reg[0] = h->sink;
+  a.reg[1] = cur_win(h);
+  a.out_ka[0] = dst;
+  a.out_ka[1] = dst + align_up((size_t)h->H * h->L.SP * h->L.DA * h->geo.esz);
+  const int32_t n[2] = {h->st.ns, h->st.nw};
+  int32_t blocks = 0;
+  for (int r = 0; r < 2; ++r) {
+    if (n[r] == 0) continue;
+    a.rng[a.nrng].region = r;
+    a.rng[a.nrng].lo = 0;
+    a.rng[a.nrng].n = n[r];
+    a.rng[a.nrng].blk0 = blocks;
+    blocks += (n[r] + 31) / 32;
+    ++a.nrng;
+  }
+  a.keys = 1;
+  a.geo = h->geo;
+  a.tab = h->tab;
+  keys->ka[0] = a.out_ka[0];
+  keys->ka[1] = a.out_ka[1];
+  return kvc::launch_retime(a, blocks, h->stream);
+}
+
 bool same_ring(const kvc::RingState& a, const kvc::RingState& b) {
   return a.ns == b.ns && a.hs == b.hs && a.nw == b.nw && a.hw == b.hw && a.win_buf == b.win_buf &&
          a.global_end == b.global_end && a.newest_valid == b.newest_valid && a.newest_frames == b.newest_frames &&
@@ -621,7 +653,7 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames) {
   if (!h || q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return 0;
   const size_t Nq = (size_t)q_frames * h->S;
   return align_up((size_t)h->H * Nq * h->D * 4) + 2 * align_up((size_t)h->H * Nq * 4) +
-         align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4);
+         align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4) + placed_ka_bytes(h);
 }
 
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
@@ -629,7 +661,6 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   if (kvc_status s = check(h)) return s;
   if (!q_win || !q_t || !scores || !scratch) return fail(KVC_EINVAL, "null argument");
   if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
-  if (h->cflags & KVC_CREATE_RAW_KEYS) return fail(KVC_EUNSUPPORTED, "score is not available on a raw-key cache");
   if (scratch_bytes < kvc_score_scratch_bytes(h, q_frames)) return fail(KVC_ENOMEM, "score scratch too small");
   if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
   if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "score on an empty cache");
@@ -647,6 +678,7 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   a.l = (float*)p;
   p += align_up((size_t)h->H * Nq * 4);
   a.part = (float*)p;
+  p += align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4);
   a.q = q_win;
   a.scores = scores;
   a.Nq = (int32_t)Nq;
@@ -660,7 +692,9 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   a.geo = h->geo;
   a.tab = h->tab;
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
-  hipError_t e = kvc::launch_score(a, h->stream, std::getenv("KVC_ATTEND_GENERAL") != nullptr);
+  hipError_t e = hipSuccess;
+  if (h->cflags & KVC_CREATE_RAW_KEYS) e = launch_placed_ka(h, p, &a.keys);
+  if (e == hipSuccess) e = kvc::launch_score(a, h->stream, std::getenv("KVC_ATTEND_GENERAL") != nullptr);
   return device_result(h, e, "score");
 }
 
@@ -670,14 +704,13 @@ size_t kvc_relax_scratch_bytes(kvc_handle h) {
   if (!h) return 0;
   const size_t nf = (size_t)(h->st.S_tok + h->st.W_tok) / h->S;   // at most this many whole frames
   return align_up(nf * relax_slices(h) * h->H * h->D * 4) + align_up(nf * h->H * h->D * 4) +
-         align_up((size_t)kvc::kRelaxMaxFrames * kvc::kRelaxMaxFrames * 4);
+         align_up((size_t)kvc::kRelaxMaxFrames * kvc::kRelaxMaxFrames * 4) + placed_ka_bytes(h);
 }
 
 kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
                             size_t scratch_bytes) {
   if (kvc_status s = check(h)) return s;
   if (!scores || !scratch) return fail(KVC_EINVAL, "null argument");
-  if (h->cflags & KVC_CREATE_RAW_KEYS) return fail(KVC_EUNSUPPORTED, "relax scores are not available on a raw-key cache");
   if (!(weight >= 0.f && weight <= 1.f)) return fail(KVC_EINVAL, "weight outside [0, 1]");
   if (scratch_bytes < kvc_relax_scratch_bytes(h)) return fail(KVC_ENOMEM, "relax scratch too small");
   if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
@@ -709,7 +742,11 @@ kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, flo
   a.scores = scores;
   a.weight = weight;
   a.geo = h->geo;
-  hipError_t e = kvc::launch_relax(a, h->stream);
+  hipError_t e = hipSuccess;
+  if (h->cflags & KVC_CREATE_RAW_KEYS)
+    e = launch_placed_ka(h, (char*)a.gram + align_up((size_t)kvc::kRelaxMaxFrames * kvc::kRelaxMaxFrames * 4),
+                         &a.keys);
+  if (e == hipSuccess) e = kvc::launch_relax(a, h->stream);
   return device_result(h, e, "relax scores");
 }
 

@@ -281,10 +281,11 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
   __shared__ int s_dl[32];
   __shared__ int s_tn[32];
   const int tid = threadIdx.x;
+  const bool placed = a.out_ka[0] != nullptr;      // out of place, by each slot's absolute time
   if (tid < ns) {
     const int t = R.t[s0 + tid];
     const int tn = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
-    s_dl[tid] = tn - t;
+    s_dl[tid] = placed ? t : tn - t;
     s_tn[tid] = tn;
   }
   __syncthreads();
@@ -300,6 +301,7 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
       cs[q][1] = d < DT ? tp[d + 1] : 0.f;
     }
     T* base = (T*)R.ka + ((int64_t)s0 + j) * (CA * E) + c * E;
+    T* obase = placed ? (T*)a.out_ka[rg.region] + ((int64_t)s0 + j) * (CA * E) + c * E : base;
     const int64_t hstride = (int64_t)R.cap * (CA * E);
     for (int h0 = 0; h0 < g.H; h0 += HU) {
       Vec16<T> x[HU];
@@ -317,10 +319,11 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
           if (c * E + 2 * q < DT) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
 #pragma unroll
         for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
-        *reinterpret_cast<uint4*>(base + (h0 + u) * hstride) = x[u].u;
+        *reinterpret_cast<uint4*>(obase + (h0 + u) * hstride) = x[u].u;
       }
     }
   }
+  if (placed) return;
   __syncthreads();
   if (tid < ns) R.t[s0 + tid] = s_tn[tid];
 }

@@ -34,6 +34,8 @@ def _drive(w, n_chunks=None, full_attention=True, compact=False, general=False, 
             kw["keep_override"] = drv.last["keep"]
         if w.name.startswith("c5b"):
             ref = run.step(i, q, k, v, q_prev=q_prev, f64=w.dtype == "f32", **kw)
+        elif w.name.startswith("c5c"):
+            ref = run.step(i, q, k, v, f64=w.dtype == "f32", **kw)
         else:
             ref = run.step(i, q, k, v, f64=w.dtype == "f32")
         assert_state_equal(gc, run.cache, w, f"{w.name} chunk {i}")
@@ -402,12 +404,11 @@ def test_raw_keys_negative_times_and_block_causal():
     assert_state_equal(gc, oc, w, "raw after negative shift")
     (q2,) = chunk_inputs(w, 96, tensors=(0,), frames=2)
     check_attention(gc.attend(dev(q2, w), -24).float().cpu().numpy(), oc.attend(q2, 2, -24), "raw negative t")
-    with pytest.raises(KVCError) as e:
-        gc.score(dev(q2, w), [-24, -23])
-    assert e.value.code == 5
-    with pytest.raises(KVCError) as e:
-        gc.relax_scores(2)
-    assert e.value.code == 5
+    # scores and Relax scores see the keys placed at their (negative) times
+    got = gc.score(dev(q2, w), [-24, -23]).cpu().numpy()
+    ref = oc.score(q2, 2, [-24, -23])
+    assert np.max(np.abs(got - ref)) <= 1e-4 * ref.max()
+    assert np.max(np.abs(gc.relax_scores(2).cpu().numpy() - oc.relax_scores(2))) <= RELAX_TOL
 
 
 # ---------------------------------------------------------------- MemRoPE memory tokens
@@ -698,3 +699,13 @@ def test_split_key_attention_flush_and_retime():
     base = WORKLOADS["c5a"]
     _drive(Workload("c5a_split", 224, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
                     (3,) * 14 + (2,), cut_chunks=(7, 11)), compact=True, split=True)
+
+
+@pytest.mark.parametrize("name", ["c5b", "c5c"])
+def test_raw_keys_deep_and_relax_forcing(name):
+    """Deep Forcing (attention-mass scores, compaction, gap-closing retimes) and Relax Forcing on raw-key
+    caches: the scores read the keys placed at their current times; state bit-exact, attention against the
+    oracle."""
+    base = WORKLOADS[name]
+    _drive(Workload(name + "_small", 225, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames, (3,) * 16,
+                    raw_keys=True), compact=True)
