@@ -709,3 +709,34 @@ def test_raw_keys_deep_and_relax_forcing(name):
     base = WORKLOADS[name]
     _drive(Workload(name + "_small", 225, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames, (3,) * 16,
                     raw_keys=True), compact=True)
+
+
+def test_split_keys_with_limit_and_memory():
+    """Split-key launches over ranges that start inside a tile (attention limit) and over the memory slots
+    of a MemRoPE cache."""
+    w = _replace(SMALL_SW, name="split_lim")
+    gc = new_cache(w, split=True)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(w.n_chunks):
+        q, k, v = chunk_inputs(w, i)
+        t0 = w.chunk_start_frame(i)
+        gc.append(dev(k, w), dev(v, w), t0)
+        oc.append(k, v, w.chunk_frames[i], t0)
+        n = oc.n
+        m = max(1, n - 150)
+        gc.set_attention_limit(m)
+        out = gc.attend(dev(q, w), t0).float().cpu().numpy()
+        check_attention(out, oc.attend(q, w.chunk_frames[i], t0, max_keys=m), f"split limit chunk {i}")
+        gc.set_attention_limit(0)
+    wm = _replace(MEM_SMALL, name="split_mem")
+    gm = new_cache(wm, split=True)
+    om = OracleCache(wm.sink_frames, wm.window_frames, wm.frame_seqlen, wm.heads, wm.head_dim, wm.grid_w, wm.dtype,
+                     raw_keys=True, memory=wm.memory)
+    for i in range(wm.n_chunks):
+        q, k, v = chunk_inputs(wm, i)
+        t0 = wm.chunk_start_frame(i)
+        gm.append(dev(k, wm), dev(v, wm), t0)
+        om.append(k, v, wm.chunk_frames[i], t0)
+        out = gm.attend(dev(q, wm), t0).float().cpu().numpy()
+        check_attention(out, om.attend(q, wm.chunk_frames[i], t0), f"split memory chunk {i}")
+    assert om.mem_frames > 0
