@@ -178,7 +178,10 @@ kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
  * bank_tokens, raw k/v are also captured into the bank.
  * flags: KVC_APPEND_REPLACE_NEWEST re-writes the newest chunk in place (its
  * frame count must match).  EINVAL if n_frames*frame_seqlen exceeds the
- * window, or |t_index|+n_frames exceeds KVC_MAX_POS. */
+ * window, or |t_index|+n_frames exceeds KVC_MAX_POS.  k and v must be
+ * finite: attention weights the unused slots of a partial key tile by exactly
+ * zero, so a non-finite value left in a slot after its entry was dropped by a
+ * compaction can still reach a later attend's output. */
 kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_frames, int32_t t_index,
                       uint32_t flags);
 

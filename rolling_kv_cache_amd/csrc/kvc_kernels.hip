@@ -424,6 +424,12 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   __shared__ uint4 s_dst[TE * sizeof(T) / 16];
   __shared__ int s_idx[kTile];
   if (tid < kTile) s_idx[tid] = tid < nn ? a.idx[j0 + tid] : INT32_MAX;
+  // slots past n in a partial tile are written as zeros: attention reads whole
+  // tiles and weights those slots by exactly 0, which needs finite values
+  // (uninitialised LDS can hold Inf/NaN patterns).  These columns are disjoint
+  // from the gathered ones; the run loop below synchronizes at least once.
+  if (nn < kTile && tid % kTile >= nn)
+    for (int d = tid / kTile; d < D; d += 256 / kTile) ((T*)s_dst)[d * kTile + tid % kTile] = T(0);
   __syncthreads();
   const T* vsrc = (const T*)a.src.v + (size_t)h * (a.src.cap / kTile) * TE;
   T* sdst = (T*)s_dst;
@@ -449,8 +455,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     __syncthreads();
     q = qe;
   }
-  // the destination tile as full rows (slots past n in a partial tile hold
-  // stale data; they are outside the valid prefix and never read)
+  // the destination tile as full rows (slots past n in a partial tile: zeros)
   uint4* dp = reinterpret_cast<uint4*>((T*)a.dst.v + ((size_t)h * (a.dst.cap / kTile) + dt) * TE);
 #pragma unroll
   for (int i = 0; i < PER; ++i) dp[tid + 256 * i] = s_dst[tid + 256 * i];

@@ -740,3 +740,98 @@ def test_split_keys_with_limit_and_memory():
         out = gm.attend(dev(q, wm), t0).float().cpu().numpy()
         check_attention(out, om.attend(q, wm.chunk_frames[i], t0), f"split memory chunk {i}")
     assert om.mem_frames > 0
+
+
+# ---------------------------------------------------------------- seeded random operation sequences
+@pytest.mark.parametrize("seed,raw", [(1, False), (2, False), (3, True), (4, True)])
+def test_random_operation_sequences(seed, raw):
+    """80 seeded random operations on a small cache (sink 2 + window 5 frames of 24 tokens, 4-frame bank,
+    compaction buffer): appends and newest-chunk re-writes, retimes of random ranges with and without clamp,
+    random compactions, sink pushes, attends at random times with random limits.  Every operation goes to the
+    oracle first; where it refuses, the library must refuse too and keep its state; after every operation the
+    cache states are equal bit for bit and every attend agrees."""
+    from oracle import OracleError
+    from rolling_kv_cache_amd import KVCError
+    w = Workload(f"rand{seed}", 230 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw)
+    S = w.frame_seqlen
+    gc = new_cache(w, compact=True)
+    oc = OracleCache(w.sink_frames, w.window_frames, S, w.heads, w.head_dim, w.grid_w, w.dtype, w.bank_frames,
+                     raw_keys=raw)
+    rng = np.random.default_rng(seed)
+    t_next, last_F, uid, pushed, attended, refused = 0, None, 0, False, 0, 0
+    for step in range(80):
+        op = rng.choice(["append", "append", "replace", "retime", "compact", "push", "attend", "attend"])
+        uid += 1
+        tag = f"seed {seed} step {step} {op}"
+        if op in ("append", "replace"):
+            F = int(rng.integers(1, 3)) if op == "append" else (last_F or 1)
+            _, k, v = chunk_inputs(w, 100 + uid, frames=F)
+            t0 = t_next if op == "append" else max(0, t_next - F)
+            args_o, args_g = (k, v, F, t0), (dev(k, w), dev(v, w), t0)
+            kw_o = {"replace_newest": op == "replace"}
+            call_o = lambda: oc.append(*args_o, **kw_o)
+            call_g = lambda: gc.append(*args_g, replace_newest=op == "replace")
+        elif op == "retime":
+            n = oc.n
+            lo = int(rng.integers(0, n + 1)) if n else 0
+            hi = int(rng.integers(lo, n + 1)) if n else 0
+            d, cl = int(rng.integers(-5, 6)), bool(rng.integers(0, 2))
+            call_o = lambda: oc.retime(d, cl, lo, hi)
+            call_g = lambda: gc.retime(d, cl, lo, hi)
+        elif op == "compact":
+            n, ns = oc.n, oc.n_sink
+            extra = np.zeros(0, np.int64)
+            if n > ns:
+                extra = np.sort(rng.choice(np.arange(ns, n), size=int(rng.integers(0, n - ns + 1)), replace=False))
+            keep = np.concatenate([np.arange(ns), extra]).astype(np.int64)
+            if keep.shape[0] == 0:
+                continue
+            call_o = lambda: oc.compact(keep)
+            call_g = lambda: gc.compact(keep)
+        elif op == "push":
+            b, F = int(rng.integers(0, 4)), int(rng.integers(1, 3))
+            t0 = int(rng.integers(0, 20))
+            call_o = lambda: oc.sink_push(b, F, t0)
+            call_g = lambda: gc.sink_push(b, F, t0)
+        else:
+            if oc.n == 0:
+                continue
+            F = int(rng.integers(1, 3))
+            (q,) = chunk_inputs(w, 500 + uid, tensors=(0,), frames=F)
+            t0 = int(rng.integers(-8, 30))
+            m = int(rng.integers(1, oc.n + 1)) if rng.integers(0, 3) == 0 else 0
+            gc.set_attention_limit(m)
+            try:
+                out = gc.attend(dev(q, w), t0).float().cpu().numpy()
+            except KVCError as e:
+                # documented refusal: a limit whose visible entries span a sink that has rolled
+                assert m and e.code == 5 and pushed, (tag, str(e))
+                refused += 1
+                continue
+            finally:
+                gc.set_attention_limit(0)
+            check_attention(out, oc.attend(q, F, t0, max_keys=m or None), tag)
+            attended += 1
+            continue
+        try:
+            call_o()
+            ok = True
+        except OracleError:
+            ok = False
+        if ok:
+            call_g()
+            if op == "append":
+                t_next, last_F = t0 + F, F
+            elif op == "compact" and oc.newest is None:
+                last_F = None
+            elif op == "push":
+                pushed = True
+        else:
+            before = gc.info()
+            with pytest.raises(KVCError):
+                call_g()
+            assert gc.info() == before, tag
+        if oc.n:
+            assert_state_equal(gc, oc, w, tag)
+    log(f"  seed {seed}: {attended} attends, {refused} limited attends refused")
+    assert attended >= 10
