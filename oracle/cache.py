@@ -253,6 +253,8 @@ class OracleCache:
         """Rolling-Sink sink FIFO step: drop the oldest `frames` sink frames, append bank frames
         [bank_frame, bank_frame+frames) freshly rotated at times t0 .. t0+frames-1."""
         N = frames * self.S
+        if self.memory is not None:
+            raise OracleError("sink push is not defined with memory tokens")
         if self.bank_tok == 0 or self.global_end < self.bank_tok:
             raise OracleError("bank incomplete")
         if self.n_sink != self.S_tok or N > self.S_tok:
@@ -314,6 +316,8 @@ class OracleCache:
         blocks 0..that block, i.e. to the first min(n, (block + 1) * block_frames * S) entries in logical
         order; there is no mask inside a block.
         """
+        if self.memory is not None:
+            raise OracleError("block-causal attention is not defined with memory tokens")
         qh = self.rotate_queries(q, frames, t0)
         N = frames * self.S
         rows = np.arange(N) if rows is None else np.asarray(rows)

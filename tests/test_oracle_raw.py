@@ -172,6 +172,8 @@ def test_memory_follows_uniform_shift():
 
 
 def test_memory_needs_raw_keys_and_refuses_compaction():
+    """MemRoPE memory is defined on a raw-key cache only, and not together with compaction, a
+    Rolling-Sink push or block-causal attention (none of those pages combine them with memory)."""
     from oracle import OracleError
     import pytest as _pt
     with _pt.raises(OracleError):
@@ -179,3 +181,8 @@ def test_memory_needs_raw_keys_and_refuses_compaction():
     c, _, _ = _mem_cache((0.9, 0.5), 6)
     with _pt.raises(OracleError):
         c.compact(np.arange(c.n))
+    with _pt.raises(OracleError):
+        c.sink_push(0, 1, 0)
+    q = np.zeros((c.S, c.H, c.D), np.float32)
+    with _pt.raises(OracleError):
+        c.attend_block_causal(q, 1, 0, 1)
