@@ -244,9 +244,10 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
  * last max_attention_size positions of the cache buffer, sink first), i.e. the
  * oldest entries -- the sink first once the limit is below the window's
  * length -- drop out of attention without leaving the cache.  0 (the default)
- * = no limit.  EINVAL if max_keys < 0.  A limited attend returns
- * KVC_EUNSUPPORTED when the visible entries span a Rolling-Sink sink that has
- * rolled, with memory tokens, or for block-causal attention. */
+ * = no limit.  EINVAL if max_keys < 0.  A limited attend (max_keys below the
+ * number of entries) returns KVC_EUNSUPPORTED when the visible entries span a
+ * Rolling-Sink sink that has rolled, on a KVC_CREATE_MEMORY cache (before its
+ * first fold too), or for block-causal attention. */
 kvc_status kvc_set_attention_limit(kvc_handle h, int32_t max_keys);
 
 /* Memory-token rates (KVC_CREATE_MEMORY caches): alpha_long for the long

@@ -538,8 +538,7 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
     // only the newest max_keys entries in logical order: at most two physical ranges (a window suffix
     // that wraps, or a sink tail plus the whole window) when the sink ring has not rolled
     if (causal_block > 0) return fail(KVC_EUNSUPPORTED, "block-causal attention with an attention limit");
-    if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0)
-      return fail(KVC_EUNSUPPORTED, "memory tokens with an attention limit");
+    if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "memory tokens with an attention limit");
     // per region: the whole valid prefix when all of it is visible (key order does not matter),
     // else the physical ranges of its visible logical suffix
     const int32_t lo = n_valid - h->max_keys, ns = h->st.ns;

@@ -743,34 +743,41 @@ def test_split_keys_with_limit_and_memory():
 
 
 # ---------------------------------------------------------------- seeded random operation sequences
-@pytest.mark.parametrize("seed,raw", [(1, False), (2, False), (3, True), (4, True)])
-def test_random_operation_sequences(seed, raw):
+RANDOM_CASES = [  # seed, raw keys, memory tokens, split-key attention
+    (1, False, False, False), (2, False, False, False), (3, True, False, False), (4, True, False, False),
+    (5, True, True, False), (6, True, True, True), (7, False, False, True), (8, True, False, True),
+]
+
+
+@pytest.mark.parametrize("seed,raw,memory,split", RANDOM_CASES)
+def test_random_operation_sequences(seed, raw, memory, split):
     """80 seeded random operations on a small cache (sink 2 + window 5 frames of 24 tokens, 4-frame bank,
     compaction buffer): appends and newest-chunk re-writes, retimes of random ranges with and without clamp,
-    random compactions, sink pushes, attends at random times with random limits.  Every operation goes to the
-    oracle first; where it refuses, the library must refuse too and keep its state; after every operation the
-    cache states are equal bit for bit and every attend agrees."""
+    random compactions, sink pushes, memory-rate changes, attends at random times with random limits.  Every
+    operation goes to the oracle first; where it refuses, the library must refuse too and keep its state; after
+    every operation the cache states (and memory tokens) are equal bit for bit, and every attend agrees.  The
+    library may also refuse a limited attend whose visible entries span a rolled sink (documented)."""
     from oracle import OracleError
     from rolling_kv_cache_amd import KVCError
-    w = Workload(f"rand{seed}", 230 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw)
-    S = w.frame_seqlen
-    gc = new_cache(w, compact=True)
-    oc = OracleCache(w.sink_frames, w.window_frames, S, w.heads, w.head_dim, w.grid_w, w.dtype, w.bank_frames,
-                     raw_keys=raw)
+    w = Workload(f"rand{seed}", 230 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw,
+                 memory=(0.9, 0.5) if memory else None)
+    gc = new_cache(w, compact=True, split=split)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                     w.bank_frames, raw_keys=raw, memory=w.memory)
     rng = np.random.default_rng(seed)
+    ops = ["append", "append", "replace", "retime", "compact", "push", "attend", "attend"] + (["rates"] if memory else [])
     t_next, last_F, uid, pushed, attended, refused = 0, None, 0, False, 0, 0
     for step in range(80):
-        op = rng.choice(["append", "append", "replace", "retime", "compact", "push", "attend", "attend"])
+        op = str(rng.choice(ops))
         uid += 1
         tag = f"seed {seed} step {step} {op}"
         if op in ("append", "replace"):
             F = int(rng.integers(1, 3)) if op == "append" else (last_F or 1)
             _, k, v = chunk_inputs(w, 100 + uid, frames=F)
             t0 = t_next if op == "append" else max(0, t_next - F)
-            args_o, args_g = (k, v, F, t0), (dev(k, w), dev(v, w), t0)
-            kw_o = {"replace_newest": op == "replace"}
-            call_o = lambda: oc.append(*args_o, **kw_o)
-            call_g = lambda: gc.append(*args_g, replace_newest=op == "replace")
+            kd, vd, rep = dev(k, w), dev(v, w), op == "replace"
+            call_o = lambda: oc.append(k, v, F, t0, replace_newest=rep)
+            call_g = lambda: gc.append(kd, vd, t0, replace_newest=rep)
         elif op == "retime":
             n = oc.n
             lo = int(rng.integers(0, n + 1)) if n else 0
@@ -793,6 +800,12 @@ def test_random_operation_sequences(seed, raw):
             t0 = int(rng.integers(0, 20))
             call_o = lambda: oc.sink_push(b, F, t0)
             call_g = lambda: gc.sink_push(b, F, t0)
+        elif op == "rates":
+            al, ash = (float(x) for x in rng.choice([0.0, 0.25, 0.5, 0.9, 1.0], size=2))
+
+            def call_o():
+                oc.memory = (al, ash)
+            call_g = lambda: gc.set_memory_rates(al, ash)
         else:
             if oc.n == 0:
                 continue
@@ -800,17 +813,22 @@ def test_random_operation_sequences(seed, raw):
             (q,) = chunk_inputs(w, 500 + uid, tensors=(0,), frames=F)
             t0 = int(rng.integers(-8, 30))
             m = int(rng.integers(1, oc.n + 1)) if rng.integers(0, 3) == 0 else 0
+            try:
+                ref = oc.attend(q, F, t0, max_keys=m or None)
+            except OracleError:
+                ref = None
             gc.set_attention_limit(m)
             try:
                 out = gc.attend(dev(q, w), t0).float().cpu().numpy()
             except KVCError as e:
-                # documented refusal: a limit whose visible entries span a sink that has rolled
-                assert m and e.code == 5 and pushed, (tag, str(e))
+                # the oracle's refusal, or the documented one: a limit whose visible entries span a rolled sink
+                assert ref is None or (m and e.code == 5 and pushed), (tag, str(e))
                 refused += 1
                 continue
             finally:
                 gc.set_attention_limit(0)
-            check_attention(out, oc.attend(q, F, t0, max_keys=m or None), tag)
+            assert ref is not None, f"{tag}: the oracle refuses, the library attends"
+            check_attention(out, ref, tag)
             attended += 1
             continue
         try:
@@ -833,5 +851,7 @@ def test_random_operation_sequences(seed, raw):
             assert gc.info() == before, tag
         if oc.n:
             assert_state_equal(gc, oc, w, tag)
-    log(f"  seed {seed}: {attended} attends, {refused} limited attends refused")
+        if memory:
+            _check_memory(gc, oc, w, tag)
+    log(f"  seed {seed}: {attended} attends, {refused} refused")
     assert attended >= 10
