@@ -600,6 +600,7 @@ kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames,
                                   int32_t block_frames, void* out) {
   if (kvc_status s = check(h)) return s;
   if (block_frames < 1 || block_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "block_frames out of range");
+  if (h->cflags & KVC_CREATE_MEMORY) return fail(KVC_EUNSUPPORTED, "block-causal attention with memory tokens");
   // key prefixes are taken in logical order, which must coincide with slot order
   if (h->st.hs != 0 || h->st.hw != 0)
     return fail(KVC_EUNSUPPORTED, "block-causal attention needs an unrolled cache (sink and window heads at 0)");

@@ -753,10 +753,12 @@ RANDOM_CASES = [  # seed, raw keys, memory tokens, split-key attention
 def test_random_operation_sequences(seed, raw, memory, split):
     """80 seeded random operations on a small cache (sink 2 + window 5 frames of 24 tokens, 4-frame bank,
     compaction buffer): appends and newest-chunk re-writes, retimes of random ranges with and without clamp,
-    random compactions, sink pushes, memory-rate changes, attends at random times with random limits.  Every
+    random compactions, sink pushes, memory-rate changes, attends at random times with random limits and
+    block-causal attends.  Every
     operation goes to the oracle first; where it refuses, the library must refuse too and keep its state; after
     every operation the cache states (and memory tokens) are equal bit for bit, and every attend agrees.  The
-    library may also refuse a limited attend whose visible entries span a rolled sink (documented)."""
+    library also refuses, as documented, a limited attend whose visible entries span a rolled sink and a
+    block-causal attend once a ring has rolled."""
     from oracle import OracleError
     from rolling_kv_cache_amd import KVCError
     w = Workload(f"rand{seed}", 230 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw,
@@ -765,7 +767,8 @@ def test_random_operation_sequences(seed, raw, memory, split):
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
                      w.bank_frames, raw_keys=raw, memory=w.memory)
     rng = np.random.default_rng(seed)
-    ops = ["append", "append", "replace", "retime", "compact", "push", "attend", "attend"] + (["rates"] if memory else [])
+    ops = ["append", "append", "replace", "retime", "compact", "push", "attend", "attend", "bcausal"] + \
+        (["rates"] if memory else [])
     t_next, last_F, uid, pushed, attended, refused = 0, None, 0, False, 0, 0
     for step in range(80):
         op = str(rng.choice(ops))
@@ -806,6 +809,28 @@ def test_random_operation_sequences(seed, raw, memory, split):
             def call_o():
                 oc.memory = (al, ash)
             call_g = lambda: gc.set_memory_rates(al, ash)
+        elif op == "bcausal":
+            if oc.n == 0:
+                continue
+            F, bf, t0 = int(rng.integers(1, 4)), int(rng.integers(1, 3)), int(rng.integers(0, 10))
+            (q,) = chunk_inputs(w, 500 + uid, tensors=(0,), frames=F)
+            try:
+                ref = oc.attend_block_causal(q, F, t0, bf)
+            except OracleError:
+                ref = None
+            inf = gc.info()
+            rolled = inf["sink_head"] != 0 or inf["window_head"] != 0
+            try:
+                out = gc.attend_block_causal(dev(q, w), t0, bf).float().cpu().numpy()
+            except KVCError as e:
+                # the oracle's refusal, or the documented one: logical order no longer equals slot order
+                assert ref is None or (rolled and e.code == 5), (tag, str(e))
+                refused += 1
+                continue
+            assert ref is not None and not rolled, f"{tag}: attended where a refusal is due"
+            check_attention(out, ref, tag)
+            attended += 1
+            continue
         else:
             if oc.n == 0:
                 continue
@@ -854,4 +879,110 @@ def test_random_operation_sequences(seed, raw, memory, split):
         if memory:
             _check_memory(gc, oc, w, tag)
     log(f"  seed {seed}: {attended} attends, {refused} refused")
-    assert attended >= 10
+    assert attended >= (5 if memory else 10)     # memory caches refuse limited and block-causal attends
+
+
+@pytest.mark.parametrize("seed,raw", [(11, False), (12, True)])
+def test_random_layer_group_sequences(seed, raw):
+    """60 seeded random operations on a three-layer group (same small geometry as above): per-layer appends,
+    re-writes and attends with each layer's own data; retimes, compactions and sink pushes as batched calls
+    over a random run of consecutive layers, followed by the same call over the other layers.  While the
+    layers differ, a batched call over the whole group must be refused with its state kept (ESTATE).  Every
+    layer's state against its own oracle after every step."""
+    from oracle import OracleError
+    from rolling_kv_cache_amd import KVCError, compact_layers, retime_layers, sink_push_layers
+    L = 3
+    w = Workload(f"grp{seed}", 250 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw)
+    caches = _group(w, L, compact=True)
+    ocs = [OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                       w.bank_frames, raw_keys=raw) for _ in range(L)]
+    rng = np.random.default_rng(seed)
+    t_next, last_F, uid, attended, batched = 0, None, 0, 0, 0
+    for step in range(60):
+        op = str(rng.choice(["append", "append", "replace", "retime", "retime", "compact", "push", "attend"]))
+        uid += 1
+        tag = f"seed {seed} step {step} {op}"
+        oc0 = ocs[0]
+        if op in ("append", "replace"):
+            F = int(rng.integers(1, 3)) if op == "append" else (last_F or 1)
+            t0 = t_next if op == "append" else max(0, t_next - F)
+            rep = op == "replace"
+            try:
+                for li in range(L):
+                    _, k, v = chunk_inputs(w, 1000 * li + uid, frames=F)
+                    ocs[li].append(k, v, F, t0, replace_newest=rep)
+                    caches[li].append(dev(k, w), dev(v, w), t0, replace_newest=rep)
+            except OracleError:
+                assert li == 0, tag
+                with pytest.raises(KVCError):
+                    caches[0].append(dev(k, w), dev(v, w), t0, replace_newest=rep)
+            else:
+                if op == "append":
+                    t_next, last_F = t0 + F, F
+        elif op == "attend":
+            if oc0.n == 0:
+                continue
+            li, F, t0 = int(rng.integers(0, L)), int(rng.integers(1, 3)), int(rng.integers(-8, 30))
+            (q,) = chunk_inputs(w, 5000 + uid, tensors=(0,), frames=F)
+            out = caches[li].attend(dev(q, w), t0).float().cpu().numpy()
+            check_attention(out, ocs[li].attend(q, F, t0), f"{tag} layer {li}")
+            attended += 1
+            continue
+        else:
+            if op == "retime":
+                n = oc0.n
+                lo = int(rng.integers(0, n + 1)) if n else 0
+                hi = int(rng.integers(lo, n + 1)) if n else 0
+                d, cl = int(rng.integers(-5, 6)), bool(rng.integers(0, 2))
+                do_o = lambda c: c.retime(d, cl, lo, hi)
+                do_g = lambda cs: retime_layers(cs, d, cl, lo, hi)
+            elif op == "compact":
+                n, ns = oc0.n, oc0.n_sink
+                extra = np.zeros(0, np.int64)
+                if n > ns:
+                    extra = np.sort(rng.choice(np.arange(ns, n), size=int(rng.integers(0, n - ns + 1)),
+                                               replace=False))
+                keep = np.concatenate([np.arange(ns), extra]).astype(np.int64)
+                if keep.shape[0] == 0:
+                    continue
+                do_o = lambda c: c.compact(keep)
+                do_g = lambda cs: compact_layers(cs, keep)
+            else:
+                b, F, t0 = int(rng.integers(0, 4)), int(rng.integers(1, 3)), int(rng.integers(0, 20))
+                do_o = lambda c: c.sink_push(b, F, t0)
+                do_g = lambda cs: sink_push_layers(cs, b, F, t0)
+            try:
+                do_o(ocs[0])
+            except OracleError:
+                before = caches[0].info()
+                with pytest.raises(KVCError):
+                    do_g(caches)
+                assert caches[0].info() == before, tag
+            else:
+                for c in ocs[1:]:
+                    do_o(c)
+                a = int(rng.integers(0, L))
+                e = int(rng.integers(a + 1, L + 1))
+                do_g(caches[a:e])
+                batched += 1
+                if (a, e) != (0, L):
+                    t_a, g_a = caches[a].slot_times()
+                    t_o, g_o = caches[0 if a > 0 else L - 1].slot_times()
+                    if caches[a].info() != caches[0 if a > 0 else L - 1].info() or not (
+                            np.array_equal(t_a, t_o) and np.array_equal(g_a, g_o)):
+                        before = [c.info() for c in caches]
+                        with pytest.raises(KVCError) as ex:
+                            do_g(caches)
+                        assert ex.value.code == 3, tag
+                        assert [c.info() for c in caches] == before, tag
+                    if a > 0:
+                        do_g(caches[:a])
+                    if e < L:
+                        do_g(caches[e:])
+                if op == "compact" and oc0.newest is None:
+                    last_F = None
+        for li in range(L):
+            if ocs[li].n:
+                assert_state_equal(caches[li], ocs[li], w, f"{tag} layer {li}")
+    log(f"  seed {seed}: {attended} attends, {batched} batched calls")
+    assert attended >= 5 and batched >= 10
