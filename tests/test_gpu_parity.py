@@ -743,25 +743,29 @@ def test_split_keys_with_limit_and_memory():
 
 
 # ---------------------------------------------------------------- seeded random operation sequences
-RANDOM_CASES = [  # seed, raw keys, memory tokens, split-key attention
-    (1, False, False, False), (2, False, False, False), (3, True, False, False), (4, True, False, False),
-    (5, True, True, False), (6, True, True, True), (7, False, False, True), (8, True, False, True),
+RANDOM_CASES = [  # seed, raw keys, memory tokens, split-key attention, dtype, head_dim
+    (1, False, False, False, "bf16", 128), (2, False, False, False, "bf16", 128),
+    (3, True, False, False, "bf16", 128), (4, True, False, False, "bf16", 128),
+    (5, True, True, False, "bf16", 128), (6, True, True, True, "bf16", 128),
+    (7, False, False, True, "bf16", 128), (8, True, False, True, "bf16", 128),
+    (9, False, False, False, "f32", 128), (10, True, True, False, "f32", 64),
+    (13, False, False, False, "bf16", 64), (14, True, False, False, "bf16", 64),
 ]
 
 
-@pytest.mark.parametrize("seed,raw,memory,split", RANDOM_CASES)
-def test_random_operation_sequences(seed, raw, memory, split):
+@pytest.mark.parametrize("seed,raw,memory,split,dtype,head_dim", RANDOM_CASES)
+def test_random_operation_sequences(seed, raw, memory, split, dtype, head_dim):
     """80 seeded random operations on a small cache (sink 2 + window 5 frames of 24 tokens, 4-frame bank,
-    compaction buffer): appends and newest-chunk re-writes, retimes of random ranges with and without clamp,
-    random compactions, sink pushes, memory-rate changes, attends at random times with random limits and
-    block-causal attends.  Every
-    operation goes to the oracle first; where it refuses, the library must refuse too and keep its state; after
-    every operation the cache states (and memory tokens) are equal bit for bit, and every attend agrees.  The
-    library also refuses, as documented, a limited attend whose visible entries span a rolled sink and a
-    block-causal attend once a ring has rolled."""
+    compaction buffer; bf16 or fp32, head_dim 128 or 64): appends and newest-chunk re-writes, retimes of
+    random ranges with and without clamp, random compactions, sink pushes, memory-rate changes, attends at
+    random times with random limits and block-causal attends.  Every operation goes to the oracle first;
+    where it refuses, the library must refuse too and keep its state; after every operation the cache states
+    (and memory tokens) are equal bit for bit, and every attend agrees.  The library also refuses, as
+    documented, a limited attend whose visible entries span a rolled sink and a block-causal attend once a
+    ring has rolled."""
     from oracle import OracleError
     from rolling_kv_cache_amd import KVCError
-    w = Workload(f"rand{seed}", 230 + seed, 2, 128, "bf16", 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw,
+    w = Workload(f"rand{seed}", 230 + seed, 2, head_dim, dtype, 4, 6, 2, 5, (1,), bank_frames=4, raw_keys=raw,
                  memory=(0.9, 0.5) if memory else None)
     gc = new_cache(w, compact=True, split=split)
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
