@@ -758,7 +758,8 @@ def test_random_operation_sequences(seed, raw, memory, split, dtype, head_dim):
     """80 seeded random operations on a small cache (sink 2 + window 5 frames of 24 tokens, 4-frame bank,
     compaction buffer; bf16 or fp32, head_dim 128 or 64): appends and newest-chunk re-writes, retimes of
     random ranges with and without clamp, random compactions, sink pushes, memory-rate changes, attends at
-    random times with random limits and block-causal attends.  Every operation goes to the oracle first;
+    random times with random limits, block-causal attends, attention-mass scores and Relax Forcing frame
+    scores.  Every operation goes to the oracle first;
     where it refuses, the library must refuse too and keep its state; after every operation the cache states
     (and memory tokens) are equal bit for bit, and every attend agrees.  The library also refuses, as
     documented, a limited attend whose visible entries span a rolled sink and a block-causal attend once a
@@ -771,9 +772,9 @@ def test_random_operation_sequences(seed, raw, memory, split, dtype, head_dim):
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
                      w.bank_frames, raw_keys=raw, memory=w.memory)
     rng = np.random.default_rng(seed)
-    ops = ["append", "append", "replace", "retime", "compact", "push", "attend", "attend", "bcausal"] + \
-        (["rates"] if memory else [])
-    t_next, last_F, uid, pushed, attended, refused = 0, None, 0, False, 0, 0
+    ops = ["append", "append", "replace", "retime", "compact", "push", "attend", "attend", "bcausal", "score",
+           "relax"] + (["rates"] if memory else [])
+    t_next, last_F, uid, pushed, attended, refused, scored = 0, None, 0, False, 0, 0, 0
     for step in range(80):
         op = str(rng.choice(ops))
         uid += 1
@@ -813,6 +814,30 @@ def test_random_operation_sequences(seed, raw, memory, split, dtype, head_dim):
             def call_o():
                 oc.memory = (al, ash)
             call_g = lambda: gc.set_memory_rates(al, ash)
+        elif op == "score":
+            if oc.n == 0:
+                continue
+            F = int(rng.integers(1, 3))
+            qt = [int(x) for x in rng.integers(-8, 30, size=F)]
+            (q,) = chunk_inputs(w, 700 + uid, tensors=(0,), frames=F)
+            got = gc.score(dev(q, w), qt).cpu().numpy().astype(np.float64)
+            ref = oc.score(q, F, qt, f64=True)
+            assert np.max(np.abs(got - ref)) <= 1e-4 * max(1.0, ref.max()), tag
+            scored += 1
+            continue
+        elif op == "relax":
+            tail, wt = int(rng.integers(1, 4)), float(rng.choice([0.0, 0.3, 0.5, 1.0]))
+            try:
+                ref = oc.relax_scores(tail, wt)
+            except OracleError:
+                ref = None
+            if ref is None:
+                with pytest.raises(KVCError):
+                    gc.relax_scores(tail, wt)
+            else:
+                assert np.max(np.abs(gc.relax_scores(tail, wt).cpu().numpy() - ref)) <= RELAX_TOL, tag
+                scored += 1
+            continue
         elif op == "bcausal":
             if oc.n == 0:
                 continue
@@ -882,8 +907,8 @@ def test_random_operation_sequences(seed, raw, memory, split, dtype, head_dim):
             assert_state_equal(gc, oc, w, tag)
         if memory:
             _check_memory(gc, oc, w, tag)
-    log(f"  seed {seed}: {attended} attends, {refused} refused")
-    assert attended >= (5 if memory else 10)     # memory caches refuse limited and block-causal attends
+    log(f"  seed {seed}: {attended} attends, {refused} refused, {scored} scores")
+    assert attended >= 5 and attended + scored >= 10
 
 
 @pytest.mark.parametrize("seed,raw", [(11, False), (12, True)])
