@@ -210,7 +210,9 @@ def main():
         "kernels": {
             "attend_ms": round(att_avg, 4),
             "attend_tflops": round(att_tflops, 2),
+            "attend_ms_p10_median_p90": [round(float(x), 4) for x in np.percentile(att_ms, [10, 50, 90])],
             "append_us_warm": round(app_avg * 1e3, 2),
+            "append_us_warm_p10_median_p90": [round(float(x) * 1e3, 2) for x in np.percentile(app_ms, [10, 50, 90])],
             "append_GBps_warm": round(app_bytes / (app_avg * 1e-3) / 1e9, 1),
             "append_us_cold": round(float(np.mean(app_cold)) * 1e3, 2),
             "append_GBps_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9, 1),
