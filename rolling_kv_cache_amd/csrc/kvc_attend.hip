@@ -570,12 +570,16 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   __shared__ u32x4_t lks[2][kKTileP];
   __shared__ u32x4_t lvs[2][kVTileP];
   const int wg = blockIdx.x;
-  const int lin = (wg & 7) * per_xcd + (wg >> 3);
+  // block-causal work per query block grows with the block index: the units are taken longest first,
+  // heads minor, one per workgroup in dispatch order, which deals them round-robin over the XCDs, so
+  // every XCD gets an equal longest-first share (a contiguous range per XCD would give one XCD the heavy
+  // half of a head and another its light half)
+  const int lin = CAUSAL ? wg : (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
   if (only_flagged != nullptr && only_flagged[lin] == 0) return;
-  const int hp = lin / mblocks;                         // head * kparts + part
+  const int hp = CAUSAL ? lin % a.geo.H : lin / mblocks;   // head * kparts + part (kparts = 1 when causal)
   const int h = hp / kparts, part = hp - h * kparts;
-  const int mb = CAUSAL ? mblocks - 1 - (lin - hp * mblocks) : lin - hp * mblocks;
+  const int mb = CAUSAL ? mblocks - 1 - lin / a.geo.H : lin - hp * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
@@ -1002,10 +1006,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   __shared__ u32x4_t lvs[2][kVTileP];
   __shared__ int s_flag;
   const int wg = blockIdx.x;
-  const int lin = (wg & 7) * per_xcd + (wg >> 3);
+  // unit order as in the running-maximum kernel (block-causal: longest first, round-robin over the XCDs)
+  const int lin = CAUSAL ? wg : (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
-  const int h = lin / mblocks;
-  const int mb = CAUSAL ? mblocks - 1 - (lin - h * mblocks) : lin - h * mblocks;
+  const int h = CAUSAL ? lin % a.geo.H : lin / mblocks;
+  const int mb = CAUSAL ? mblocks - 1 - lin / a.geo.H : lin - h * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
