@@ -26,6 +26,20 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+def back_to_back_ms(stream, ev, call, n=10):
+    """Median event-timed duration of `call` over n calls queued back to back on `stream` with one
+    synchronize at the end: the protocol of the chunk loop, used by every matrix-core leg."""
+    import numpy as np
+    import torch
+    evs = [(ev(), ev()) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -136,18 +150,11 @@ def main():
         if i >= 2:
             app_cold.append(a.elapsed_time(b))
     # attention-mass scores of this chunk's queries over the whole cache (the Deep-Forcing scoring pass)
-    sc_ms = []
     qwin = pool[0][0]
-    cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
+    sc_out = cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
     torch.cuda.synchronize()
-    for i in range(6):
-        a, b = ev(), ev()
-        a.record(stream)
-        cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
-        b.record(stream)
-        torch.cuda.synchronize()
-        sc_ms.append(a.elapsed_time(b))
-    score_ms = float(np.median(sc_ms))
+    score_ms = back_to_back_ms(stream, ev, lambda: cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1],
+                                                              out=sc_out), n=6)
     extras = sink_push_and_compact(dev, stream, flush, ev)
     extras.update(per_gpu_share(dev, stream, ev, w))
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
@@ -336,17 +343,9 @@ def per_gpu_share(dev, stream, ev, w):
         try:
             out = c.attend(q, 15)
             torch.cuda.synchronize()
-            ts = []
-            for i in range(8):
-                a, b = ev(), ev()
-                a.record(stream)
-                c.attend(q, 15, out=out)
-                b.record(stream)
-                torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b))
+            ms = back_to_back_ms(stream, ev, lambda: c.attend(q, 15, out=out))
         finally:
             os.environ.pop("KVC_ATTEND_SPLIT", None)
-        ms = float(np.median(ts))
         res[f"attend_5head_share{tag}_ms"] = round(ms, 4)
         res[f"attend_5head_share{tag}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
     return res
@@ -367,15 +366,7 @@ def block_causal_clip(dev, stream, ev, w, block_frames=3):
     (q,) = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w, 99, tensors=(0,), frames=F))
     out = c.attend_block_causal(q, 0, block_frames)
     torch.cuda.synchronize()
-    ts = []
-    for i in range(8):
-        a, b = ev(), ev()
-        a.record(stream)
-        c.attend_block_causal(q, 0, block_frames, out=out)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ms = float(np.median(ts))
+    ms = back_to_back_ms(stream, ev, lambda: c.attend_block_causal(q, 0, block_frames, out=out), n=8)
     cb = block_frames * S
     n = c.info()["n_valid"]
     vis = sum(min(n, (r // cb + 1) * cb) * min(cb, F * S - r) for r in range(0, F * S, cb))
@@ -399,15 +390,7 @@ def raw_keys_ab(dev, stream, ev, flush, w):
         q = q_
     out = c.attend(q, 15)
     torch.cuda.synchronize()
-    ts = []
-    for i in range(10):
-        a, b = ev(), ev()
-        a.record(stream)
-        c.attend(q, 15, out=out)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ms = float(np.median(ts))
+    ms = back_to_back_ms(stream, ev, lambda: c.attend(q, 15, out=out))
     flop = 4.0 * H * q.shape[0] * c.info()["n_valid"] * D
     rt = []
     for i in range(10):
@@ -454,15 +437,8 @@ def memrope_chunk(dev, stream, ev, flush, w):
         if mem is not None:
             q = chunks[0][0]
             o = c.attend(q, 54)
-            tt = []
-            for i in range(8):
-                a, b = ev(), ev()
-                a.record(stream)
-                c.attend(q, 54, out=o)
-                b.record(stream)
-                torch.cuda.synchronize()
-                tt.append(a.elapsed_time(b))
-            ms = float(np.median(tt))
+            torch.cuda.synchronize()
+            ms = back_to_back_ms(stream, ev, lambda: c.attend(q, 54, out=o), n=8)
             nk = c.info()["n_valid"] + 2 * S
             out["memrope_attend_ms"] = round(ms, 4)
             out["memrope_attend_tflops"] = round(4.0 * H * q.shape[0] * nk * D / (ms * 1e-3) / 1e12, 1)

@@ -73,11 +73,14 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
  * article: keys kept un-rotated, placed at attention time).  Keys are stored
  * with their height and width bands rotated (those positions never change)
  * and the time band raw; kvc_attend rotates each key's time band at its slot's
- * current time while staging it, so every attended key equals a fresh
- * rotation of the raw key and kvc_retime only rewrites time indices.
- * kvc_score and kvc_relax_scores see the keys placed the same way (their
- * scratch then also holds a copy of the keys' time-band plane, rotated to each
- * slot's current time; the *_scratch_bytes calls include it). */
+ * current time, so every attended key equals a fresh rotation of the raw key
+ * and kvc_retime only rewrites time indices.  For bf16 caches with head_dim
+ * 128 the workspace holds a copy of the keys' time-band plane that each
+ * kvc_attend first fills, in one pass, with every slot (and the memory
+ * tokens) placed at its current time; the attention then reads it (other
+ * caches rotate inside the attention kernel).  kvc_score and kvc_relax_scores
+ * see the keys placed the same way (their scratch then also holds such a copy;
+ * the *_scratch_bytes calls include it). */
 #define KVC_CREATE_RAW_KEYS 2u
 /* kvc_create: MemRoPE memory tokens (rCM length-extrapolation article: evicted
  * frames are compressed into long- and short-term EMA memories instead of
@@ -126,7 +129,8 @@ typedef struct {
 
 /* Device bytes the caller must provide to kvc_create for this geometry
  * (includes K/V planes, time/global-index arrays, RoPE tables, the optional
- * raw-key bank, with KVC_CREATE_COMPACT the second window buffer, and the
+ * raw-key bank, with KVC_CREATE_COMPACT the second window buffer, with
+ * KVC_CREATE_RAW_KEYS the placed time-band plane described there, and the
  * small per-block flag array kvc_attend uses to mark blocks for recompute).
  * Returns 0 for an unsupported geometry (head_dim not 64/128, bad sizes). */
 size_t kvc_workspace_bytes(int32_t sink_frames, int32_t window_frames, int32_t frame_seqlen,

@@ -80,6 +80,7 @@ struct AppendArgs {
 struct RangeW {
   int32_t region, lo, n;
   int32_t blk0;                           // first block of this range
+  int32_t fixed, tfix;                    // placed mode: fixed != 0 places every slot at time tfix
 };
 
 struct RetimeArgs {

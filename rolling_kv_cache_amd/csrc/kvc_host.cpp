@@ -41,6 +41,7 @@ struct Layout {
   RegionLayout sink{}, win[2]{};
   size_t bank_k = 0, bank_v = 0, tab_t = 0, tab_h = 0, tab_w = 0, keep = 0, att_flags = 0, total = 0;
   size_t mem_k = 0, mem_v = 0, split_o = 0, split_ml = 0;
+  size_t placed_sink = 0, placed_win = 0;   // raw keys: time band placed for the matrix-core attention
 };
 
 Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_t H, int32_t D, kvc_dtype dt,
@@ -98,6 +99,12 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   if (cflags & KVC_CREATE_MEMORY) {
     L.mem_k = take((size_t)2 * H * S * D * 4);
     L.mem_v = take((size_t)2 * H * S * D * 4);
+  }
+  // raw-key caches on the matrix-core path: KA planes with every slot's time band placed at its
+  // current time, written once per attend call and read by the plain attention kernels
+  if ((cflags & KVC_CREATE_RAW_KEYS) && L.esz == 2 && D == 128) {
+    L.placed_sink = take((size_t)H * L.SP * L.DA * L.esz);
+    L.placed_win = take((size_t)H * L.WP * L.DA * L.esz);
   }
   L.total = off;
   L.ok = true;
@@ -283,6 +290,52 @@ hipError_t launch_placed_ka(kvc_handle h, char* dst, kvc::KeyRegions* keys) {
   keys->ka[0] = a.out_ka[0];
   keys->ka[1] = a.out_ka[1];
   return kvc::launch_retime(a, blocks, h->stream);
+}
+
+// Raw-key caches on the matrix-core path: place the time band of every slot the attention may read --
+// the valid prefixes of the sink and the current window, and the memory frames at their times -- into
+// the workspace's placed KA planes in one pass, and point the key regions' KA planes there, so that the
+// plain kernels run (each staged tile would otherwise be rotated again by every query block).  Slots
+// past the valid prefixes keep what the placed planes held (zeros from creation, or keys placed by an
+// earlier call): finite, and masked by the attention.
+hipError_t launch_placed_attend(kvc_handle h, kvc::AttendArgs& a) {
+  char* ps = h->ws + h->L.placed_sink;
+  char* pw = h->ws + h->L.placed_win;
+  kvc::RetimeArgs r{};
+  r.reg[0] = h->sink;
+  r.reg[1] = cur_win(h);
+  r.out_ka[0] = ps;
+  r.out_ka[1] = pw;
+  int32_t blocks = 0;
+  auto add = [&](int32_t region, int32_t lo, int32_t n, int32_t fixed, int32_t t) {
+    if (n <= 0) return;
+    kvc::RangeW& g = r.rng[r.nrng++];
+    g.region = region;
+    g.lo = lo;
+    g.n = n;
+    g.blk0 = blocks;
+    g.fixed = fixed;
+    g.tfix = t;
+    blocks += (n + 31) / 32;
+  };
+  add(kvc::kSink, 0, h->st.ns, 0, 0);
+  add(kvc::kWin, 0, h->st.nw, 0, 0);
+  if (a.mem_lo != INT32_MAX) {
+    add(kvc::kSink, a.mem_lo, h->S, 1, a.mem_t[0]);
+    add(kvc::kSink, a.mem_lo + h->S, h->S, 1, a.mem_t[1]);
+  }
+  r.keys = 1;
+  r.geo = h->geo;
+  r.tab = h->tab;
+  for (int i = 0; i < 2; ++i) {
+    if (a.keys.ka[i] == h->sink.ka)
+      a.keys.ka[i] = ps;
+    else if (a.keys.ka[i] == cur_win(h).ka)
+      a.keys.ka[i] = pw;
+  }
+  a.raw = 0;
+  a.mem_lo = INT32_MAX;
+  return kvc::launch_retime(r, blocks, h->stream);
 }
 
 bool same_ring(const kvc::RingState& a, const kvc::RingState& b) {
@@ -587,7 +640,13 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
     a.keys.n[0] = h->L.S_tok + 2 * h->S;
   }
   const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
-  hipError_t e = kvc::launch_attend(a, h->stream, force_general);
+  hipError_t e = hipSuccess;
+  // raw keys: placed once, then the plain matrix-core kernels (KVC_RAW_ATTEND=lds keeps the rotation of
+  // every staged tile inside the kernels instead, for comparison)
+  const char* ra = std::getenv("KVC_RAW_ATTEND");
+  if (a.raw && h->L.placed_win != 0 && !force_general && !(ra && std::string(ra) == "lds"))
+    e = launch_placed_attend(h, a);
+  if (e == hipSuccess) e = kvc::launch_attend(a, h->stream, force_general);
   return device_result(h, e, "attend");
 }
 

@@ -283,7 +283,7 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
   const int tid = threadIdx.x;
   const bool placed = a.out_ka[0] != nullptr;      // out of place, by each slot's absolute time
   if (tid < ns) {
-    const int t = R.t[s0 + tid];
+    const int t = (placed && rg.fixed) ? rg.tfix : R.t[s0 + tid];
     const int tn = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
     s_dl[tid] = placed ? t : tn - t;
     s_tn[tid] = tn;

@@ -1015,3 +1015,61 @@ def test_random_layer_group_sequences(seed, raw):
                 assert_state_equal(caches[li], ocs[li], w, f"{tag} layer {li}")
     log(f"  seed {seed}: {attended} attends, {batched} batched calls")
     assert attended >= 5 and batched >= 10
+
+
+# ---------------------------------------------------------------- raw keys: placed planes vs in-kernel rotation
+def test_raw_keys_placed_attention_equals_in_kernel_rotation():
+    """On bf16 head_dim-128 raw-key caches kvc_attend first places every slot's time band (and the memory
+    tokens) into the workspace's placed plane and runs the plain kernels; KVC_RAW_ATTEND=lds rotates each
+    staged tile inside the kernel instead.  Both place a key with the same arithmetic, so the outputs are
+    bit-identical -- over a plain window, an attention limit, memory tokens, split keys and block-causal
+    attention -- and match the oracle."""
+    def both(call):
+        a = call().float().cpu().numpy()
+        os.environ["KVC_RAW_ATTEND"] = "lds"
+        try:
+            b = call().float().cpu().numpy()
+        finally:
+            os.environ.pop("KVC_RAW_ATTEND", None)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        return a
+
+    for memory, split in ((None, False), ((0.9, 0.5), False), (None, True), ((0.9, 0.5), True)):
+        w = _replace(SMALL_SW, name="raw_placed", raw_keys=True, memory=memory)
+        gc = new_cache(w, split=split)
+        oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                         raw_keys=True, memory=memory)
+        for i in range(w.n_chunks):
+            q, k, v = chunk_inputs(w, i)
+            t0 = w.chunk_start_frame(i)
+            gc.append(dev(k, w), dev(v, w), t0)
+            oc.append(k, v, w.chunk_frames[i], t0)
+            if i % 3 == 2:
+                gc.retime(-2, True)
+                oc.retime(-2, True)
+            tag = f"memory {memory} split {split} chunk {i}"
+            out = both(lambda: gc.attend(dev(q, w), t0 + 1))
+            check_attention(out, oc.attend(q, w.chunk_frames[i], t0 + 1), tag)
+            if memory is None and oc.n > 100:
+                m = oc.n - 70
+                gc.set_attention_limit(m)
+                try:
+                    out = both(lambda: gc.attend(dev(q, w), t0))
+                finally:
+                    gc.set_attention_limit(0)
+                check_attention(out, oc.attend(q, w.chunk_frames[i], t0, max_keys=m), tag + " limited")
+        assert memory is None or oc.mem_frames > 0
+    # block-causal over a raw clip cache
+    w = Workload("raw_placed_bc", 241, 2, 128, "bf16", 6, 10, 0, 8, (2, 2, 2, 2), raw_keys=True)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype,
+                     raw_keys=True)
+    for i in range(4):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    gc.retime(3)
+    oc.retime(3, False)
+    (q,) = chunk_inputs(w, 90, tensors=(0,), frames=8)
+    out = both(lambda: gc.attend_block_causal(dev(q, w), 3, 2))
+    check_attention(out, oc.attend_block_causal(q, 8, 3, 2), "raw placed block-causal")
