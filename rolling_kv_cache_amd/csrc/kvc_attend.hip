@@ -1001,24 +1001,27 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
 
 template <bool CAUSAL, bool RAW>
 __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                           int ntile0, int ntiles) {
+                                                           int ntile0, int ntiles, int kparts) {
   __shared__ u32x4_t lks[2][kKTileP];
   __shared__ u32x4_t lvs[2][kVTileP];
   __shared__ int s_flag;
   const int wg = blockIdx.x;
-  // unit order as in the running-maximum kernel (block-causal: longest first, round-robin over the XCDs)
+  // unit order and key parts as in the running-maximum kernel (block-causal: longest first, round-robin
+  // over the XCDs; split keys: kparts balanced parts of the tile sequence, never when causal)
   const int lin = CAUSAL ? wg : (wg & 7) * per_xcd + (wg >> 3);
   if (lin >= total) return;
-  const int h = CAUSAL ? lin % a.geo.H : lin / mblocks;
-  const int mb = CAUSAL ? mblocks - 1 - lin / a.geo.H : lin - h * mblocks;
+  const int hp = CAUSAL ? lin % a.geo.H : lin / mblocks;   // head * kparts + part
+  const int h = hp / kparts, part = hp - h * kparts;
+  const int mb = CAUSAL ? mblocks - 1 - lin / a.geo.H : lin - hp * mblocks;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  ts.first = part * ntiles / kparts;
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
   // block-causal limits, as in the running-maximum kernel
-  int nt = ntiles, lim = 0, lim_lo = 0;
+  int nt = (part + 1) * ntiles / kparts - ts.first, lim = 0, lim_lo = 0;
   if (CAUSAL) {
     const int cb = a.causal_block, nall = a.keys.n[0] + a.keys.n[1];
     auto limit = [&](int r) { return min(nall, (r / cb + 1) * cb); };
@@ -1122,7 +1125,10 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   if (__ballot(!(pmax <= kPLimit)) != 0 && lane == 0) s_flag = 1;
   __syncthreads();
   if (tid == 0) a.flags[lin] = s_flag;
-  store_out(a, o, lsum, qrow, h, hl);
+  if (kparts > 1)
+    store_partial(a, o, -negm, lsum, qrow, h, part, hl);   // the fixed reference, log2 units like v5's max
+  else
+    store_out(a, o, lsum, qrow, h, hl);
 }
 
 // key parts for a split launch (one workgroup per CU at a time): the count in
@@ -1170,11 +1176,14 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     n0 = ntile1;
     nt = ntile1;
   }
-  if (VAR == 7) {            // split keys: partials, then the merge
+  if (VAR == 7) {            // split keys: fixed-reference partials, flagged parts again, then the merge
     const int kp = split_parts(total, nt);
     const int tot = total * kp, pxcd = (tot + 7) / 8;
+    hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * pxcd), dim3(512), 0, s, b, mblocks, tot, pxcd, n0,
+                       nt, kp);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * pxcd), dim3(512), 0, s, b, mblocks, tot, pxcd, n0, nt,
-                       (const int32_t*)nullptr, kp);
+                       (const int32_t*)b.flags, kp);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const int64_t threads = (int64_t)a.geo.H * a.Lq * 32;
     hipLaunchKernelGGL(merge_split_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, b, kp);
@@ -1186,13 +1195,13 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
                        n0, nt, (const int32_t*)nullptr, 1);
   else if (VAR == 6) {       // block-causal: fixed reference, then the flagged blocks with the running maximum
     hipLaunchKernelGGL((attend_v5f_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
-                       per_xcd, n0, nt);
+                       per_xcd, n0, nt, 1);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
                        n0, nt, (const int32_t*)b.flags, 1);
   } else if (VAR == 4) {
     hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
-                       per_xcd, n0, nt);
+                       per_xcd, n0, nt, 1);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
                        n0, nt, (const int32_t*)b.flags, 1);

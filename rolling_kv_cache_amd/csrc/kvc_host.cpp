@@ -90,8 +90,11 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
   L.tab_h = take((size_t)S * (L.bw / 2) * 2 * 4);
   L.tab_w = take((size_t)S * (L.bw / 2) * 2 * 4);
   L.keep = take((size_t)L.WP * 4);
-  // one recompute flag per 256-query attention block of the largest query chunk
-  L.att_flags = take((size_t)H * (((size_t)KVC_MAX_Q_FRAMES * S + 255) / 256) * 4);
+  // one recompute flag per 256-query attention block of the largest query chunk, and with split keys
+  // per (block, part): kparts * blocks * 256 <= kSplitRows bounds those units
+  size_t n_flags = (size_t)H * (((size_t)KVC_MAX_Q_FRAMES * S + 255) / 256);
+  if (cflags & KVC_CREATE_SPLIT_ATTEND) n_flags = std::max(n_flags, (size_t)kvc::kSplitRows / 256);
+  L.att_flags = take(n_flags * 4);
   if (cflags & KVC_CREATE_SPLIT_ATTEND) {
     L.split_o = take((size_t)kvc::kSplitRows * 128 * 4);
     L.split_ml = take((size_t)kvc::kSplitRows * 2 * 4);
