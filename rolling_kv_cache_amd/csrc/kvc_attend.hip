@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 #include "kvc_common.hip.hpp"
 #include "kvc_launch.hpp"
@@ -1095,7 +1096,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   // tile 0 holds at least one valid key (for every row, also block-causal), so the reference is finite
   const float negm = -tile_max(sa, c2);
 
-  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext, auto masked) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
     if constexpr (RAW)
       loadR(sr, rp, a, tid, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
@@ -1108,20 +1109,37 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     pmax = fmaxf(pmax, psum);
     lsum += psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
-    mask(snext, min(t + 1, last));
+    if constexpr (decltype(masked)::value) mask(snext, min(t + 1, last));
     if constexpr (RAW)
       storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     else
       store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
+  using Masked = std::integral_constant<bool, true>;
+  using Clean = std::integral_constant<bool, false>;
 
-  int t = 0;
-  for (; t + 1 < nt; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  // block-causal: the leading steps whose next tile (t + 1) is a whole tile ending before every row's
+  // limit run without the mask code (its branches and temporaries otherwise cost the loop registers);
+  // steps 0 .. clean - 1 are such steps
+  int clean = 0;
+  if (CAUSAL) {
+    auto whole_before = [&](int tt) {
+      const int lb = tt < ntile0 ? tt * kBN : a.keys.n[0] + (tt - ntile0) * kBN;
+      return ts.valid(tt) >= kBN && ts.lead(tt) <= 0 && lb + kBN <= lim_lo;
+    };
+    while (clean + 1 < nt && whole_before(clean + 1)) ++clean;
   }
-  if (t < nt) step(t, sa, sb);
+  int t = 0;
+  for (; t + 1 < clean; t += 2) {
+    step(t, sa, sb, Clean{});
+    step(t + 1, sb, sa, Clean{});
+  }
+  for (; t + 1 < nt; t += 2) {
+    step(t, sa, sb, Masked{});
+    step(t + 1, sb, sa, Masked{});
+  }
+  if (t < nt) step(t, sa, sb, Masked{});
   if (__ballot(!(pmax <= kPLimit)) != 0 && lane == 0) s_flag = 1;
   __syncthreads();
   if (tid == 0) a.flags[lin] = s_flag;
