@@ -77,9 +77,25 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // Per-thread source pointers of the register-staged tile loads.  Thread tid
 // always moves chunk column (tid & 15) of K rows (tid >> 4) + 16 i, and the
 // 16-byte pieces tid + 256 i of the contiguous V^T tile.
+// Two regions' pointers are kept as region 0's address and region 1's offset
+// from it, chosen by integer arithmetic: a two-element pointer array chosen by
+// a computed region bit becomes an indexed load, which keeps the array in
+// scratch memory.
+struct RegionPtr {
+  uintptr_t p0, d;        // region 0's address, region 1's minus it
+  __device__ __forceinline__ void set(const void* a0, const void* a1) {
+    p0 = (uintptr_t)a0;
+    d = (uintptr_t)a1 - p0;
+  }
+  template <typename T>
+  __device__ __forceinline__ const T* get(int r) const {
+    return (const T*)(p0 + (r ? d : (uintptr_t)0));
+  }
+};
+
 struct TilePtrs {
-  const uint16_t* k[2];   // region r, base slot 0, row (tid >> 4)
-  const uint16_t* v[2];   // region r, tile 0, piece tid
+  RegionPtr k;            // region r, base slot 0, row (tid >> 4)
+  RegionPtr v;            // region r, tile 0, piece tid
   int kstride;            // elements per key row of this thread's plane
 };
 
@@ -87,12 +103,16 @@ __device__ __forceinline__ TilePtrs tile_ptrs(const KeyRegions& kr, int h, int t
   TilePtrs p;
   const int c = tid & 15;
   p.kstride = c < 6 ? kDA : kDB;
+  const uint16_t* k[2];
+  const uint16_t* v[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const uint16_t* plane = c < 6 ? (const uint16_t*)kr.ka[r] + c * 8 : (const uint16_t*)kr.kb[r] + (c - 6) * 8;
-    p.k[r] = plane + ((int64_t)h * kr.cap[r] + (tid >> 4)) * p.kstride;
-    p.v[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile + tid * 8;
+    k[r] = plane + ((int64_t)h * kr.cap[r] + (tid >> 4)) * p.kstride;
+    v[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile + tid * 8;
   }
+  p.k.set(k[0], k[1]);
+  p.v.set(v[0], v[1]);
   return p;
 }
 
@@ -102,8 +122,8 @@ struct TileRegs {
 };
 
 __device__ __forceinline__ void tile_load(TileRegs& tr, const TilePtrs& p, int r, int base) {
-  const uint16_t* kp = (r == 0 ? p.k[0] : p.k[1]) + base * p.kstride;
-  const uint16_t* vp = (r == 0 ? p.v[0] : p.v[1]) + (base / kTile) * kVTile;
+  const uint16_t* kp = p.k.get<uint16_t>(r) + base * p.kstride;
+  const uint16_t* vp = p.v.get<uint16_t>(r) + (base / kTile) * kVTile;
 #pragma unroll
   for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * p.kstride);
 #pragma unroll
@@ -188,27 +208,93 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o
     }
 }
 
-// Key tiles in visiting order: the tiles covering region 0's visible slots
-// [lo0, n0), then region 1's.  base = first slot of the tile (64-aligned),
-// valid = slots of the tile before the range end, lead = slots of the tile
-// before the range start (> 0 only in a range's first tile).
-// `first` shifts the sequence (a split-key workgroup starts at its part's first tile).
+// Key tiles in visiting order.  Logical order: the tiles covering region 0's
+// visible slots [lo0, n0), then region 1's.  Edges-last order (any order
+// gives the same softmax when no row's keys depend on the order, i.e. without
+// a causal limit): each range's whole tiles first, then its edge tiles -- the
+// first tile when the range starts inside it, the last when it ends inside it
+// -- so all but the last few tiles need no mask.  base = first slot of the
+// tile (64-aligned), valid = slots of the tile before the range end, lead =
+// slots of the tile before the range start.  `first` shifts the sequence (a
+// split-key workgroup starts at its part's first tile).
 struct TileSeq {
   int ntile0, ntiles;
   int t00, t01;            // first tile of each range
   int lo0, lo1, n0, n1;
   int first;
-  __device__ __forceinline__ int region(int it) const { return it + first < ntile0 ? 0 : 1; }
-  __device__ __forceinline__ int base(int it) const {
+  int f0, f1;              // tiles visited first from each range (all of them in logical order)
+  int w00, w01;            // the first of those in each range
+  int epos;                // edge tiles visited after them: 2 bits each, in order, naming range 0's
+                           // first (0) or last (1) tile, or range 1's first (2) or last (3)
+  int t0last, t1last;      // last tile of each range
+  // range and first slot of the it-th tile, for a tile visited before the edges (any tile in logical
+  // order): two plain selects, which stay branch-free inside the pipelined step
+  __device__ __forceinline__ int region_w(int it) const { return it + first < f0 ? 0 : 1; }
+  __device__ __forceinline__ int base_w(int it) const {
     const int jt = it + first;
-    return (jt < ntile0 ? t00 + jt : t01 + jt - ntile0) * kBN;
+    return (jt < f0 ? w00 + jt : w01 + jt - f0) * kBN;
   }
-  __device__ __forceinline__ int valid(int it) const { return (it + first < ntile0 ? n0 : n1) - base(it); }
-  __device__ __forceinline__ int lead(int it) const { return (it + first < ntile0 ? lo0 : lo1) - base(it); }
+  // (tile index << 1) | range of any tile of the sequence
+  __device__ __forceinline__ int at(int it) const {
+    const int jt = it + first;
+    if (jt < f0 + f1) return (base_w(it) / kBN) << 1 | region_w(it);
+    const int b = (epos >> (2 * (jt - f0 - f1))) & 3;
+    const int te = (b & 1) ? ((b & 2) ? t1last : t0last) : ((b & 2) ? t01 : t00);
+    return (te << 1) | (b >> 1);
+  }
+  __device__ __forceinline__ int region(int it) const { return at(it) & 1; }
+  __device__ __forceinline__ int base(int it) const { return (at(it) >> 1) * kBN; }
+  __device__ __forceinline__ int valid(int it) const {
+    const int x = at(it);
+    return ((x & 1) ? n1 : n0) - (x >> 1) * kBN;
+  }
+  __device__ __forceinline__ int lead(int it) const {
+    const int x = at(it);
+    return ((x & 1) ? lo1 : lo0) - (x >> 1) * kBN;
+  }
+  // tiles of the sequence, counted from `first`, that need no mask (edges-last order)
+  __device__ __forceinline__ int whole_prefix(int n) const { return max(0, min(n, f0 + f1 - first)); }
 };
 
 __device__ __forceinline__ TileSeq tile_seq(const KeyRegions& k, int ntile0, int ntiles) {
-  return TileSeq{ntile0, ntiles, k.lo[0] / kBN, k.lo[1] / kBN, k.lo[0], k.lo[1], k.n[0], k.n[1], 0};
+  TileSeq s{};
+  s.ntile0 = ntile0;
+  s.ntiles = ntiles;
+  s.t00 = k.lo[0] / kBN;
+  s.t01 = k.lo[1] / kBN;
+  s.lo0 = k.lo[0];
+  s.lo1 = k.lo[1];
+  s.n0 = k.n[0];
+  s.n1 = k.n[1];
+  s.f0 = ntile0;
+  s.f1 = ntiles - ntile0;
+  s.w00 = s.t00;
+  s.w01 = s.t01;
+  s.t0last = s.t00 + ntile0 - 1;
+  s.t1last = s.t01 + ntiles - ntile0 - 1;
+  return s;
+}
+
+__device__ __forceinline__ TileSeq tile_seq_edges_last(const KeyRegions& k, int ntile0, int ntiles) {
+  TileSeq s = tile_seq(k, ntile0, ntiles);
+  const int nt1 = ntiles - ntile0;
+  // a range's first tile is an edge when the range starts inside it, its last when it ends inside it
+  const int e0lo = ntile0 > 0 && s.lo0 % kBN != 0;
+  const int e0hi = ntile0 > 0 && s.n0 % kBN != 0 && !(ntile0 == 1 && e0lo);
+  const int e1lo = nt1 > 0 && s.lo1 % kBN != 0;
+  const int e1hi = nt1 > 0 && s.n1 % kBN != 0 && !(nt1 == 1 && e1lo);
+  s.w00 = s.t00 + e0lo;
+  s.f0 = ntile0 - e0lo - e0hi;
+  s.w01 = s.t01 + e1lo;
+  s.f1 = nt1 - e1lo - e1hi;
+  s.t0last = s.t00 + ntile0 - 1;
+  s.t1last = s.t01 + nt1 - 1;
+  int ne = 0;
+  if (e0lo) s.epos |= 0 << (2 * ne++);
+  if (e0hi) s.epos |= 1 << (2 * ne++);
+  if (e1lo) s.epos |= 2 << (2 * ne++);
+  if (e1hi) s.epos |= 3 << (2 * ne++);
+  return s;
 }
 
 // tiles covering region r's visible slots
@@ -375,8 +461,8 @@ __global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mbl
     const int tk = min(t + 2, last), tv = min(t + 1, last);
     // K(t+2) and V(t+1) in flight (clamped at the last tile: harmless re-loads)
     {
-      const uint16_t* kp = (ts.region(tk) == 0 ? tp.k[0] : tp.k[1]) + ts.base(tk) * tp.kstride;
-      const uint16_t* vp = (ts.region(tv) == 0 ? tp.v[0] : tp.v[1]) + (ts.base(tv) / kTile) * kVTile;
+      const uint16_t* kp = tp.k.get<uint16_t>(ts.region(tk)) + ts.base(tk) * tp.kstride;
+      const uint16_t* vp = tp.v.get<uint16_t>(ts.region(tv)) + (ts.base(tv) / kTile) * kVTile;
 #pragma unroll
       for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * tp.kstride);
 #pragma unroll
@@ -420,8 +506,8 @@ struct Stage5 {
 };
 
 __device__ __forceinline__ void load5(Stage5& st, const TilePtrs& p, int rk, int bk, int rv, int bv) {
-  const uint16_t* kp = (rk == 0 ? p.k[0] : p.k[1]) + bk * p.kstride;
-  const uint16_t* vp = (rv == 0 ? p.v[0] : p.v[1]) + (bv / kTile) * kVTile;
+  const uint16_t* kp = p.k.get<uint16_t>(rk) + bk * p.kstride;
+  const uint16_t* vp = p.v.get<uint16_t>(rv) + (bv / kTile) * kVTile;
 #pragma unroll
   for (int i = 0; i < 2; ++i) st.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 32 * i * p.kstride);
 #pragma unroll
@@ -454,10 +540,7 @@ __device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* l
 // rotate it, plus KB chunk tid; threads 384..511 move KB chunks tid and
 // tid + 128 (KB chunk i: row i / 10, column 6 + i % 10).
 struct RawPtrs {
-  const uint16_t* ka[2];   // region r, head h: key planes, V^T tiles and times (wave-uniform)
-  const uint16_t* kb[2];
-  const uint16_t* v[2];
-  const int32_t* t[2];
+  RegionPtr ka, kb, v, t;  // region r, head h: key planes, V^T tiles and times (wave-uniform)
   int o0, o1;              // element offsets of the two chunks in their planes at slot base 0
   int l0, l1;              // LDS chunk index (row * kKSt + column) of the two chunks
   int lrow;                // the KA chunk's row in the tile
@@ -474,13 +557,19 @@ __device__ __forceinline__ RawPtrs raw_ptrs(const KeyRegions& kr, int h, int tid
   p.l1 = (i1 / 10) * kKSt + 6 + i1 % 10;
   p.o0 = tid * 8;
   p.o1 = i1 * 8;
+  const uint16_t* pka[2];
+  const uint16_t* pkb[2];
+  const uint16_t* pv[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    p.ka[r] = (const uint16_t*)kr.ka[r] + (int64_t)h * kr.cap[r] * kDA;
-    p.kb[r] = (const uint16_t*)kr.kb[r] + (int64_t)h * kr.cap[r] * kDB;
-    p.v[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile;
-    p.t[r] = kr.t[r];
+    pka[r] = (const uint16_t*)kr.ka[r] + (int64_t)h * kr.cap[r] * kDA;
+    pkb[r] = (const uint16_t*)kr.kb[r] + (int64_t)h * kr.cap[r] * kDB;
+    pv[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile;
   }
+  p.ka.set(pka[0], pka[1]);
+  p.kb.set(pkb[0], pkb[1]);
+  p.v.set(pv[0], pv[1]);
+  p.t.set(kr.t[0], kr.t[1]);
   return p;
 }
 
@@ -495,18 +584,18 @@ struct StageR {
 __device__ __forceinline__ void loadR(StageR& st, const RawPtrs& p, const AttendArgs& a, int tid, int rk, int bk,
                                       int rv, int bv) {
   const bool ka = tid < 384;
-  const uint16_t* pa = rk == 0 ? p.ka[0] : p.ka[1];
-  const uint16_t* pb = rk == 0 ? p.kb[0] : p.kb[1];
+  const uint16_t* pa = p.ka.get<uint16_t>(rk);
+  const uint16_t* pb = p.kb.get<uint16_t>(rk);
   if (ka) {
     const int slot = bk + p.lrow;
-    st.t = (rk == 0 ? p.t[0] : p.t[1])[slot];
+    st.t = p.t.get<int32_t>(rk)[slot];
     if (rk == 0 && slot >= a.mem_lo) st.t = a.mem_t[slot - a.mem_lo >= a.geo.S ? 1 : 0];
     st.k[0] = *reinterpret_cast<const u32x4_t*>(pa + (bk * kDA + p.o0));
   } else {
     st.k[0] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o0));
   }
   st.k[1] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o1));
-  const uint16_t* vp = (rv == 0 ? p.v[0] : p.v[1]) + (bv / kTile) * kVTile + tid * 8;
+  const uint16_t* vp = p.v.get<uint16_t>(rv) + (bv / kTile) * kVTile + tid * 8;
 #pragma unroll
   for (int i = 0; i < 2; ++i) st.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 4096 * i);
 }
@@ -584,7 +673,8 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  // not causal: edges-last order, as in the fixed-reference kernel (a split part covers the same tiles in both)
+  TileSeq ts = CAUSAL ? tile_seq(a.keys, ntile0, ntiles) : tile_seq_edges_last(a.keys, ntile0, ntiles);
   // balanced parts: [part * ntiles / kparts, (part + 1) * ntiles / kparts), never empty (kparts <= ntiles / 4)
   ts.first = part * ntiles / kparts;
   const int kbase = perm_row(l32) * kKSt + hl;
@@ -664,9 +754,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
     if constexpr (RAW)
-      loadR(sr, rp, a, tid, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+      loadR(sr, rp, a, tid, CAUSAL ? ts.region_w(tk) : ts.region(tk), CAUSAL ? ts.base_w(tk) : ts.base(tk),
+            CAUSAL ? ts.region_w(tv) : ts.region(tv), CAUSAL ? ts.base_w(tv) : ts.base(tv));
     else
-      load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+      load5(st, tp, CAUSAL ? ts.region_w(tk) : ts.region(tk), CAUSAL ? ts.base_w(tk) : ts.base(tk),
+            CAUSAL ? ts.region_w(tv) : ts.region(tv), CAUSAL ? ts.base_w(tv) : ts.base(tv));
     bf16x8_t pb[2][2];
     float psum, alpha;
     bool upd;
@@ -746,7 +838,7 @@ __global__ __launch_bounds__(256) void merge_split_kernel(AttendArgs a, int kpar
 // 16 rows of every tile, and the two wave halves are added at the end.
 
 __device__ __forceinline__ void tile_load_k(TileRegs& tr, const TilePtrs& p, int r, int base) {
-  const uint16_t* kp = (r == 0 ? p.k[0] : p.k[1]) + base * p.kstride;
+  const uint16_t* kp = p.k.get<uint16_t>(r) + base * p.kstride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * p.kstride);
 }
@@ -1017,7 +1109,8 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * 256 + wave * 32 + l32;
-  TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  // not causal: whole tiles first, the few edge tiles (which need masks) last
+  TileSeq ts = CAUSAL ? tile_seq(a.keys, ntile0, ntiles) : tile_seq_edges_last(a.keys, ntile0, ntiles);
   ts.first = part * ntiles / kparts;
   const int kbase = perm_row(l32) * kKSt + hl;
   const int vbase = l32 * kVSt + hl;
@@ -1098,10 +1191,14 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext, auto masked) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
+    // clean steps load only tiles visited before the edges (or any tile in logical order)
+    constexpr bool any = decltype(masked)::value && !CAUSAL;
+    const int rk = any ? ts.region(tk) : ts.region_w(tk), bk = any ? ts.base(tk) : ts.base_w(tk);
+    const int rv = any ? ts.region(tv) : ts.region_w(tv), bv = any ? ts.base(tv) : ts.base_w(tv);
     if constexpr (RAW)
-      loadR(sr, rp, a, tid, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+      loadR(sr, rp, a, tid, rk, bk, rv, bv);
     else
-      load5(st, tp, ts.region(tk), ts.base(tk), ts.region(tv), ts.base(tv));
+      load5(st, tp, rk, bk, rv, bv);
     bf16x8_t pb[2][2];
     float psum;
     qk_and_exp(snext, lks[(t + 1) & 1], qf, kbase, scur, negm, c2, pb, psum);
@@ -1119,16 +1216,20 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   using Masked = std::integral_constant<bool, true>;
   using Clean = std::integral_constant<bool, false>;
 
-  // block-causal: the leading steps whose next tile (t + 1) is a whole tile ending before every row's
-  // limit run without the mask code (its branches and temporaries otherwise cost the loop registers);
-  // steps 0 .. clean - 1 are such steps
-  int clean = 0;
+  // the leading steps whose next tile (t + 1) needs no mask run without the mask code (its branches and
+  // temporaries otherwise cost the loop issue slots and registers); steps 0 .. clean - 1 are such steps.
+  // Not causal: the whole tiles the edges-last order visits first.  Block-causal: the whole tiles that
+  // end before every row's limit.
+  int clean = CAUSAL ? 0 : max(0, ts.whole_prefix(nt) - 2);   // tile t + 2 (loaded ahead) is whole too
   if (CAUSAL) {
-    auto whole_before = [&](int tt) {
-      const int lb = tt < ntile0 ? tt * kBN : a.keys.n[0] + (tt - ntile0) * kBN;
-      return ts.valid(tt) >= kBN && ts.lead(tt) <= 0 && lb + kBN <= lim_lo;
-    };
-    while (clean + 1 < nt && whole_before(clean + 1)) ++clean;
+    // the tiles from tile 1 on that are whole and end before lim_lo, in closed form (logical order, both
+    // ranges from slot 0): region 0's tiles below n0 / 64 and lim_lo / 64, then, when all of region 0's
+    // tiles 1 .. ntile0 - 1 qualify, region 1's below n1 / 64 and (lim_lo - n0) / 64
+    const int n0 = a.keys.n[0], n1 = a.keys.n[1];
+    const int w0 = min(n0 / kBN, lim_lo / kBN);
+    const int c = (ntile0 > 1 && w0 < ntile0) ? w0 - 1
+                                              : ntile0 - 1 + (lim_lo >= n0 ? min(n1 / kBN, (lim_lo - n0) / kBN) : 0);
+    clean = max(0, min(c, nt - 1));
   }
   int t = 0;
   for (; t + 1 < clean; t += 2) {
