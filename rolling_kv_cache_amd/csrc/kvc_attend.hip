@@ -45,6 +45,7 @@
 
 #include "kvc_common.hip.hpp"
 #include "kvc_launch.hpp"
+#include "kvc_tiles.hpp"
 
 namespace kvc {
 
@@ -57,7 +58,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;                       // queries per workgroup
-constexpr int kBN = 64;                        // keys per tile
 constexpr int kDA = 48, kDB = 80;              // key plane widths for head_dim 128
 constexpr int kVTile = 128 * kTile;            // elements of one V^T tile
 
@@ -208,99 +208,6 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o
     }
 }
 
-// Key tiles in visiting order.  Logical order: the tiles covering region 0's
-// visible slots [lo0, n0), then region 1's.  Edges-last order (any order
-// gives the same softmax when no row's keys depend on the order, i.e. without
-// a causal limit): each range's whole tiles first, then its edge tiles -- the
-// first tile when the range starts inside it, the last when it ends inside it
-// -- so all but the last few tiles need no mask.  base = first slot of the
-// tile (64-aligned), valid = slots of the tile before the range end, lead =
-// slots of the tile before the range start.  `first` shifts the sequence (a
-// split-key workgroup starts at its part's first tile).
-struct TileSeq {
-  int ntile0, ntiles;
-  int t00, t01;            // first tile of each range
-  int lo0, lo1, n0, n1;
-  int first;
-  int f0, f1;              // tiles visited first from each range (all of them in logical order)
-  int w00, w01;            // the first of those in each range
-  int epos;                // edge tiles visited after them: 2 bits each, in order, naming range 0's
-                           // first (0) or last (1) tile, or range 1's first (2) or last (3)
-  int t0last, t1last;      // last tile of each range
-  // range and first slot of the it-th tile, for a tile visited before the edges (any tile in logical
-  // order): two plain selects, which stay branch-free inside the pipelined step
-  __device__ __forceinline__ int region_w(int it) const { return it + first < f0 ? 0 : 1; }
-  __device__ __forceinline__ int base_w(int it) const {
-    const int jt = it + first;
-    return (jt < f0 ? w00 + jt : w01 + jt - f0) * kBN;
-  }
-  // (tile index << 1) | range of any tile of the sequence
-  __device__ __forceinline__ int at(int it) const {
-    const int jt = it + first;
-    if (jt < f0 + f1) return (base_w(it) / kBN) << 1 | region_w(it);
-    const int b = (epos >> (2 * (jt - f0 - f1))) & 3;
-    const int te = (b & 1) ? ((b & 2) ? t1last : t0last) : ((b & 2) ? t01 : t00);
-    return (te << 1) | (b >> 1);
-  }
-  __device__ __forceinline__ int region(int it) const { return at(it) & 1; }
-  __device__ __forceinline__ int base(int it) const { return (at(it) >> 1) * kBN; }
-  __device__ __forceinline__ int valid(int it) const {
-    const int x = at(it);
-    return ((x & 1) ? n1 : n0) - (x >> 1) * kBN;
-  }
-  __device__ __forceinline__ int lead(int it) const {
-    const int x = at(it);
-    return ((x & 1) ? lo1 : lo0) - (x >> 1) * kBN;
-  }
-  // tiles of the sequence, counted from `first`, that need no mask (edges-last order)
-  __device__ __forceinline__ int whole_prefix(int n) const { return max(0, min(n, f0 + f1 - first)); }
-};
-
-__device__ __forceinline__ TileSeq tile_seq(const KeyRegions& k, int ntile0, int ntiles) {
-  TileSeq s{};
-  s.ntile0 = ntile0;
-  s.ntiles = ntiles;
-  s.t00 = k.lo[0] / kBN;
-  s.t01 = k.lo[1] / kBN;
-  s.lo0 = k.lo[0];
-  s.lo1 = k.lo[1];
-  s.n0 = k.n[0];
-  s.n1 = k.n[1];
-  s.f0 = ntile0;
-  s.f1 = ntiles - ntile0;
-  s.w00 = s.t00;
-  s.w01 = s.t01;
-  s.t0last = s.t00 + ntile0 - 1;
-  s.t1last = s.t01 + ntiles - ntile0 - 1;
-  return s;
-}
-
-__device__ __forceinline__ TileSeq tile_seq_edges_last(const KeyRegions& k, int ntile0, int ntiles) {
-  TileSeq s = tile_seq(k, ntile0, ntiles);
-  const int nt1 = ntiles - ntile0;
-  // a range's first tile is an edge when the range starts inside it, its last when it ends inside it
-  const int e0lo = ntile0 > 0 && s.lo0 % kBN != 0;
-  const int e0hi = ntile0 > 0 && s.n0 % kBN != 0 && !(ntile0 == 1 && e0lo);
-  const int e1lo = nt1 > 0 && s.lo1 % kBN != 0;
-  const int e1hi = nt1 > 0 && s.n1 % kBN != 0 && !(nt1 == 1 && e1lo);
-  s.w00 = s.t00 + e0lo;
-  s.f0 = ntile0 - e0lo - e0hi;
-  s.w01 = s.t01 + e1lo;
-  s.f1 = nt1 - e1lo - e1hi;
-  s.t0last = s.t00 + ntile0 - 1;
-  s.t1last = s.t01 + nt1 - 1;
-  int ne = 0;
-  if (e0lo) s.epos |= 0 << (2 * ne++);
-  if (e0hi) s.epos |= 1 << (2 * ne++);
-  if (e1lo) s.epos |= 2 << (2 * ne++);
-  if (e1hi) s.epos |= 3 << (2 * ne++);
-  return s;
-}
-
-// tiles covering region r's visible slots
-__host__ __device__ __forceinline__ int range_tiles(const KeyRegions& k, int r) {
-  return k.n[r] > k.lo[r] ? (k.n[r] + kBN - 1) / kBN - k.lo[r] / kBN : 0;
-}
 
 // ---------------------------------------------------------------------------
 // Interleaved pipeline (v3).  LDS rows are padded by one 16-byte chunk (K rows
@@ -1221,16 +1128,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   // Not causal: the whole tiles the edges-last order visits first.  Block-causal: the whole tiles that
   // end before every row's limit.
   int clean = CAUSAL ? 0 : max(0, ts.whole_prefix(nt) - 2);   // tile t + 2 (loaded ahead) is whole too
-  if (CAUSAL) {
-    // the tiles from tile 1 on that are whole and end before lim_lo, in closed form (logical order, both
-    // ranges from slot 0): region 0's tiles below n0 / 64 and lim_lo / 64, then, when all of region 0's
-    // tiles 1 .. ntile0 - 1 qualify, region 1's below n1 / 64 and (lim_lo - n0) / 64
-    const int n0 = a.keys.n[0], n1 = a.keys.n[1];
-    const int w0 = min(n0 / kBN, lim_lo / kBN);
-    const int c = (ntile0 > 1 && w0 < ntile0) ? w0 - 1
-                                              : ntile0 - 1 + (lim_lo >= n0 ? min(n1 / kBN, (lim_lo - n0) / kBN) : 0);
-    clean = max(0, min(c, nt - 1));
-  }
+  if (CAUSAL) clean = causal_clean_steps(a.keys.n[0], a.keys.n[1], ntile0, nt, lim_lo);
   int t = 0;
   for (; t + 1 < clean; t += 2) {
     step(t, sa, sb, Clean{});

@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "kvc_ring.hpp"
+#include "kvc_tiles.hpp"
 
 namespace {
 thread_local std::string g_ring_err;
@@ -69,6 +70,52 @@ void kvr_logical(void* p, int32_t* t, int64_t* g) { static_cast<kvc::RingState*>
 void kvr_physical(void* p, int32_t* region, int32_t* slot) {
   auto* st = static_cast<kvc::RingState*>(p);
   for (int32_t l = 0; l < st->n_valid(); ++l) st->phys(l, region + l, slot + l);
+}
+
+// The attention kernels' key-tile order (kvc_tiles.hpp), built for the host so
+// that CPU tests can check it.  Visible slot ranges [lo0, n0) and [lo1, n1);
+// an empty range 0 is replaced by range 1, as the attention launch does.
+// kvr_tile_count returns the number of tiles.  kvr_tile_order writes
+// (tile << 1) | range of tiles first .. first + count - 1 of the sequence
+// (edges_last: whole tiles first, else logical order) to out, the same from
+// the whole-tile lookup the pipelined steps use to out_whole, and returns how
+// many of them come before the first edge tile; -1 for a bad range.
+static kvc::KeyRegions tile_ranges(int32_t lo0, int32_t n0, int32_t lo1, int32_t n1) {
+  kvc::KeyRegions k{};
+  k.lo[0] = lo0;
+  k.n[0] = n0;
+  k.lo[1] = lo1;
+  k.n[1] = n1;
+  if (kvc::range_tiles(k, 0) == 0) {
+    k.lo[0] = lo1;
+    k.n[0] = n1;
+    k.lo[1] = 0;
+    k.n[1] = 0;
+  }
+  return k;
+}
+
+int32_t kvr_tile_count(int32_t lo0, int32_t n0, int32_t lo1, int32_t n1) {
+  const kvc::KeyRegions k = tile_ranges(lo0, n0, lo1, n1);
+  return kvc::range_tiles(k, 0) + kvc::range_tiles(k, 1);
+}
+
+int32_t kvr_tile_order(int32_t lo0, int32_t n0, int32_t lo1, int32_t n1, int32_t edges_last, int32_t first,
+                       int32_t count, int32_t* out, int32_t* out_whole) {
+  const kvc::KeyRegions k = tile_ranges(lo0, n0, lo1, n1);
+  const int nt0 = kvc::range_tiles(k, 0), nt = nt0 + kvc::range_tiles(k, 1);
+  if (first < 0 || count < 0 || first + count > nt) return -1;
+  kvc::TileSeq s = edges_last ? kvc::tile_seq_edges_last(k, nt0, nt) : kvc::tile_seq(k, nt0, nt);
+  s.first = first;
+  for (int32_t it = 0; it < count; ++it) {
+    out[it] = s.at(it);
+    out_whole[it] = (s.base_w(it) / kvc::kBN) << 1 | s.region_w(it);
+  }
+  return s.whole_prefix(count);
+}
+
+int32_t kvr_causal_clean_steps(int32_t n0, int32_t n1, int32_t ntile0, int32_t nt, int32_t lim_lo) {
+  return kvc::causal_clean_steps(n0, n1, ntile0, nt, lim_lo);
 }
 
 }  // extern "C"
