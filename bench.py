@@ -187,8 +187,10 @@ def main():
     if os.path.exists(args.traffic):
         # counters taken on an older version of the kernel source do not count
         import hashlib
-        src = os.path.join(ROOT, "rolling_kv_cache_amd", "csrc", "kvc_attend.hip")
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for name in ("kvc_attend.hip", "kvc_tiles.hpp"):     # the attention kernels' sources
+            h.update(open(os.path.join(ROOT, "rolling_kv_cache_amd", "csrc", name), "rb").read())
+        digest = h.hexdigest()
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_sha256") == digest:

@@ -599,7 +599,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   const int last = nt - 1;
   // mask tile t: slots past the region's valid prefix, and (causal) keys past this row's prefix
   auto mask = [&](f32x16_t* s, int t) {
-    const int nv = ts.valid(t);
+    const int nv = CAUSAL ? ts.valid_w(t) : ts.valid(t);   // causal: logical order
     if (CAUSAL) {
       const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
       if (lb + kBN > lim_lo) {
@@ -607,18 +607,21 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
         return;
       }
     }
-    mask_tile(s, ts.lead(t), nv, hl);
+    mask_tile(s, CAUSAL ? ts.lead_w(t) : ts.lead(t), nv, hl);
   };
+  // tile lookups of the prologue (logical order when causal)
+  auto reg = [&](int t) { return CAUSAL ? ts.region_w(t) : ts.region(t); };
+  auto bas = [&](int t) { return CAUSAL ? ts.base_w(t) : ts.base(t); };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
   const RawPtrs rp = raw_ptrs(a.keys, h, tid);
 
   Stage5 st;
   StageR sr;
   if constexpr (RAW) {
-    loadR(sr, rp, a, tid, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
+    loadR(sr, rp, a, tid, reg(0), bas(0), reg(0), bas(0));
     loadR_table(sr, rp, a, tid);
   } else {
-    load5(st, tp, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
+    load5(st, tp, reg(0), bas(0), reg(0), bas(0));
   }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
@@ -629,11 +632,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   {
     const int t1 = min(1, last);
     if constexpr (RAW) {
-      loadR(sr, rp, a, tid, ts.region(t1), ts.base(t1), 0, 0);
+      loadR(sr, rp, a, tid, reg(t1), bas(t1), 0, 0);
       loadR_table(sr, rp, a, tid);
       storeR(sr, rp, lks[1], lvs[1], tid, true, false);
     } else {
-      load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+      load5(st, tp, reg(t1), bas(t1), 0, 0);
       store5(st, lks[1], lvs[1], tid, true, false);
     }
   }
@@ -1034,7 +1037,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   }
   const int last = nt - 1;
   auto mask = [&](f32x16_t* s, int t) {
-    const int nv = ts.valid(t);
+    const int nv = CAUSAL ? ts.valid_w(t) : ts.valid(t);   // causal: logical order
     if (CAUSAL) {
       const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
       if (lb + kBN > lim_lo) {
@@ -1042,8 +1045,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
         return;
       }
     }
-    mask_tile(s, ts.lead(t), nv, hl);
+    mask_tile(s, CAUSAL ? ts.lead_w(t) : ts.lead(t), nv, hl);
   };
+  // tile lookups of the prologue (logical order when causal)
+  auto reg = [&](int t) { return CAUSAL ? ts.region_w(t) : ts.region(t); };
+  auto bas = [&](int t) { return CAUSAL ? ts.base_w(t) : ts.base(t); };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
   const RawPtrs rp = raw_ptrs(a.keys, h, tid);
   if (tid == 0) s_flag = 0;
@@ -1051,10 +1057,10 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   Stage5 st;
   StageR sr;
   if constexpr (RAW) {
-    loadR(sr, rp, a, tid, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
+    loadR(sr, rp, a, tid, reg(0), bas(0), reg(0), bas(0));
     loadR_table(sr, rp, a, tid);
   } else {
-    load5(st, tp, ts.region(0), ts.base(0), ts.region(0), ts.base(0));
+    load5(st, tp, reg(0), bas(0), reg(0), bas(0));
   }
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
@@ -1065,11 +1071,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   {
     const int t1 = min(1, last);
     if constexpr (RAW) {
-      loadR(sr, rp, a, tid, ts.region(t1), ts.base(t1), 0, 0);
+      loadR(sr, rp, a, tid, reg(t1), bas(t1), 0, 0);
       loadR_table(sr, rp, a, tid);
       storeR(sr, rp, lks[1], lvs[1], tid, true, false);
     } else {
-      load5(st, tp, ts.region(t1), ts.base(t1), 0, 0);
+      load5(st, tp, reg(t1), bas(t1), 0, 0);
       store5(st, lks[1], lvs[1], tid, true, false);
     }
   }

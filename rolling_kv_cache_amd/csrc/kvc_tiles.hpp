@@ -17,6 +17,16 @@ constexpr int kBN = 64;   // keys per tile
 KVC_HD int imin(int a, int b) { return a < b ? a : b; }
 KVC_HD int imax(int a, int b) { return a > b ? a : b; }
 
+// a (bit = 0) or b (bit = 1), by arithmetic on a bit the optimizer cannot see
+// through: a select between two fields of a struct on a computed bit becomes a
+// load from a computed address, which keeps the struct in scratch memory.
+KVC_HD int pick(int bit, int a, int b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("" : "+v"(bit));
+#endif
+  return a + bit * (b - a);
+}
+
 // Key tiles in visiting order.  Logical order: the tiles covering region 0's
 // visible slots [lo0, n0), then region 1's.  Edges-last order (any order
 // gives the same softmax when no row's keys depend on the order, i.e. without
@@ -43,23 +53,26 @@ struct TileSeq {
     const int jt = it + first;
     return (jt < f0 ? w00 + jt : w01 + jt - f0) * kBN;
   }
+  KVC_HD int valid_w(int it) const { return (it + first < f0 ? n0 : n1) - base_w(it); }
+  KVC_HD int lead_w(int it) const { return (it + first < f0 ? lo0 : lo1) - base_w(it); }
   // (tile index << 1) | range of any tile of the sequence
   KVC_HD int at(int it) const {
     const int jt = it + first;
     if (jt < f0 + f1) return (base_w(it) / kBN) << 1 | region_w(it);
     const int b = (epos >> (2 * (jt - f0 - f1))) & 3;
-    const int te = (b & 1) ? ((b & 2) ? t1last : t0last) : ((b & 2) ? t01 : t00);
-    return (te << 1) | (b >> 1);
+    const int r = b >> 1;
+    const int te = pick(b & 1, pick(r, t00, t01), pick(r, t0last, t1last));
+    return (te << 1) | r;
   }
   KVC_HD int region(int it) const { return at(it) & 1; }
   KVC_HD int base(int it) const { return (at(it) >> 1) * kBN; }
   KVC_HD int valid(int it) const {
     const int x = at(it);
-    return ((x & 1) ? n1 : n0) - (x >> 1) * kBN;
+    return pick(x & 1, n0, n1) - (x >> 1) * kBN;
   }
   KVC_HD int lead(int it) const {
     const int x = at(it);
-    return ((x & 1) ? lo1 : lo0) - (x >> 1) * kBN;
+    return pick(x & 1, lo0, lo1) - (x >> 1) * kBN;
   }
   // tiles of the sequence, counted from `first`, that need no mask (edges-last order)
   KVC_HD int whole_prefix(int n) const { return imax(0, imin(n, f0 + f1 - first)); }
