@@ -31,10 +31,18 @@
 //    (whose maximum moves only when a tile exceeds it by more than 8).  The
 //    row sum is accumulated from the packed bf16 P with v_dot2_f32_bf16, i.e.
 //    from the same rounded probabilities the P.V product uses;
+//  * key tiles are visited whole tiles first, the few edge tiles of each range
+//    (kvc_tiles.hpp) last, so every step but the last two runs without mask
+//    code; block-causal attention keeps the logical order and skips the mask
+//    on the tiles every row of the block sees;
 //  * queries are rotated (3D RoPE, fp32, no FMA) and rounded to bf16 in the
 //    prologue, exactly as the cache rotates keys;
 //  * workgroup -> (head, query block) mapping is XCD-aware: consecutive
-//    blocks of the same head land on the same XCD so they share its L2.
+//    blocks of the same head land on the same XCD so they share its L2;
+//    block-causal units are dealt longest first, round-robin over the XCDs;
+//  * launches with fewer workgroups than CUs split the keys into parts (same
+//    kernels, a part index, partial O with its reference and row sum) and
+//    merge them in a second pass.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
