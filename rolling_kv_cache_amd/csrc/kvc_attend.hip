@@ -22,8 +22,9 @@
 //    (K rows 272 B, V^T rows 144 B): every operand read is a per-lane base plus
 //    an immediate, and any 16 consecutive lanes hit 16 distinct bank groups;
 //  * the softmax of tile t is interleaved instruction by instruction with the
-//    QK^T MFMAs of tile t+1 (sched_group_barrier), and four LDS operand reads
-//    stay in flight ahead of every MFMA;
+//    QK^T MFMAs of tile t+1 (sched_group_barrier), and four (six in the
+//    fixed-reference kernel's QK^T) LDS operand reads stay in flight ahead of
+//    every MFMA;
 //  * softmax in the log2 domain (exp2 with log2(e)/sqrt(D) folded into one
 //    FMA) against a fixed per-row reference (the row's maximum over tile 0),
 //    so no tile needs a maximum or an O rescale; blocks whose probabilities
@@ -1001,7 +1002,7 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[kb][hf])));
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);     // six operand reads ahead (eight spill)
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
