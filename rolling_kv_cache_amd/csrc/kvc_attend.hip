@@ -1163,25 +1163,6 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     store_out(a, o, lsum, qrow, h, hl);
 }
 
-// key parts for a split launch (one workgroup per CU at a time): the count in
-// 2..8 whose workgroups fill the last round of 256 CUs best, when that beats
-// the unsplit launch's fill by more than 2 % (ties: fewer parts), with at
-// least four tiles per part and kSplitRows rows of partials; 1 = no split
-static int split_parts(int total, int ntiles) {
-  auto fill = [](int wgs) { return (double)wgs / (256.0 * ((wgs + 255) / 256)); };
-  int best = 1;
-  double best_fill = fill(total);
-  for (int kp = 2; kp <= 8; ++kp) {
-    if (kp * 4 > ntiles || (int64_t)kp * total * 256 > kSplitRows) break;
-    const double f = fill(kp * total);
-    if (f > best_fill + 0.02) {
-      best = kp;
-      best_fill = f;
-    }
-  }
-  return best;
-}
-
 template <int VAR, bool RAW>
 static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int bm = (VAR == 2 || VAR == 4 || VAR == 5 || VAR == 6 || VAR == 7) ? 256 : kBM;

@@ -114,6 +114,9 @@ int32_t kvr_tile_order(int32_t lo0, int32_t n0, int32_t lo1, int32_t n1, int32_t
   return s.whole_prefix(count);
 }
 
+// the key-part count of a split attention launch with `total` workgroups over `ntiles` key tiles
+int32_t kvr_split_parts(int32_t total, int32_t ntiles) { return kvc::split_parts(total, ntiles); }
+
 int32_t kvr_causal_clean_steps(int32_t n0, int32_t n1, int32_t ntile0, int32_t nt, int32_t lim_lo) {
   return kvc::causal_clean_steps(n0, n1, ntile0, nt, lim_lo);
 }

@@ -136,4 +136,25 @@ KVC_HD int causal_clean_steps(int n0, int n1, int ntile0, int nt, int lim_lo) {
   return imax(0, imin(c, nt - 1));
 }
 
+// key parts for a split launch (one workgroup per CU at a time): the count in
+// 2..8 whose workgroups fill the last round of 256 CUs best, when that beats
+// the unsplit launch's fill by more than 2 % (ties: fewer parts), with at
+// least four tiles per part and kSplitRows rows of partials (the split
+// buffers' size: kparts * workgroups * 256 rows never exceeds it); 1 = no
+// split.  Host code.
+inline int split_parts(int total, int ntiles) {
+  auto fill = [](int wgs) { return (double)wgs / (256.0 * ((wgs + 255) / 256)); };
+  int best = 1;
+  double best_fill = fill(total);
+  for (int kp = 2; kp <= 8; ++kp) {
+    if (kp * 4 > ntiles || (int64_t)kp * total * 256 > kSplitRows) break;
+    const double f = fill(kp * total);
+    if (f > best_fill + 0.02) {
+      best = kp;
+      best_fill = f;
+    }
+  }
+  return best;
+}
+
 }  // namespace kvc

@@ -9,7 +9,9 @@ exactly once, if the tiles it reports as whole really are whole, and if the
 whole-tile lookup the pipelined steps use agrees with the general one wherever
 those steps reach -- also for every part of a split-key launch.  The
 block-causal kernels keep the logical order and count their mask-free steps in
-closed form, checked here against the definition.
+closed form, checked here against the definition.  The key-part count of a
+split launch (same header) is checked against its rule and against the split
+buffers' size.
 """
 import ctypes
 import os
@@ -139,3 +141,26 @@ def test_causal_clean_steps_closed_form(tiles):
         while c + 1 < nt and qualifies(c + 1):
             c += 1
         assert tiles.kvr_causal_clean_steps(n0, n1, nt0, nt, lim_lo) == c, (n0, n1, nt, lim_lo)
+
+
+def test_split_parts(tiles):
+    """The key-part count of a split launch: 2..8 parts only when that fills the last round of 256 CUs
+    better than the unsplit launch (by more than 2 %), each part holding at least four tiles, and never
+    more partial rows (parts x workgroups x 256) than the split buffers hold (512 x 256)."""
+    tiles.kvr_split_parts.restype = ctypes.c_int32
+    tiles.kvr_split_parts.argtypes = [ctypes.c_int32, ctypes.c_int32]
+
+    def fill(w):
+        return w / (256.0 * ((w + 255) // 256))
+    for total in range(1, 256):
+        for ntiles in (1, 4, 7, 8, 16, 31, 32, 100, 439, 561):
+            k = tiles.kvr_split_parts(total, ntiles)
+            assert 1 <= k <= 8
+            if k == 1:
+                continue
+            assert k * 4 <= ntiles and k * total * 256 <= 512 * 256, (total, ntiles, k)
+            assert fill(k * total) > fill(total) + 0.02, (total, ntiles, k)
+            allowed = [kp for kp in range(2, 9) if kp * 4 <= ntiles and kp * total * 256 <= 512 * 256]
+            assert fill(k * total) >= max(fill(kp * total) for kp in allowed) - 0.02, (total, ntiles, k)
+    assert tiles.kvr_split_parts(95, 439) == 5        # one GPU's 5-head share of the C3 layer
+    assert tiles.kvr_split_parts(228, 561) == 1       # 12 heads x 19 blocks: as full unsplit as split
