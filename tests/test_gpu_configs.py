@@ -196,3 +196,44 @@ def test_head_share_split_keys():
         os.environ.pop("KVC_ATTEND_SPLIT", None)
     check_attention(out1[rows], ref, "head share unsplit")
     log(f"head share split: max_abs {mx:.3e} rel_rms {rr:.3e}")
+
+
+@pytest.mark.parametrize("raw_keys", [False, True])
+def test_attention_kernel_variants(raw_keys):
+    """The kernels kept for A/B timing beside the default fixed-reference kernel: the running-maximum
+    8-wave kernel alone (KVC_ATTEND_VARIANT=v5) and the 4-wave kernel with two workgroups per CU (v3, no
+    raw-key path).  Every kernel matches the oracle on sampled rows, and v3 matches v5 on every row (the
+    same online softmax; v5 visits whole key tiles before edge tiles and v3 keeps the logical order, so
+    their fp32 sums round differently and the outputs agree to rounding, not bit for bit).  The cache is
+    8 heads of the 14B-shaped layer after two evictions, so the ring holds two key regions with edge
+    tiles."""
+    import os
+    from oracle import OracleCache
+    w = WORKLOADS["c3"]
+    H = 8
+    S = w.frame_seqlen
+    from rolling_kv_cache_amd import KVCache
+    import torch
+    gc = KVCache(w.sink_frames, w.window_frames, S, H, w.head_dim, w.grid_w, torch.bfloat16, raw_keys=raw_keys)
+    oc = OracleCache(w.sink_frames, w.window_frames, S, H, w.head_dim, w.grid_w, w.dtype, raw_keys=raw_keys)
+    q = None
+    for i in range(8):
+        q, k, v = (x[:, :H].copy() for x in chunk_inputs(w, i))
+        gc.append(dev(k, w), dev(v, w), 3 * i)
+        oc.append(k, v, 3, 3 * i)
+    rows = np.sort(np.random.default_rng(78).choice(q.shape[0], size=384, replace=False))
+    ref = oc.attend(q, 3, 21, rows=rows)
+    outs = {}
+    for var in ["", "v5"] + ([] if raw_keys else ["v3"]):
+        if var:
+            os.environ["KVC_ATTEND_VARIANT"] = var
+        try:
+            log(f"attention variant {var or 'default'} raw_keys={raw_keys}")
+            outs[var] = gc.attend(dev(q, w), 21).float().cpu().numpy()
+        finally:
+            os.environ.pop("KVC_ATTEND_VARIANT", None)
+        mx, rr = check_attention(outs[var][rows], ref, f"variant {var or 'default'}")
+        log(f"variant {var or 'default'}: max_abs {mx:.3e} rel_rms {rr:.3e}")
+    if "v3" in outs:
+        mx, rr = check_attention(outs["v3"], outs["v5"], "v3 vs v5, all rows")
+        log(f"v3 vs v5: max_abs {mx:.3e} rel_rms {rr:.3e}")
