@@ -155,7 +155,8 @@ def main():
     torch.cuda.synchronize()
     score_ms = back_to_back_ms(stream, ev, lambda: cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1],
                                                               out=sc_out), n=6)
-    extras = sink_push_and_compact(dev, stream, flush, ev)
+    extras = ceilings(dev, stream, ev)
+    extras.update(sink_push_and_compact(dev, stream, flush, ev))
     extras.update(per_gpu_share(dev, stream, ev, w))
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
     extras.update(raw_keys_ab(dev, stream, ev, flush, w))
@@ -242,6 +243,60 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def ceilings(dev, stream, ev):
+    """This board's own ceilings beside the published peaks (probe kernels of libkvc_probe.so, not the
+    product): the sustained bf16 matrix-core rate of v_mfma_f32_32x32x16_bf16 (four independent chains per
+    wave, four waves per SIMD on every CU) with the shader clock it ran at (shader-clock cycles over
+    constant-rate wall-clock ticks, per workgroup), and plain streaming kernels over 2 GiB buffers (16-byte
+    vectors, four in flight per thread, grid-stride): read, copy, write, and copy with non-temporal stores,
+    each the best of a few grid sizes (median of 3 runs per size)."""
+    import ctypes
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "rolling_kv_cache_amd", "libkvc_probe.so"))
+    vp = ctypes.c_void_p
+    lib.kvc_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.kvc_probe_hbm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    lib.kvc_probe_wall_clock_khz.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    sp = vp(stream.cuda_stream)
+    out = {}
+    blocks, iters = 4 * 256, 4096
+    fo = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    tk = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
+    call = lambda: lib.kvc_probe_mfma(blocks, iters, vp(fo.data_ptr()), vp(tk.data_ptr()), sp)
+    assert call() == 0
+    torch.cuda.synchronize()
+    ms = back_to_back_ms(stream, ev, call, n=5)
+    flop = blocks * 4.0 * iters * 4 * 32 * 32 * 16 * 2
+    khz = ctypes.c_int()
+    lib.kvc_probe_wall_clock_khz(torch.cuda.current_device(), ctypes.byref(khz))
+    t = tk.view(blocks, 2).cpu().numpy().astype(np.float64)
+    clock_mhz = float(np.mean(t[:, 0] / (t[:, 1] / (khz.value * 1e3)))) / 1e6 if khz.value > 0 else None
+    out["mfma_bf16_tflops_measured"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    out["mfma_clock_mhz_under_load"] = round(clock_mhz, 0) if clock_mhz else None
+    if clock_mhz:
+        # the same MFMA stream at the nominal 2.4 GHz clock would reach the published peak
+        out["mfma_peak_at_measured_clock_tflops"] = round(PEAK_BF16_TFLOPS * clock_mhz / 2400.0, 1)
+    del fo, tk
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b.fill_(2)
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
+    for mode, name, nbytes in ((0, "read", n), (1, "copy", 2 * n), (2, "write", n), (3, "copy_nt", 2 * n)):
+        best = 0.0
+        for grid in (1024, 2048, 4096, 16384):
+            f = lambda: lib.kvc_probe_hbm(mode, vp(a.data_ptr()), vp(b.data_ptr()), n, grid, vp(sink.data_ptr()), sp)
+            assert f() == 0
+            torch.cuda.synchronize()
+            ms = back_to_back_ms(stream, ev, f, n=3)
+            best = max(best, nbytes / (ms * 1e-3) / 1e9)
+        out[f"hbm_{name}_GBps_measured"] = round(best, 1)
+    del a, b, sink
+    return out
+
+
 def sink_push_and_compact(dev, stream, flush, ev):
     """The remaining data-movement kernels at their workloads' shapes, MALL flushed before each sample:
     a Rolling-Sink push of one 3-frame bank block (12 heads x 1560-token frames, 15 sink + 6 window frames,
@@ -325,7 +380,6 @@ def per_gpu_share(dev, stream, ev, w):
     """Attention at one GPU's share of the 40-head layer when heads are split over 8 GPUs: 5 heads, the same
     4680 queries over 28080 keys (19 query blocks x 5 heads = 95 workgroups for 256 CUs): split keys (the
     cache reserves the split buffers), and the unsplit launch for comparison."""
-    import os
     import numpy as np
     import torch
     import rolling_kv_cache_amd as kvc
@@ -339,15 +393,14 @@ def per_gpu_share(dev, stream, ev, w):
         q = q_
     flop = 4.0 * Hs * q.shape[0] * c.info()["n_valid"] * D
     res = {}
-    for tag, env in (("", None), ("_unsplit", "0")):
-        if env is not None:
-            os.environ["KVC_ATTEND_SPLIT"] = env
+    for tag, no_split in (("", False), ("_unsplit", True)):
+        c.set_paths(no_split=no_split)
         try:
             out = c.attend(q, 15)
             torch.cuda.synchronize()
             ms = back_to_back_ms(stream, ev, lambda: c.attend(q, 15, out=out))
         finally:
-            os.environ.pop("KVC_ATTEND_SPLIT", None)
+            c.set_paths()
         res[f"attend_5head_share{tag}_ms"] = round(ms, 4)
         res[f"attend_5head_share{tag}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
     return res
@@ -377,8 +430,9 @@ def block_causal_clip(dev, stream, ev, w, block_frames=3):
 
 
 def raw_keys_ab(dev, stream, ev, flush, w):
-    """The bench chunk on a raw-key cache (same 40-head, 28080-key shape): attention rotates every key's
-    time band while staging it, and a retime of the whole cache only rewrites 28080 time indices."""
+    """The bench chunk on a raw-key cache (same 40-head, 28080-key shape): each attend first places every
+    key's time band at its slot's current time in one pass over the time-band plane, then runs the plain
+    attention kernels; a retime of the whole cache only rewrites 28080 time indices."""
     import numpy as np
     import torch
     import rolling_kv_cache_amd as kvc

@@ -169,8 +169,27 @@ kvc_status kvc_create_group(int32_t n_layers, int32_t sink_frames, int32_t windo
 /* Free host state; the workspace stays the caller's. */
 kvc_status kvc_destroy(kvc_handle h);
 
-/* Change the stream later calls enqueue on. */
+/* Change the stream later calls enqueue on.  The new stream is first made to
+ * wait (hipStreamWaitEvent) for the work already queued on the old one, so
+ * later calls see the cache as that work leaves it; nothing else is
+ * synchronized. */
 kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
+
+/* Kernel paths (bits for kvc_set_paths; 0 selects the default kernels).  They
+ * exist to compare the kernels against each other and to test each one; every
+ * path gives results within the attention tolerance of the others, and the
+ * cache state they leave is identical.
+ *  KVC_PATH_RUNNING_MAX  attention: the running-maximum kernel alone instead
+ *                        of the fixed per-row reference with its recompute pass
+ *  KVC_PATH_GENERAL      attention and scores: the general one-thread-per-row
+ *                        passes (the only ones for fp32 or head_dim 64 caches)
+ *  KVC_PATH_NO_SPLIT     attention: never split the keys (KVC_CREATE_SPLIT_ATTEND) */
+#define KVC_PATH_RUNNING_MAX 1u
+#define KVC_PATH_GENERAL 2u
+#define KVC_PATH_NO_SPLIT 4u
+/* Select the kernel paths of later calls on this handle.  EINVAL for unknown
+ * bits. */
+kvc_status kvc_set_paths(kvc_handle h, uint32_t paths);
 
 /* Append n_frames new frames at time indices t_index .. t_index+n_frames-1.
  * k, v: device, [n_frames*frame_seqlen, heads, head_dim] raw (un-rotated) keys
@@ -183,9 +202,11 @@ kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
  * flags: KVC_APPEND_REPLACE_NEWEST re-writes the newest chunk in place (its
  * frame count must match).  EINVAL if n_frames*frame_seqlen exceeds the
  * window, or |t_index|+n_frames exceeds KVC_MAX_POS.  k and v must be
- * finite: attention weights the unused slots of a partial key tile by exactly
- * zero, so a non-finite value left in a slot after its entry was dropped by a
- * compaction can still reach a later attend's output. */
+ * finite for attention to be defined: attention weights the unused slots of a
+ * partial key tile by exactly zero, so a non-finite value left in a slot after
+ * its entry was dropped by a compaction can still reach a later attend's
+ * output.  (Storage itself is defined for any input: a NaN is stored as the
+ * quiet bf16 NaN 0x7FC0 with its sign, infinities as infinities.) */
 kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_frames, int32_t t_index,
                       uint32_t flags);
 

@@ -24,11 +24,15 @@ KVC_CREATE_COMPACT = 1
 KVC_CREATE_RAW_KEYS = 2
 KVC_CREATE_MEMORY = 4
 KVC_CREATE_SPLIT_ATTEND = 8
+KVC_PATH_RUNNING_MAX = 1
+KVC_PATH_GENERAL = 2
+KVC_PATH_NO_SPLIT = 4
 KVC_MAX_POS = 16383
 KVC_MAX_Q_FRAMES = 32
 
 # Every symbol include/kvc.h declares.
-EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_append", "kvc_attend",
+EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_set_paths", "kvc_append",
+            "kvc_attend",
             "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
             "kvc_relax_scores", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
             "kvc_compact", "kvc_sink_push", "kvc_group_workspace_bytes", "kvc_create_group", "kvc_retime_layers",
@@ -70,6 +74,7 @@ def _load():
         "kvc_compact_layers": (ctypes.c_int, [ctypes.POINTER(vp), i32, p32, i32]),
         "kvc_sink_push_layers": (ctypes.c_int, [ctypes.POINTER(vp), i32, i32, i32, i32]),
         "kvc_set_stream": (ctypes.c_int, [vp, vp]),
+        "kvc_set_paths": (ctypes.c_int, [vp, u32]),
         "kvc_append": (ctypes.c_int, [vp, vp, vp, i32, i32, u32]),
         "kvc_attend": (ctypes.c_int, [vp, vp, i32, i32, vp]),
         "kvc_attend_blockcausal": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
@@ -188,8 +193,13 @@ class KVCache:
         return x.shape[0] // self.S
 
     def set_stream(self, stream):
-        self._stream = stream
         _check(lib.kvc_set_stream(self._h, ctypes.c_void_p(stream.cuda_stream)))
+        self._stream = stream
+
+    def set_paths(self, running_max: bool = False, general: bool = False, no_split: bool = False):
+        """Kernel paths of later calls (all False: the default kernels); for comparisons and tests."""
+        _check(lib.kvc_set_paths(self._h, (KVC_PATH_RUNNING_MAX if running_max else 0)
+                                 | (KVC_PATH_GENERAL if general else 0) | (KVC_PATH_NO_SPLIT if no_split else 0)))
 
     # -------------------------------------------------------------- verbs
     def append(self, k, v, t_index: int, replace_newest: bool = False):
@@ -232,6 +242,9 @@ class KVCache:
         n = self.info()["n_valid"]
         if out is None:
             out = torch.empty(n, dtype=torch.float32, device=self.device)
+        elif (out.device.type != "cuda" or out.dtype != torch.float32 or not out.is_contiguous()
+              or out.numel() < n):
+            raise ValueError("out must be a contiguous float32 CUDA tensor of at least n_valid elements")
         _check(lib.kvc_score(self._h, self._tensor(q_win, F, "q_win"), F,
                              q_t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.c_void_p(out.data_ptr()),
                              ctypes.c_void_p(self._score_scratch.data_ptr() + off), need))

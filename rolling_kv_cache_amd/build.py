@@ -1,4 +1,5 @@
-"""Build libkvc.so (HIP for gfx950) and the host-only ring planner library, in-tree.
+"""Build libkvc.so (HIP for gfx950), the benchmark's probe library and the host-only ring planner
+library, in-tree.
 
     python rolling_kv_cache_amd/build.py
 
@@ -20,6 +21,7 @@ INC = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvc.so")
 RING_LIB = os.path.join(HERE, "libkvc_ring_host.so")
+PROBE_LIB = os.path.join(HERE, "libkvc_probe.so")
 
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled for all device code
@@ -30,6 +32,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INC, "-I" + CSRC]
 
 HIP_SOURCES = ["kvc_kernels.hip", "kvc_attend.hip", "kvc_relax.hip"]
 HOST_SOURCES = ["kvc_host.cpp"]
+PROBE_SOURCES = ["kvc_probe.hip"]     # measurement probes for bench.py (not part of libkvc)
 
 
 def _hipcc() -> str:
@@ -58,11 +61,18 @@ def build(verbose: bool = False) -> str:
     for s in HOST_SOURCES:
         o = os.path.join(BUILD, s + ".o")
         jobs.append(([hipcc, "-c", os.path.join(CSRC, s), "-o", o] + HOST_FLAGS, o))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    probe_jobs = []
+    for s in PROBE_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        probe_jobs.append(([hipcc, "-c", "-x", "hip", os.path.join(CSRC, s), "-o", o] + DEVICE_FLAGS, o))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=5) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs + probe_jobs))
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in jobs], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in probe_jobs], verbose)
+    os.replace(tmp, PROBE_LIB)
     # host-only build of the ring planner (no HIP), for CPU tests of the index arithmetic
     tmp = RING_LIB + ".tmp"
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-I" + CSRC, "-o", tmp,

@@ -8,8 +8,7 @@
 // Design (bf16 inputs, fp32 accumulation, head_dim 128):
 //  * workgroup = 8 waves x 32 query rows (one per CU, two waves per SIMD); key
 //    tiles of 64 slots staged in LDS (K + V^T, 35 KB with row padding), double
-//    buffered, one barrier per tile; a 4-wave variant with two workgroups per
-//    CU is kept for comparison (KVC_ATTEND_VARIANT=v3);
+//    buffered, one barrier per tile;
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16, so every lane owns one query
 //    row: the row max needs one exchange between the wave's halves
 //    (v_permlane32_swap), the row sum none;
@@ -48,8 +47,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
-#include <string>
 #include <type_traits>
 
 #include "kvc_common.hip.hpp"
@@ -129,15 +126,6 @@ struct TileRegs {
   u32x4_t k[4];
   u32x4_t v[4];
 };
-
-__device__ __forceinline__ void tile_load(TileRegs& tr, const TilePtrs& p, int r, int base) {
-  const uint16_t* kp = p.k.get<uint16_t>(r) + base * p.kstride;
-  const uint16_t* vp = p.v.get<uint16_t>(r) + (base / kTile) * kVTile;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * p.kstride);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tr.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 2048 * i);
-}
 
 // Rotate this lane's 64 query elements (row qc, halves hl) and pack them as the
 // eight B operands of S^T = K . Q^T.
@@ -219,28 +207,17 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o
 
 
 // ---------------------------------------------------------------------------
-// Interleaved pipeline (v3).  LDS rows are padded by one 16-byte chunk (K rows
+// Interleaved pipeline.  LDS rows are padded by one 16-byte chunk (K rows
 // 272 B, V^T rows 144 B) instead of XOR-swizzled, so every operand read is a
 // per-lane base plus an immediate offset, and any 16 consecutive lanes still
 // hit 16 distinct 16-byte bank slots.  Iteration t issues the global loads of
 // K(t+2) and V(t+1), then computes S^T(t+1) on the matrix cores interleaved
 // instruction by instruction (sched_group_barrier) with the softmax of tile t
-// on the VALU; the rare O rescale and the P.V product of tile t follow.
+// on the VALU; the P.V product of tile t follows.
 constexpr int kKSt = 17;                       // K row stride in 16-byte chunks
 constexpr int kVSt = 9;                        // V^T row stride in 16-byte chunks
 constexpr int kKTileP = kBN * kKSt;            // padded K tile, 16-byte chunks
 constexpr int kVTileP = 128 * kVSt;            // padded V^T tile
-
-__device__ __forceinline__ void tile_store_padded(const TileRegs& tr, u32x4_t* lk, u32x4_t* lv, int tid) {
-  const int c = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lk[((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ci = tid + 256 * i;
-    lv[(ci >> 3) * kVSt + (ci & 7)] = tr.v[i];
-  }
-}
 
 // S^T for one tile into s, with the softmax of the previous tile (sp) woven in:
 // returns P(previous) packed in pb, the tile's row-sum in psum and the scale
@@ -315,101 +292,6 @@ __device__ __forceinline__ void pv_padded(f32x16_t* o, const u32x4_t* lv, int vb
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attend_v3_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
-                                                           int ntile0, int ntiles) {
-  __shared__ u32x4_t lks[2][kKTileP];
-  __shared__ u32x4_t lvs[2][kVTileP];
-  const int wg = blockIdx.x;
-  const int lin = (wg & 7) * per_xcd + (wg >> 3);
-  if (lin >= total) return;
-  const int h = lin / mblocks;
-  const int mb = lin - h * mblocks;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int qrow = mb * kBM + wave * 32 + l32;
-  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
-  const int kbase = perm_row(l32) * kKSt + hl;
-  const int vbase = l32 * kVSt + hl;
-
-  bf16x8_t qf[8];
-  load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
-  const float c2 = a.scale * 1.4426950408889634f;
-  const int last = ntiles - 1;
-
-  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
-  TileRegs tr;
-  // K(0), V(0) -> buffer 0; K(1) -> buffer 1 (tile 0 starts at slot 0 unless attention is limited)
-  tile_load(tr, tp, ts.region(0), ts.base(0));
-  tile_store_padded(tr, lks[0], lvs[0], tid);
-  {
-    const int t1 = min(1, last);
-    tile_load(tr, tp, ts.region(t1), ts.base(t1));
-    const int c = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lks[1][((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
-  }
-  __syncthreads();
-  f32x16_t sa[2], sb[2];
-  {
-    // S^T(0) alone
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kKSt + ks * 2]);
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
-      }
-    }
-    mask_tile(sa, ts.lead(0), ts.valid(0), hl);
-  }
-
-  // one pipeline step: scur holds S^T(t); computes S^T(t+1) into snext
-  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
-    const int tk = min(t + 2, last), tv = min(t + 1, last);
-    // K(t+2) and V(t+1) in flight (clamped at the last tile: harmless re-loads)
-    {
-      const uint16_t* kp = tp.k.get<uint16_t>(ts.region(tk)) + ts.base(tk) * tp.kstride;
-      const uint16_t* vp = tp.v.get<uint16_t>(ts.region(tv)) + (ts.base(tv) / kTile) * kVTile;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i * tp.kstride);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tr.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 2048 * i);
-    }
-    bf16x8_t pb[2][2];
-    float psum, alpha;
-    bool upd;
-    qk_and_softmax(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
-    if (__ballot(upd) != 0) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-    }
-    lsum = lsum * alpha + psum;
-    pv_padded(o, lvs[t & 1], vbase, pb);
-    mask_tile(snext, ts.lead(min(t + 1, last)), ts.valid(min(t + 1, last)), hl);
-    tile_store_padded(tr, lks[t & 1], lvs[(t + 1) & 1], tid);
-    __syncthreads();
-  };
-
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
-  }
-  if (t < ntiles) step(t, sa, sb);
-  store_out(a, o, lsum, qrow, h, hl);
-}
-
 // ---------------------------------------------------------------------------
 // v5: v3's interleaved pipeline with 8 waves (256 query rows) per workgroup.
 // A 32 KB K+V^T tile is then 16 staging registers per thread instead of 32,
@@ -445,119 +327,6 @@ __device__ __forceinline__ void store5(const Stage5& st, u32x4_t* lk, u32x4_t* l
   }
 }
 
-// Raw-key caches store the key's time band un-rotated (the height and width
-// bands, whose positions never change, are stored rotated), and attention
-// places every key at its slot's current time while staging the tile.  Each
-// pair is rotated by one band only, so rotating the stored time band now gives
-// exactly the key a full rotation of the raw key at that time would give (fp32,
-// no FMA, rounded to nearest even).  The 22 time pairs sit in the first six
-// 16-byte chunks of a key row (the KA plane), so the staging map changes for
-// raw tiles: threads 0..383 (waves 0-5) move KA chunk tid (row tid / 6) and
-// rotate it, plus KB chunk tid; threads 384..511 move KB chunks tid and
-// tid + 128 (KB chunk i: row i / 10, column 6 + i % 10).
-struct RawPtrs {
-  RegionPtr ka, kb, v, t;  // region r, head h: key planes, V^T tiles and times (wave-uniform)
-  int o0, o1;              // element offsets of the two chunks in their planes at slot base 0
-  int l0, l1;              // LDS chunk index (row * kKSt + column) of the two chunks
-  int lrow;                // the KA chunk's row in the tile
-  int cpair;               // first pair of the KA chunk (4 * column)
-};
-
-__device__ __forceinline__ RawPtrs raw_ptrs(const KeyRegions& kr, int h, int tid) {
-  RawPtrs p;
-  const bool ka = tid < 384;
-  const int i1 = ka ? tid : tid + 128;
-  p.lrow = tid / 6;
-  p.cpair = 4 * (tid % 6);
-  p.l0 = ka ? p.lrow * kKSt + tid % 6 : (tid / 10) * kKSt + 6 + tid % 10;
-  p.l1 = (i1 / 10) * kKSt + 6 + i1 % 10;
-  p.o0 = tid * 8;
-  p.o1 = i1 * 8;
-  const uint16_t* pka[2];
-  const uint16_t* pkb[2];
-  const uint16_t* pv[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    pka[r] = (const uint16_t*)kr.ka[r] + (int64_t)h * kr.cap[r] * kDA;
-    pkb[r] = (const uint16_t*)kr.kb[r] + (int64_t)h * kr.cap[r] * kDB;
-    pv[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kVTile;
-  }
-  p.ka.set(pka[0], pka[1]);
-  p.kb.set(pkb[0], pkb[1]);
-  p.v.set(pv[0], pv[1]);
-  p.t.set(kr.t[0], kr.t[1]);
-  return p;
-}
-
-struct StageR {
-  u32x4_t k[2];
-  u32x4_t v[2];
-  int t;                   // time of the KA chunk's row
-  float cs[8];             // (cos, sin) of its four pairs at that time
-};
-
-// issue the loads of K tile (rk, bk) and V tile (rv, bv), and the KA row's time
-__device__ __forceinline__ void loadR(StageR& st, const RawPtrs& p, const AttendArgs& a, int tid, int rk, int bk,
-                                      int rv, int bv) {
-  const bool ka = tid < 384;
-  const uint16_t* pa = p.ka.get<uint16_t>(rk);
-  const uint16_t* pb = p.kb.get<uint16_t>(rk);
-  if (ka) {
-    const int slot = bk + p.lrow;
-    st.t = p.t.get<int32_t>(rk)[slot];
-    if (rk == 0 && slot >= a.mem_lo) st.t = a.mem_t[slot - a.mem_lo >= a.geo.S ? 1 : 0];
-    st.k[0] = *reinterpret_cast<const u32x4_t*>(pa + (bk * kDA + p.o0));
-  } else {
-    st.k[0] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o0));
-  }
-  st.k[1] = *reinterpret_cast<const u32x4_t*>(pb + (bk * kDB + p.o1));
-  const uint16_t* vp = p.v.get<uint16_t>(rv) + (bv / kTile) * kVTile + tid * 8;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) st.v[i] = *reinterpret_cast<const u32x4_t*>(vp + 4096 * i);
-}
-
-// the (cos, sin) table entries of the KA chunk's time pairs (issued once its t has arrived)
-__device__ __forceinline__ void loadR_table(StageR& st, const RawPtrs& p, const AttendArgs& a, int tid) {
-  if (tid >= 384) return;
-  const float* tp = a.tab.tcs + ((st.t + a.tab.maxpos) * 22 + p.cpair) * 2;
-  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(tp);
-  u32x4_t hi = {__float_as_uint(1.f), 0u, __float_as_uint(1.f), 0u};
-  if (p.cpair < 20) hi = *reinterpret_cast<const u32x4_t*>(tp + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.cs[i] = __uint_as_float(lo[i]);
-    st.cs[4 + i] = __uint_as_float(hi[i]);
-  }
-}
-
-// rotate the KA chunk's time pairs and write the tile into LDS
-__device__ __forceinline__ void storeR(StageR& st, const RawPtrs& p, u32x4_t* lk, u32x4_t* lv, int tid, bool k,
-                                       bool v) {
-  if (k) {
-    if (tid < 384) {
-      u32x4_t x = st.k[0];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q >= 2 && p.cpair >= 20) break;            // pairs 22, 23 belong to the height band
-        float x0 = __uint_as_float(x[q] << 16), x1 = __uint_as_float(x[q] & 0xFFFF0000u);
-        rot_pair(x0, x1, st.cs[2 * q], st.cs[2 * q + 1]);
-        const bf16x2_t r = {(__bf16)x0, (__bf16)x1};   // round to nearest even, as the cache rounds
-        x[q] = __builtin_bit_cast(uint32_t, r);
-      }
-      st.k[0] = x;
-    }
-    lk[p.l0] = st.k[0];
-    lk[p.l1] = st.k[1];
-  }
-  if (v) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + 512 * i;
-      lv[(ci >> 3) * kVSt + (ci & 7)] = st.v[i];
-    }
-  }
-}
-
 // With only_flagged set, blocks whose flag is 0 exit at once (the recompute
 // pass behind the fixed-reference kernel).  CAUSAL: block-causal attention of
 // a clip -- query row r sees the logical key prefix of length
@@ -569,7 +338,7 @@ __device__ __forceinline__ void storeR(StageR& st, const RawPtrs& p, u32x4_t* lk
 // tiles are cut into kparts contiguous parts, workgroup (head, part, query
 // block) runs over its part only and writes its unnormalised O with the row's
 // reference and sum to the split buffers; merge_split_kernel combines them.
-template <bool CAUSAL, bool RAW>
+template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles, const int32_t* only_flagged,
                                                            int kparts) {
@@ -622,32 +391,16 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   auto reg = [&](int t) { return CAUSAL ? ts.region_w(t) : ts.region(t); };
   auto bas = [&](int t) { return CAUSAL ? ts.base_w(t) : ts.base(t); };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
-  const RawPtrs rp = raw_ptrs(a.keys, h, tid);
 
   Stage5 st;
-  StageR sr;
-  if constexpr (RAW) {
-    loadR(sr, rp, a, tid, reg(0), bas(0), reg(0), bas(0));
-    loadR_table(sr, rp, a, tid);
-  } else {
-    load5(st, tp, reg(0), bas(0), reg(0), bas(0));
-  }
+  load5(st, tp, reg(0), bas(0), reg(0), bas(0));
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-  if constexpr (RAW)
-    storeR(sr, rp, lks[0], lvs[0], tid, true, true);
-  else
-    store5(st, lks[0], lvs[0], tid, true, true);
+  store5(st, lks[0], lvs[0], tid, true, true);
   {
     const int t1 = min(1, last);
-    if constexpr (RAW) {
-      loadR(sr, rp, a, tid, reg(t1), bas(t1), 0, 0);
-      loadR_table(sr, rp, a, tid);
-      storeR(sr, rp, lks[1], lvs[1], tid, true, false);
-    } else {
-      load5(st, tp, reg(t1), bas(t1), 0, 0);
-      store5(st, lks[1], lvs[1], tid, true, false);
-    }
+    load5(st, tp, reg(t1), bas(t1), 0, 0);
+    store5(st, lks[1], lvs[1], tid, true, false);
   }
   f32x16_t o[4];
 #pragma unroll
@@ -672,17 +425,12 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
-    if constexpr (RAW)
-      loadR(sr, rp, a, tid, CAUSAL ? ts.region_w(tk) : ts.region(tk), CAUSAL ? ts.base_w(tk) : ts.base(tk),
-            CAUSAL ? ts.region_w(tv) : ts.region(tv), CAUSAL ? ts.base_w(tv) : ts.base(tv));
-    else
-      load5(st, tp, CAUSAL ? ts.region_w(tk) : ts.region(tk), CAUSAL ? ts.base_w(tk) : ts.base(tk),
-            CAUSAL ? ts.region_w(tv) : ts.region(tv), CAUSAL ? ts.base_w(tv) : ts.base(tv));
+    load5(st, tp, CAUSAL ? ts.region_w(tk) : ts.region(tk), CAUSAL ? ts.base_w(tk) : ts.base(tk),
+          CAUSAL ? ts.region_w(tv) : ts.region(tv), CAUSAL ? ts.base_w(tv) : ts.base(tv));
     bf16x8_t pb[2][2];
     float psum, alpha;
     bool upd;
     qk_and_softmax(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
-    if constexpr (RAW) loadR_table(sr, rp, a, tid);
     if (__ballot(upd) != 0) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -692,10 +440,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     lsum = lsum * alpha + psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
     mask(snext, min(t + 1, last));
-    if constexpr (RAW)
-      storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
-    else
-      store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
 
@@ -1011,7 +756,7 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
   }
 }
 
-template <bool CAUSAL, bool RAW>
+template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
                                                            int ntile0, int ntiles, int kparts) {
   __shared__ u32x4_t lks[2][kKTileP];
@@ -1060,33 +805,17 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   auto reg = [&](int t) { return CAUSAL ? ts.region_w(t) : ts.region(t); };
   auto bas = [&](int t) { return CAUSAL ? ts.base_w(t) : ts.base(t); };
   const TilePtrs tp = tile_ptrs(a.keys, h, tid);
-  const RawPtrs rp = raw_ptrs(a.keys, h, tid);
   if (tid == 0) s_flag = 0;
 
   Stage5 st;
-  StageR sr;
-  if constexpr (RAW) {
-    loadR(sr, rp, a, tid, reg(0), bas(0), reg(0), bas(0));
-    loadR_table(sr, rp, a, tid);
-  } else {
-    load5(st, tp, reg(0), bas(0), reg(0), bas(0));
-  }
+  load5(st, tp, reg(0), bas(0), reg(0), bas(0));
   bf16x8_t qf[8];
   load_query(qf, a, h, min(qrow, a.Lq - 1), hl);
-  if constexpr (RAW)
-    storeR(sr, rp, lks[0], lvs[0], tid, true, true);
-  else
-    store5(st, lks[0], lvs[0], tid, true, true);
+  store5(st, lks[0], lvs[0], tid, true, true);
   {
     const int t1 = min(1, last);
-    if constexpr (RAW) {
-      loadR(sr, rp, a, tid, reg(t1), bas(t1), 0, 0);
-      loadR_table(sr, rp, a, tid);
-      storeR(sr, rp, lks[1], lvs[1], tid, true, false);
-    } else {
-      load5(st, tp, reg(t1), bas(t1), 0, 0);
-      store5(st, lks[1], lvs[1], tid, true, false);
-    }
+    load5(st, tp, reg(t1), bas(t1), 0, 0);
+    store5(st, lks[1], lvs[1], tid, true, false);
   }
   f32x16_t o[4];
 #pragma unroll
@@ -1117,22 +846,15 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     constexpr bool any = decltype(masked)::value && !CAUSAL;
     const int rk = any ? ts.region(tk) : ts.region_w(tk), bk = any ? ts.base(tk) : ts.base_w(tk);
     const int rv = any ? ts.region(tv) : ts.region_w(tv), bv = any ? ts.base(tv) : ts.base_w(tv);
-    if constexpr (RAW)
-      loadR(sr, rp, a, tid, rk, bk, rv, bv);
-    else
-      load5(st, tp, rk, bk, rv, bv);
+    load5(st, tp, rk, bk, rv, bv);
     bf16x8_t pb[2][2];
     float psum;
     qk_and_exp(snext, lks[(t + 1) & 1], qf, kbase, scur, negm, c2, pb, psum);
-    if constexpr (RAW) loadR_table(sr, rp, a, tid);
     pmax = fmaxf(pmax, psum);
     lsum += psum;
     pv_padded(o, lvs[t & 1], vbase, pb);
     if constexpr (decltype(masked)::value) mask(snext, min(t + 1, last));
-    if constexpr (RAW)
-      storeR(sr, rp, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
-    else
-      store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
+    store5(st, lks[t & 1], lvs[(t + 1) & 1], tid, true, true);
     __syncthreads();
   };
   using Masked = std::integral_constant<bool, true>;
@@ -1163,10 +885,11 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     store_out(a, o, lsum, qrow, h, hl);
 }
 
-template <int VAR, bool RAW>
-static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-  const int bm = (VAR == 2 || VAR == 4 || VAR == 5 || VAR == 6 || VAR == 7) ? 256 : kBM;
-  const int mblocks = (a.Lq + bm - 1) / bm;
+// Launch shapes of the matrix-core attention.
+enum class AttendPlan { kFixedRef, kRunningMax, kCausalFixedRef, kCausalRunningMax, kSplit };
+
+static hipError_t attend_launch(const AttendArgs& a, AttendPlan plan, hipStream_t s) {
+  const int mblocks = (a.Lq + 255) / 256;
   const int total = mblocks * a.geo.H;
   const int per_xcd = (total + 7) / 8;
   const int ntile0 = range_tiles(a.keys, 0);
@@ -1175,9 +898,7 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   AttendArgs b = a;
   int n0 = ntile0, nt = ntile0 + ntile1;
   // a region with no valid keys contributes no tiles; keep region 0 non-empty
-  // (memory tokens live in region 0, so there are none when it is empty)
   if (ntile0 == 0) {
-    b.mem_lo = INT32_MAX;
     b.keys.ka[0] = a.keys.ka[1];
     b.keys.kb[0] = a.keys.kb[1];
     b.keys.v[0] = a.keys.v[1];
@@ -1190,68 +911,61 @@ static hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     n0 = ntile1;
     nt = ntile1;
   }
-  if (VAR == 7) {            // split keys: fixed-reference partials, flagged parts again, then the merge
-    const int kp = split_parts(total, nt);
-    const int tot = total * kp, pxcd = (tot + 7) / 8;
-    hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * pxcd), dim3(512), 0, s, b, mblocks, tot, pxcd, n0,
-                       nt, kp);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * pxcd), dim3(512), 0, s, b, mblocks, tot, pxcd, n0, nt,
-                       (const int32_t*)b.flags, kp);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    const int64_t threads = (int64_t)a.geo.H * a.Lq * 32;
-    hipLaunchKernelGGL(merge_split_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, b, kp);
-  } else if (VAR == 2)
-    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)nullptr, 1);
-  else if (VAR == 5)
-    hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)nullptr, 1);
-  else if (VAR == 6) {       // block-causal: fixed reference, then the flagged blocks with the running maximum
-    hipLaunchKernelGGL((attend_v5f_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
-                       per_xcd, n0, nt, 1);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_v5_kernel<true, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)b.flags, 1);
-  } else if (VAR == 4) {
-    hipLaunchKernelGGL((attend_v5f_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total,
-                       per_xcd, n0, nt, 1);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_v5_kernel<false, RAW>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
-                       n0, nt, (const int32_t*)b.flags, 1);
+  const dim3 grid(8 * per_xcd), block(512);
+  switch (plan) {
+    case AttendPlan::kSplit: {   // fixed-reference partials, flagged parts again, then the merge
+      const int kp = split_parts(total, nt);
+      const int tot = total * kp, pxcd = (tot + 7) / 8;
+      hipLaunchKernelGGL((attend_v5f_kernel<false>), dim3(8 * pxcd), block, 0, s, b, mblocks, tot, pxcd, n0, nt, kp);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      hipLaunchKernelGGL((attend_v5_kernel<false>), dim3(8 * pxcd), block, 0, s, b, mblocks, tot, pxcd, n0, nt,
+                         (const int32_t*)b.flags, kp);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      const int64_t threads = (int64_t)a.geo.H * a.Lq * 32;
+      hipLaunchKernelGGL(merge_split_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, b, kp);
+      break;
+    }
+    case AttendPlan::kRunningMax:
+      hipLaunchKernelGGL((attend_v5_kernel<false>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt,
+                         (const int32_t*)nullptr, 1);
+      break;
+    case AttendPlan::kCausalRunningMax:
+      hipLaunchKernelGGL((attend_v5_kernel<true>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt,
+                         (const int32_t*)nullptr, 1);
+      break;
+    case AttendPlan::kCausalFixedRef:   // fixed reference, then the flagged blocks with the running maximum
+      hipLaunchKernelGGL((attend_v5f_kernel<true>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt, 1);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      hipLaunchKernelGGL((attend_v5_kernel<true>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt,
+                         (const int32_t*)b.flags, 1);
+      break;
+    case AttendPlan::kFixedRef:
+      hipLaunchKernelGGL((attend_v5f_kernel<false>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt, 1);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      hipLaunchKernelGGL((attend_v5_kernel<false>), grid, block, 0, s, b, mblocks, total, per_xcd, n0, nt,
+                         (const int32_t*)b.flags, 1);
+      break;
   }
-  else
-    hipLaunchKernelGGL(attend_v3_kernel, dim3(8 * per_xcd), dim3(256), 0, s, b, mblocks, total, per_xcd, n0, nt);
   return hipGetLastError();
 }
 
-// Default: the fixed-reference 8-wave kernel plus the recompute pass (it needs
-// the workspace flags; without them the running-maximum kernel runs alone).
-// KVC_ATTEND_VARIANT=v5 (running maximum, 8 waves) or v3 (4 waves, two
-// workgroups per CU) selects another kernel for A/B timing.
-hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
-  const char* v = std::getenv("KVC_ATTEND_VARIANT");
-  // fewer workgroups than CUs: split the keys when the workspace holds the partials
-  // (KVC_ATTEND_SPLIT=0 turns this off for comparisons)
-  if (a.split_o && a.causal_block == 0 && !(std::getenv("KVC_ATTEND_SPLIT") &&
-                                            std::string(std::getenv("KVC_ATTEND_SPLIT")) == "0")) {
+// Default: the fixed-reference kernel plus the recompute pass (it needs the
+// workspace flags; without them the running-maximum kernel runs alone); split
+// keys for launches with fewer workgroups than CUs when the workspace holds
+// the partials.  kPathRunningMax / kPathNoSplit select the alternatives.  Keys
+// must be stored rotated (a raw-key cache's time band is placed first).
+hipError_t launch_attend_mfma(const AttendArgs& a, uint32_t paths, hipStream_t s) {
+  if (a.raw) return hipErrorInvalidValue;
+  const bool running_max = (paths & kPathRunningMax) != 0 || a.flags == nullptr;
+  if (a.split_o && a.causal_block == 0 && !(paths & kPathNoSplit) && !running_max) {
     const int total = (a.Lq + 255) / 256 * a.geo.H;
     const int kp = split_parts(total, range_tiles(a.keys, 0) + range_tiles(a.keys, 1));
     if (total < 256 && kp >= 2 && (int64_t)kp * a.geo.H * a.Lq <= kSplitRows)
-      return a.raw ? attend_launch<7, true>(a, s) : attend_launch<7, false>(a, s);
+      return attend_launch(a, AttendPlan::kSplit, s);
   }
-  if (a.raw) {
-    // raw-key caches: the 8-wave kernels only (the 4-wave variant has no time-band staging)
-    if (a.causal_block > 0) return (a.flags && !(v && std::string(v) == "v5")) ? attend_launch<6, true>(a, s)
-                                                                              : attend_launch<5, true>(a, s);
-    if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, true>(a, s);
-    return attend_launch<4, true>(a, s);
-  }
-  if (a.causal_block > 0) return (a.flags && !(v && std::string(v) == "v5")) ? attend_launch<6, false>(a, s)
-                                                                            : attend_launch<5, false>(a, s);
-  if (v && std::string(v) == "v3") return attend_launch<0, false>(a, s);
-  if ((v && std::string(v) == "v5") || a.flags == nullptr) return attend_launch<2, false>(a, s);
-  return attend_launch<4, false>(a, s);
+  if (a.causal_block > 0)
+    return attend_launch(a, running_max ? AttendPlan::kCausalRunningMax : AttendPlan::kCausalFixedRef, s);
+  return attend_launch(a, running_max ? AttendPlan::kRunningMax : AttendPlan::kFixedRef, s);
 }
 
 }  // namespace kvc

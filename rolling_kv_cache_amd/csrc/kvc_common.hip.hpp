@@ -11,13 +11,15 @@ namespace kvc {
 
 // bfloat16 <-> float.  Storage rounding is round-to-nearest-even written out
 // on the bit pattern so the cache contents do not depend on a conversion
-// instruction's denormal mode.
+// instruction's denormal mode.  A NaN is stored as the quiet NaN 0x7FC0 with
+// its sign (adding the rounding bias to a NaN pattern could carry into the
+// exponent and turn it into an infinity or a zero).
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) & 0x8000u) | 0x7FC0u : r);
 }
 
 template <typename T>

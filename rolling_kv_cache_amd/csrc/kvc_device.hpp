@@ -24,6 +24,12 @@ namespace kvc {
 constexpr int kTile = 64;        // slots per V tile / attention key tile
 constexpr int kMaxSegs = 4;
 
+// Kernel-path bits (kvc_set_paths): alternatives to the default kernels, for
+// comparisons and tests.
+constexpr uint32_t kPathRunningMax = 1u;  // attention: the running-maximum kernel alone
+constexpr uint32_t kPathGeneral = 2u;     // attention and scores: the general per-row passes
+constexpr uint32_t kPathNoSplit = 4u;     // attention: never split keys
+
 struct RegionPtrs {
   void* ka;
   void* kb;

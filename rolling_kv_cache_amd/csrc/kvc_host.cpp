@@ -5,7 +5,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -16,6 +15,9 @@
 #include "kvc_ring.hpp"
 
 static_assert(KVC_MAX_POS == kvc::kMaxPos, "time table range");
+static_assert(KVC_PATH_RUNNING_MAX == kvc::kPathRunningMax && KVC_PATH_GENERAL == kvc::kPathGeneral &&
+                  KVC_PATH_NO_SPLIT == kvc::kPathNoSplit,
+              "path bits");
 
 namespace {
 
@@ -129,10 +131,14 @@ struct kvc_cache {
   void* bank_v;
   int32_t* keep_dev;
   int32_t* att_flags;
-  int32_t* keep_pinned;
-  hipEvent_t keep_evt;
-  bool keep_pending;
+  int32_t* keep_pinned;      // two halves of WP entries: the host fills one while the other may still be read
+  int32_t* keep_pinned_dev;  // the same memory's device-visible address
+  hipEvent_t keep_evt[2];    // recorded after the staging kernel that reads each half
+  bool keep_pending[2];
+  int32_t keep_half;
+  hipEvent_t order_evt;      // kvc_set_stream: the new stream waits for the old one's queued work
   hipStream_t stream;
+  uint32_t paths;            // kPath* bits (kvc_set_paths)
   kvc::RingState st;
   bool poisoned;
   float mem_alpha[2];
@@ -422,7 +428,10 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->keep_dev = (int32_t*)(h->ws + L.keep);
   h->att_flags = (int32_t*)(h->ws + L.att_flags);
   h->keep_pinned = nullptr;
-  h->keep_pending = false;
+  h->keep_pinned_dev = nullptr;
+  h->keep_pending[0] = h->keep_pending[1] = false;
+  h->keep_half = 0;
+  h->paths = 0;
   h->max_keys = 0;
   h->group = nullptr;
   h->layer = 0;
@@ -431,12 +440,20 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   h->mem_alpha[1] = 0.5f;
   h->mem_frames = 0;
   h->st.init(frame_seqlen, L.S_tok, L.W_tok);
-  hipError_t e = hipSuccess;
+  hipError_t e = hipEventCreateWithFlags(&h->order_evt, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(KVC_ENOMEM, std::string("event: ") + hipGetErrorString(e));
+  }
   if (create_flags & KVC_CREATE_COMPACT) {
-    e = hipHostMalloc((void**)&h->keep_pinned, (size_t)L.WP * 4, hipHostMallocDefault);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->keep_evt, hipEventDisableTiming);
+    int n_evt = 0;
+    e = hipHostMalloc((void**)&h->keep_pinned, (size_t)2 * L.WP * 4, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&h->keep_pinned_dev, h->keep_pinned, 0);
+    for (; e == hipSuccess && n_evt < 2; ++n_evt) e = hipEventCreateWithFlags(&h->keep_evt[n_evt], hipEventDisableTiming);
     if (e != hipSuccess) {
+      for (int i = 0; i < n_evt; ++i) (void)hipEventDestroy(h->keep_evt[i]);
       if (h->keep_pinned) (void)hipHostFree(h->keep_pinned);
+      (void)hipEventDestroy(h->order_evt);
       delete h;
       return fail(KVC_ENOMEM, std::string("pinned staging: ") + hipGetErrorString(e));
     }
@@ -454,8 +471,10 @@ kvc_status kvc_create(int32_t sink_frames, int32_t window_frames, int32_t frame_
   if (e != hipSuccess) {
     if (h->keep_pinned) {
       (void)hipHostFree(h->keep_pinned);
-      (void)hipEventDestroy(h->keep_evt);
+      (void)hipEventDestroy(h->keep_evt[0]);
+      (void)hipEventDestroy(h->keep_evt[1]);
     }
+    (void)hipEventDestroy(h->order_evt);
     delete h;
     return fail(KVC_EDEVICE, std::string("create: ") + hipGetErrorString(e));
   }
@@ -503,17 +522,34 @@ kvc_status kvc_create_group(int32_t n_layers, int32_t sink_frames, int32_t windo
 kvc_status kvc_destroy(kvc_handle h) {
   if (!h) return fail(KVC_EINVAL, "null handle");
   if (h->keep_pinned) {
-    if (h->keep_pending) (void)hipEventSynchronize(h->keep_evt);
-    (void)hipEventDestroy(h->keep_evt);
+    for (int i = 0; i < 2; ++i) {
+      if (h->keep_pending[i]) (void)hipEventSynchronize(h->keep_evt[i]);
+      (void)hipEventDestroy(h->keep_evt[i]);
+    }
     (void)hipHostFree(h->keep_pinned);
   }
+  (void)hipEventDestroy(h->order_evt);
   delete h;
   return KVC_OK;
 }
 
 kvc_status kvc_set_stream(kvc_handle h, void* hip_stream) {
   if (kvc_status s = check(h)) return s;
-  h->stream = (hipStream_t)hip_stream;
+  const hipStream_t ns = (hipStream_t)hip_stream;
+  if (ns != h->stream) {
+    // work already queued on the old stream (which may read or write the workspace) comes first
+    hipError_t e = hipEventRecord(h->order_evt, h->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ns, h->order_evt, 0);
+    if (kvc_status s = device_result(h, e, "set_stream")) return s;
+  }
+  h->stream = ns;
+  return KVC_OK;
+}
+
+kvc_status kvc_set_paths(kvc_handle h, uint32_t paths) {
+  if (kvc_status s = check(h)) return s;
+  if (paths & ~(KVC_PATH_RUNNING_MAX | KVC_PATH_GENERAL | KVC_PATH_NO_SPLIT)) return fail(KVC_EINVAL, "unknown path bit");
+  h->paths = paths;
   return KVC_OK;
 }
 
@@ -642,14 +678,10 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
     a.mem_t[1] = t_w - 1;
     a.keys.n[0] = h->L.S_tok + 2 * h->S;
   }
-  const bool force_general = std::getenv("KVC_ATTEND_GENERAL") != nullptr;
   hipError_t e = hipSuccess;
-  // raw keys: placed once, then the plain matrix-core kernels (KVC_RAW_ATTEND=lds keeps the rotation of
-  // every staged tile inside the kernels instead, for comparison)
-  const char* ra = std::getenv("KVC_RAW_ATTEND");
-  if (a.raw && h->L.placed_win != 0 && !force_general && !(ra && std::string(ra) == "lds"))
-    e = launch_placed_attend(h, a);
-  if (e == hipSuccess) e = kvc::launch_attend(a, h->stream, force_general);
+  // raw keys on the matrix-core path: the time band placed once, then the plain kernels
+  if (a.raw && h->L.placed_win != 0 && !(h->paths & KVC_PATH_GENERAL)) e = launch_placed_attend(h, a);
+  if (e == hipSuccess) e = kvc::launch_attend(a, h->paths, h->stream);
   return device_result(h, e, "attend");
 }
 
@@ -756,7 +788,7 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   a.scale = (float)(1.0 / std::sqrt((double)h->D));
   hipError_t e = hipSuccess;
   if (h->cflags & KVC_CREATE_RAW_KEYS) e = launch_placed_ka(h, p, &a.keys);
-  if (e == hipSuccess) e = kvc::launch_score(a, h->stream, std::getenv("KVC_ATTEND_GENERAL") != nullptr);
+  if (e == hipSuccess) e = kvc::launch_score(a, h->paths, h->stream);
   return device_result(h, e, "score");
 }
 
@@ -857,18 +889,25 @@ static kvc_status compact_layers(const kvc_handle* hs, int32_t nl, const int32_t
   if (!kvc::plan_compact(nx, keep_idx, n_keep, &src, &err)) return fail(KVC_EINVAL, err);
   hipError_t e = hipSuccess;
   if (!src.empty()) {
-    // the source slots go up once, into the first layer's workspace, and serve every layer
-    if (h->keep_pending) {
-      e = hipEventSynchronize(h->keep_evt);
-      h->keep_pending = false;
+    // The source slots go up once, into the first layer's workspace, and serve every layer: the host
+    // writes them to one half of the pinned staging buffer and a small kernel copies them to the device
+    // (a stream copy of a few tens of KB costs several times longer).  The half used two calls ago is
+    // rewritten only after its staging kernel has run.
+    const int half = h->keep_half;
+    int32_t* stage = h->keep_pinned + (size_t)half * h->L.WP;
+    if (h->keep_pending[half]) {
+      e = hipEventSynchronize(h->keep_evt[half]);
+      h->keep_pending[half] = false;
     }
     if (e == hipSuccess) {
-      std::memcpy(h->keep_pinned, src.data(), src.size() * 4);
-      e = hipMemcpyAsync(h->keep_dev, h->keep_pinned, src.size() * 4, hipMemcpyHostToDevice, h->stream);
+      std::memcpy(stage, src.data(), src.size() * 4);
+      e = kvc::launch_stage_idx(h->keep_pinned_dev + (size_t)half * h->L.WP, h->keep_dev, (int32_t)src.size(),
+                                h->stream);
     }
     if (e == hipSuccess) {
-      e = hipEventRecord(h->keep_evt, h->stream);
-      h->keep_pending = e == hipSuccess;
+      e = hipEventRecord(h->keep_evt[half], h->stream);
+      h->keep_pending[half] = e == hipSuccess;
+      h->keep_half = half ^ 1;
     }
     if (e == hipSuccess) {
       kvc::CompactArgs a{};

@@ -353,23 +353,26 @@ hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
 //    that 16-byte chunk of the slot's key row for every head (eight heads in
 //    flight) and, for chunk 0, the slot's t and g;
 //  * value blocks: one destination V^T tile (64 slots) of one head.  A slot's
-//    value is a column of a V^T tile (one element per 128-byte row), so the
-//    block brings whole source tiles into LDS -- only those holding kept
-//    entries, once per run of consecutive entries in the same tile -- gathers
-//    the columns there, and writes the destination tile as full rows.  A
-//    source tile is read by a few destination tiles at most (two, plus one
-//    more at the ring's wrap).
+//    value is a column of a source V^T tile (one element in each 64-slot row),
+//    so lane l of every wave owns destination slot l of the tile and wave w
+//    the rows [w D/4, (w+1) D/4): the lanes of one load read the kept columns
+//    of one source row (a few 128-byte lines, as the kept slots rise), and the
+//    lanes of one store write a whole destination row.  All D/4 loads of a
+//    thread are in flight before its stores.  Slots past n in the last tile
+//    are written as zeros: attention reads whole tiles and weights those slots
+//    by exactly 0, which needs finite values.
 template <typename T, int D>
 struct CompactShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int CH = D / E;          // 16-byte chunks per key row
   static constexpr int KS = 256 / CH;       // destination slots per key block
+  static constexpr int VR = D / 4;          // value rows per wave
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   using Sh = CompactShape<T, D>;
-  constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, HU = 8;
+  constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, VR = Sh::VR, HU = 8;
   const Geo& g = a.geo;
   if (blockIdx.y > 0) {
     a.src = layer_region(a.src, (int64_t)blockIdx.y * a.layer_stride);
@@ -417,48 +420,33 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   b -= (int)a.nk;
   const int NT = (a.n + kTile - 1) / kTile;
   const int h = b / NT, dt = b - (b / NT) * NT;
-  const int j0 = dt * kTile, nn = min(kTile, a.n - j0);
   constexpr int TE = D * kTile;                       // elements per V^T tile
-  constexpr int PER = TE * (int)sizeof(T) / (256 * 16);   // 16-byte pieces per thread
-  __shared__ uint4 s_src[TE * sizeof(T) / 16];
-  __shared__ uint4 s_dst[TE * sizeof(T) / 16];
-  __shared__ int s_idx[kTile];
-  if (tid < kTile) s_idx[tid] = tid < nn ? a.idx[j0 + tid] : INT32_MAX;
-  // slots past n in a partial tile are written as zeros: attention reads whole
-  // tiles and weights those slots by exactly 0, which needs finite values
-  // (uninitialised LDS can hold Inf/NaN patterns).  These columns are disjoint
-  // from the gathered ones; the run loop below synchronizes at least once.
-  if (nn < kTile && tid % kTile >= nn)
-    for (int d = tid / kTile; d < D; d += 256 / kTile) ((T*)s_dst)[d * kTile + tid % kTile] = T(0);
-  __syncthreads();
-  const T* vsrc = (const T*)a.src.v + (size_t)h * (a.src.cap / kTile) * TE;
-  T* sdst = (T*)s_dst;
-  const T* ssrc = (const T*)s_src;
-  // Source tiles in the order the kept entries visit them, one per run of consecutive entries in the same
-  // tile.  Sorted logical indices give increasing slots except where the window ring wraps, so a tile
-  // can come back once (staged again; its entries are copied again, unchanged).
-  for (int q = 0; q < nn;) {
-    const int st = s_idx[q] / kTile;
-    int qe = q + 1;
-    while (qe < nn && s_idx[qe] / kTile == st) ++qe;
-    const uint4* tp = reinterpret_cast<const uint4*>(vsrc + (size_t)st * TE);
+  const int lane = tid & (kTile - 1), w = tid / kTile;
+  const int j = dt * kTile + lane;
+  const bool ok = j < a.n;
+  const int sj = ok ? a.idx[j] : 0;
+  const T* sp = (const T*)a.src.v + ((size_t)h * (a.src.cap / kTile) + sj / kTile) * TE + (size_t)w * VR * kTile +
+                sj % kTile;
+  T* dp = (T*)a.dst.v + ((size_t)h * (a.dst.cap / kTile) + dt) * TE + (size_t)w * VR * kTile + lane;
+  T x[VR];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) s_src[tid + 256 * i] = tp[tid + 256 * i];
-    __syncthreads();
-    // gather: thread owns destination slot jj = tid % 64 and rows d = tid / 64 + 4k
-    const int jj = tid % kTile;
-    const int sj = s_idx[jj];
-    if (sj / kTile == st) {
-      const int col = sj % kTile;
-      for (int d = tid / kTile; d < D; d += 256 / kTile) sdst[d * kTile + jj] = ssrc[d * kTile + col];
-    }
-    __syncthreads();
-    q = qe;
-  }
-  // the destination tile as full rows (slots past n in a partial tile: zeros)
-  uint4* dp = reinterpret_cast<uint4*>((T*)a.dst.v + ((size_t)h * (a.dst.cap / kTile) + dt) * TE);
+  for (int r = 0; r < VR; ++r) x[r] = ok ? sp[r * kTile] : T(0);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dp[tid + 256 * i] = s_dst[tid + 256 * i];
+  for (int r = 0; r < VR; ++r) dp[r * kTile] = x[r];
+}
+
+// Copy n int32 values from host-visible (pinned) memory to device memory: one
+// read of each value over the bus, so the gather kernel then reads device memory.
+__global__ __launch_bounds__(256) void stage_idx_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst,
+                                                        int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+hipError_t launch_stage_idx(const int32_t* host_visible, int32_t* dst, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stage_idx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, host_visible, dst, n);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -632,8 +620,8 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
   for (int d = 0; d < D; ++d) out[d] = Elem<T>::st(o[d] * inv);
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general) {
-  if (!force_general && a.geo.esz == 2 && a.geo.D == 128) return launch_attend_mfma(a, s);
+hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s) {
+  if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 128) return launch_attend_mfma(a, paths, s);
   const int64_t total = (int64_t)a.Lq * a.geo.H;
   const unsigned blocks = (unsigned)((total + 63) / 64);
   if (a.geo.esz == 2) {
@@ -758,8 +746,8 @@ static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
 }
 
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general) {
-  if (!force_general && a.geo.esz == 2 && a.geo.D == 128) {
+hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s) {
+  if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 128) {
     const int64_t rows = (int64_t)a.Nq * a.geo.H;
     hipLaunchKernelGGL((score_rot_kernel<uint16_t, 128, true>), dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, a);
     if (hipError_t e = launch_score_mfma(a, (const uint16_t*)a.qh, s); e != hipSuccess) return e;

@@ -11,14 +11,17 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+// copy n int32 from pinned host memory (its device-visible address) to device memory
+hipError_t launch_stage_idx(const int32_t* host_visible, int32_t* dst, int32_t n, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s);
 // Attention: the matrix-core path for bf16 with head_dim 128, else the
-// general per-row path.  `force_general` selects the latter (tests).
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s, bool force_general);
-hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
+// general per-row path; `paths` holds kPath* bits (kPathGeneral selects the
+// general path for any cache).
+hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s);
+hipError_t launch_attend_mfma(const AttendArgs& a, uint32_t paths, hipStream_t s);
 // Scores: the matrix-core passes for bf16 with head_dim 128, else the general
-// per-row/per-column path (force_general selects the latter).
-hipError_t launch_score(const ScoreArgs& a, hipStream_t s, bool force_general);
+// per-row/per-column path (kPathGeneral in `paths` selects the latter).
+hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s);
 // MemRoPE: fold evicted frames into the EMA memories; copy the memory slots out
 hipError_t launch_mem_fold(const MemFoldArgs& a, hipStream_t s);
 hipError_t launch_mem_export(const MemExportArgs& a, hipStream_t s);

@@ -7,10 +7,11 @@
 //             then pinned (LingBot-World 2.0 article, "sink_size attention
 //             sink"); a FIFO of blocks only under the Rolling-Sink push.
 //   window -- W_tok slots used as a ring: appending past capacity advances the
-//             head over the oldest tokens, which is the article's
-//             "num_evicted = new + local_end - kv_size, shift left after the
-//             sink" ("how the window rolls when full") done as index
-//             arithmetic instead of a copy.
+//             head over the oldest tokens.  This is the eviction rule of the
+//             LingBot-World 2.0 article, section "how the window rolls when
+//             full" (evict as many of the oldest non-sink tokens as the new
+//             block overflows the capacity by), done as a ring-head advance
+//             instead of a left shift of everything after the sink.
 // Logical order (what exports, retime ranges, scores and keep lists use):
 // sink oldest..newest, then window oldest..newest.
 //

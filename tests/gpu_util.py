@@ -1,4 +1,5 @@
 """Helpers shared by the GPU parity tests (not collected by pytest)."""
+import contextlib
 import sys
 import time
 
@@ -88,3 +89,13 @@ class Timer:
 
     def __exit__(self, *a):
         log(f"  [{self.tag}] {time.time() - self.t:.1f}s")
+
+
+@contextlib.contextmanager
+def paths(gc, **kw):
+    """Run the body with kernel paths selected on cache gc (kvc_set_paths), then restore the defaults."""
+    gc.set_paths(**kw)
+    try:
+        yield
+    finally:
+        gc.set_paths()

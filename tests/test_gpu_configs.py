@@ -189,25 +189,22 @@ def test_head_share_split_keys():
     with Timer("head share split"):
         out = gc.attend(dev(q, w), 15).float().cpu().numpy()
     mx, rr = check_attention(out[rows], ref, "head share split")
-    os.environ["KVC_ATTEND_SPLIT"] = "0"
+    gc.set_paths(no_split=True)
     try:
         out1 = gc.attend(dev(q, w), 15).float().cpu().numpy()
     finally:
-        os.environ.pop("KVC_ATTEND_SPLIT", None)
+        gc.set_paths()
     check_attention(out1[rows], ref, "head share unsplit")
     log(f"head share split: max_abs {mx:.3e} rel_rms {rr:.3e}")
 
 
 @pytest.mark.parametrize("raw_keys", [False, True])
 def test_attention_kernel_variants(raw_keys):
-    """The kernels kept for A/B timing beside the default fixed-reference kernel: the running-maximum
-    8-wave kernel alone (KVC_ATTEND_VARIANT=v5) and the 4-wave kernel with two workgroups per CU (v3, no
-    raw-key path).  Every kernel matches the oracle on sampled rows, and v3 matches v5 on every row (the
-    same online softmax; v5 visits whole key tiles before edge tiles and v3 keeps the logical order, so
-    their fp32 sums round differently and the outputs agree to rounding, not bit for bit).  The cache is
-    8 heads of the 14B-shaped layer after two evictions, so the ring holds two key regions with edge
-    tiles."""
-    import os
+    """The running-maximum 8-wave kernel alone (kvc_set_paths KVC_PATH_RUNNING_MAX) beside the default
+    fixed-reference kernel: both match the oracle on sampled rows and each other on every row (the same
+    tile order; the fixed reference and the running maximum round their fp32 sums differently, so they
+    agree to rounding, not bit for bit).  The cache is 8 heads of the 14B-shaped layer after two
+    evictions, so the ring holds two key regions with edge tiles."""
     from oracle import OracleCache
     w = WORKLOADS["c3"]
     H = 8
@@ -224,16 +221,14 @@ def test_attention_kernel_variants(raw_keys):
     rows = np.sort(np.random.default_rng(78).choice(q.shape[0], size=384, replace=False))
     ref = oc.attend(q, 3, 21, rows=rows)
     outs = {}
-    for var in ["", "v5"] + ([] if raw_keys else ["v3"]):
-        if var:
-            os.environ["KVC_ATTEND_VARIANT"] = var
+    for var in ("default", "running_max"):
+        log(f"attention variant {var} raw_keys={raw_keys}")
+        gc.set_paths(running_max=var == "running_max")
         try:
-            log(f"attention variant {var or 'default'} raw_keys={raw_keys}")
             outs[var] = gc.attend(dev(q, w), 21).float().cpu().numpy()
         finally:
-            os.environ.pop("KVC_ATTEND_VARIANT", None)
-        mx, rr = check_attention(outs[var][rows], ref, f"variant {var or 'default'}")
-        log(f"variant {var or 'default'}: max_abs {mx:.3e} rel_rms {rr:.3e}")
-    if "v3" in outs:
-        mx, rr = check_attention(outs["v3"], outs["v5"], "v3 vs v5, all rows")
-        log(f"v3 vs v5: max_abs {mx:.3e} rel_rms {rr:.3e}")
+            gc.set_paths()
+        mx, rr = check_attention(outs[var][rows], ref, f"variant {var}")
+        log(f"variant {var}: max_abs {mx:.3e} rel_rms {rr:.3e}")
+    mx, rr = check_attention(outs["default"], outs["running_max"], "fixed reference vs running maximum, all rows")
+    log(f"fixed reference vs running maximum: max_abs {mx:.3e} rel_rms {rr:.3e}")
