@@ -311,6 +311,21 @@ size_t kvc_relax_scratch_bytes(kvc_handle h);
 kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
                             size_t scratch_bytes);
 
+/* Bytes of the scratch the library holds for kvc_relax_scores_noalloc, per GPU. */
+#define KVC_RELAX_NOALLOC_SCRATCH_BYTES (8u << 20)
+/* kvc_relax_scores for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid allocation): the same
+ * computation and result, with the scratch taken from an array of
+ * KVC_RELAX_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory
+ * from the first such call on that GPU until the process ends.  Allocates
+ * nothing.  ENOMEM, before anything is enqueued, when the cache needs more
+ * scratch than that (kvc_relax_scratch_bytes(h) > KVC_RELAX_NOALLOC_SCRATCH_BYTES);
+ * other errors as kvc_relax_scores.  Every call on one GPU uses the same array
+ * and nothing in it needs to start at zero (a call writes every element it
+ * reads): calls ordered on one stream are safe, calls that overlap in time on
+ * one GPU (other streams, other host threads) race. */
+kvc_status kvc_relax_scores_noalloc(kvc_handle h, int32_t tail_frames, float weight, float* scores);
+
 /* Keep exactly the logical entries keep_idx[0..n_keep) (host int32, sorted,
  * unique, in [0, n_valid), containing every sink entry), packed in that
  * order; window entries are gathered into the other window buffer.  Requires

@@ -34,7 +34,7 @@ KVC_MAX_Q_FRAMES = 32
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_set_paths", "kvc_append",
             "kvc_attend",
             "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
-            "kvc_relax_scores", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
+            "kvc_relax_scores", "kvc_relax_scores_noalloc", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
             "kvc_compact", "kvc_sink_push", "kvc_group_workspace_bytes", "kvc_create_group", "kvc_retime_layers",
             "kvc_compact_layers", "kvc_sink_push_layers",
             "kvc_info",
@@ -83,6 +83,7 @@ def _load():
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
         "kvc_relax_scratch_bytes": (sz, [vp]),
         "kvc_relax_scores": (ctypes.c_int, [vp, i32, ctypes.c_float, vp, vp, sz]),
+        "kvc_relax_scores_noalloc": (ctypes.c_int, [vp, i32, ctypes.c_float, vp]),
         "kvc_set_attention_limit": (ctypes.c_int, [vp, i32]),
         "kvc_set_memory_rates": (ctypes.c_int, [vp, ctypes.c_float, ctypes.c_float]),
         "kvc_export_memory": (ctypes.c_int, [vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]),
@@ -265,6 +266,19 @@ class KVCache:
             raise ValueError("out must be a contiguous float32 CUDA tensor of at least n_cand elements")
         _check(lib.kvc_relax_scores(self._h, int(tail_frames), float(weight), ctypes.c_void_p(out.data_ptr()),
                                     ctypes.c_void_p(self._relax_scratch.data_ptr() + off), need))
+        return out
+
+    def relax_scores_noalloc(self, tail_frames: int, weight: float = 0.5, out=None):
+        """relax_scores on the scratch the library holds per GPU (kvc_relax_scores_noalloc): the call itself
+        allocates nothing; `out` (float32, at least n_cand elements) is allocated here only when not given."""
+        info = self.info()
+        n_cand = max(1, info["n_valid"] // self.S - info["sink_filled"] // self.S - int(tail_frames))
+        if out is None:
+            out = torch.empty(n_cand, dtype=torch.float32, device=self.device)
+        elif (out.device.type != "cuda" or out.dtype != torch.float32 or not out.is_contiguous()
+              or out.numel() < n_cand):
+            raise ValueError("out must be a contiguous float32 CUDA tensor of at least n_cand elements")
+        _check(lib.kvc_relax_scores_noalloc(self._h, int(tail_frames), float(weight), ctypes.c_void_p(out.data_ptr())))
         return out
 
     def set_attention_limit(self, max_keys: int):

@@ -208,6 +208,7 @@ struct RelaxArgs {
 };
 
 constexpr int kRelaxSlice = 256;          // tokens per frame-sum workgroup
+constexpr size_t kRelaxNoallocScratch = (size_t)8 << 20;   // bytes of the library-held relax scratch per GPU
 constexpr int kRelaxMaxFrames = 64;       // candidates + Tail frames per relax call (Gram matrix in LDS)
 
 }  // namespace kvc

@@ -15,6 +15,7 @@
 #include "kvc_ring.hpp"
 
 static_assert(KVC_MAX_POS == kvc::kMaxPos, "time table range");
+static_assert(KVC_RELAX_NOALLOC_SCRATCH_BYTES == kvc::kRelaxNoallocScratch, "relax scratch size");
 static_assert(KVC_PATH_RUNNING_MAX == kvc::kPathRunningMax && KVC_PATH_GENERAL == kvc::kPathGeneral &&
                   KVC_PATH_NO_SPLIT == kvc::kPathNoSplit,
               "path bits");
@@ -801,13 +802,16 @@ size_t kvc_relax_scratch_bytes(kvc_handle h) {
          align_up((size_t)kvc::kRelaxMaxFrames * kvc::kRelaxMaxFrames * 4) + placed_ka_bytes(h);
 }
 
-kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
-                            size_t scratch_bytes) {
-  if (kvc_status s = check(h)) return s;
-  if (!scores || !scratch) return fail(KVC_EINVAL, "null argument");
+// Relax Forcing scores on a given scratch (validated by the callers); `noalloc` only changes the error
+// text for a scratch that is too small.
+static kvc_status relax_impl(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
+                             size_t scratch_bytes, bool noalloc) {
+  if (!scores) return fail(KVC_EINVAL, "null argument");
   if (!(weight >= 0.f && weight <= 1.f)) return fail(KVC_EINVAL, "weight outside [0, 1]");
-  if (scratch_bytes < kvc_relax_scratch_bytes(h)) return fail(KVC_ENOMEM, "relax scratch too small");
-  if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
+  if (scratch_bytes < kvc_relax_scratch_bytes(h))
+    return fail(KVC_ENOMEM, noalloc ? "this cache needs more relax scratch than the library holds "
+                                      "(kvc_relax_scratch_bytes > KVC_RELAX_NOALLOC_SCRATCH_BYTES)"
+                                    : "relax scratch too small");
   const int32_t n = h->st.n_valid(), ns = h->st.ns, S = h->S;
   if (n % S != 0 || ns % S != 0) return fail(KVC_EINVAL, "relax scores need whole frames in the cache");
   if (tail_frames < 1) return fail(KVC_EINVAL, "tail_frames must be >= 1");
@@ -842,6 +846,25 @@ kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, flo
                          &a.keys);
   if (e == hipSuccess) e = kvc::launch_relax(a, h->stream);
   return device_result(h, e, "relax scores");
+}
+
+kvc_status kvc_relax_scores(kvc_handle h, int32_t tail_frames, float weight, float* scores, void* scratch,
+                            size_t scratch_bytes) {
+  if (kvc_status s = check(h)) return s;
+  if (!scratch) return fail(KVC_EINVAL, "null argument");
+  if ((uintptr_t)scratch % kAlign != 0) return fail(KVC_EINVAL, "scratch must be 256-byte aligned");
+  return relax_impl(h, tail_frames, weight, scores, scratch, scratch_bytes, false);
+}
+
+kvc_status kvc_relax_scores_noalloc(kvc_handle h, int32_t tail_frames, float weight, float* scores) {
+  if (kvc_status s = check(h)) return s;
+  if (kvc_relax_scratch_bytes(h) > kvc::kRelaxNoallocScratch)
+    return fail(KVC_ENOMEM, "this cache needs more relax scratch than the library holds "
+                            "(kvc_relax_scratch_bytes > KVC_RELAX_NOALLOC_SCRATCH_BYTES)");
+  void* p = nullptr;
+  const hipError_t e = kvc::relax_noalloc_scratch(&p);
+  if (e != hipSuccess) return fail(KVC_EDEVICE, std::string("relax scratch address: ") + hipGetErrorString(e));
+  return relax_impl(h, tail_frames, weight, scores, p, kvc::kRelaxNoallocScratch, true);
 }
 
 kvc_status kvc_set_attention_limit(kvc_handle h, int32_t max_keys) {

@@ -27,6 +27,9 @@ hipError_t launch_mem_fold(const MemFoldArgs& a, hipStream_t s);
 hipError_t launch_mem_export(const MemExportArgs& a, hipStream_t s);
 // frame sums, their Gram matrix, then the Relax Forcing scores
 hipError_t launch_relax(const RelaxArgs& a, hipStream_t s);
+// Device address of the current GPU's copy of the library-held relax scratch
+// (kRelaxNoallocScratch bytes), looked up once per device.
+hipError_t relax_noalloc_scratch(void** ptr);
 // rows + columns passes over a query window already rotated into qbf
 // ([H][Nq][128] bf16); writes a.m (log2 normaliser per row) and a.part
 hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s);

@@ -13,11 +13,40 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "kvc_common.hip.hpp"
 #include "kvc_launch.hpp"
 
+// Scratch of kvc_relax_scores_noalloc: each GPU the library runs on holds its
+// own copy for the life of the process.  Host code never passes this name to a
+// kernel (on the host it is a stand-in, not a device address); it uses the
+// address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[kvc::kRelaxNoallocScratch];
+
 namespace kvc {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t relax_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));     // with this device current: its own copy
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
 
