@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-context", action="store_true", help="skip the vendor-library reference timings")
-    p.add_argument("--cpu-rows", type=int, default=3840, help="query rows of the oracle sample (about 10 s of host BLAS)")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-config chunk streams")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_attend_c3.json"))
     return p.parse_args()
 
@@ -177,6 +177,7 @@ def main():
     copy_gbps = 2.0 * (1 << 30) / (float(np.median(cp_ms)) * 1e-3) / 1e9
     del flush, cx, cy
     context = None if args.no_context else vendor_context(dev, stream, H, N, Lk, D)
+    configs = {} if args.no_configs else config_streams(dev, stream, ev, cpu=not args.no_cpu_baseline)
 
     dt = D - 4 * (D // 6)
     app_bytes = 4.0 * N * H * D * 2
@@ -230,7 +231,7 @@ def main():
             "retime_GBps_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9, 1),
             "append_hbm_frac_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "retime_hbm_frac_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "hbm_copy_GBps_measured": round(copy_gbps, 1),
+            "hbm_copy_torch_GBps_measured": round(copy_gbps, 1),
             "score_ms": round(score_ms, 4),
             "score_tflops": round(flop / (score_ms * 1e-3) / 1e12, 2),
             **extras,
@@ -238,9 +239,145 @@ def main():
     }
     if context:
         res["context"] = context
+    if configs:
+        res["configs"] = configs
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_rows, w, cache)
+        res["cpu_baseline"] = cpu_baseline(w)
+        if "c3" in res.get("configs", {}):
+            res["configs"]["c3"]["oracle_s_per_chunk"] = res["cpu_baseline"]["seconds"]
     print(json.dumps(res), flush=True)
+
+
+# steady-state chunks of each config's stream (the rest warm the cache up, or are the short last chunk)
+STREAM_STEADY = {
+    "tiny": lambda i, w: i >= 5,                                   # evicting from chunk 5 on
+    "c2": lambda i, w: True,                                       # keys grow 4680 -> 32760: every chunk
+    "c3": lambda i, w: 6 <= i < w.n_chunks - 1,                    # evicting 4680 per chunk
+    "c4": lambda i, w: 7 <= i < w.n_chunks - 1,                    # a sink push every chunk
+    "c5a": lambda i, w: 1 <= i < w.n_chunks - 1,                   # a clamped shift every chunk, three cuts
+    "c5b": lambda i, w: 7 <= i < w.n_chunks - 1,                   # scores + compaction every 4th chunk
+}
+# the chunk of each stream the oracle is timed on: a steady one (for c5b one that compacts)
+STREAM_ORACLE_CHUNK = {"tiny": 6, "c2": 6, "c4": 8, "c5a": 8, "c5b": 7}
+
+
+class _TimedCache:
+    """A KVCache whose library calls are bracketed by events on the cache's stream (per-operation GPU time)."""
+    OPS = ("append", "attend", "retime", "score", "compact", "sink_push", "relax_scores")
+
+    def __init__(self, cache, stream, ev):
+        self._c, self._s, self._ev, self.log = cache, stream, ev, []
+
+    def __getattr__(self, name):
+        f = getattr(self._c, name)
+        if name not in self.OPS:
+            return f
+
+        def timed(*a, **kw):
+            e0, e1 = self._ev(), self._ev()
+            e0.record(self._s)
+            r = f(*a, **kw)
+            e1.record(self._s)
+            self.log.append((name, e0, e1, self._c.info()["n_valid"]))
+            return r
+        return timed
+
+
+def config_streams(dev, stream, ev, cpu):
+    """Every config's whole chunk stream through the product's policy driver (rolling_kv_cache_amd.policies),
+    inputs resident in HBM (four seeded chunks of the config's shape, cycled; the stream's own frame
+    counts), each chunk and each library call bracketed by events: ms per chunk over the steady-state chunks
+    (mean, p10/p50/p90), attention TFLOP/s over all attends, append and retime GB/s (warm: the stream runs
+    back to back, no MALL flush).  With `cpu`, the oracle's time for one steady chunk of the same config on
+    this host (its earlier chunks replayed with one query row attended, so that only the timed chunk pays
+    the full attention)."""
+    import numpy as np
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from rolling_kv_cache_amd.policies import driver_for
+    from workloads import WORKLOADS, chunk_inputs
+    res = {}
+    for name in STREAM_STEADY:
+        w = WORKLOADS[name]
+        td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        pools = {}
+        for F in sorted(set(w.chunk_frames)):
+            pools[F] = [tuple(torch.from_numpy(x).to(dev, td) for x in chunk_inputs(w, c, frames=F))
+                        for c in range(4)]
+        cache = kvc.KVCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, td,
+                            bank_frames=w.bank_frames, compact=name.startswith("c5"))
+        tc = _TimedCache(cache, stream, ev)
+        drv = driver_for(name)(tc, w)
+        chunk_ev, q_prev = [], None
+        torch.cuda.synchronize()
+        for i in range(w.n_chunks):
+            q, k, v = pools[w.chunk_frames[i]][i % 4]
+            e0, e1 = ev(), ev()
+            n0 = len(tc.log)
+            e0.record(stream)
+            drv.step(i, q, k, v, q_prev=q_prev)
+            e1.record(stream)
+            chunk_ev.append((e0, e1, n0, len(tc.log)))
+            q_prev = q
+        torch.cuda.synchronize()
+        S, H, D, esz = w.frame_seqlen, w.heads, w.head_dim, 2 if w.dtype == "bf16" else 4
+        dtb = D - 4 * (D // 6)
+        steady = [i for i in range(w.n_chunks) if STREAM_STEADY[name](i, w)]
+        ms = np.array([a.elapsed_time(b) for a, b, _, _ in chunk_ev])
+        att_flop = att_ms = app_b = app_ms = ret_b = ret_ms = 0.0
+        op_ms = {}
+        for i, (_, _, lo, hi) in enumerate(chunk_ev):
+            Lq = w.chunk_frames[i] * S
+            for op, a, b, n in tc.log[lo:hi]:
+                t = a.elapsed_time(b)
+                if i in steady:
+                    op_ms[op] = op_ms.get(op, 0.0) + t
+                if op == "attend":
+                    att_flop += 4.0 * H * Lq * n * D
+                    att_ms += t
+                elif op == "append":
+                    app_b += 4.0 * Lq * H * D * esz
+                    app_ms += t
+        for op, a, b, n in tc.log:
+            if op == "retime" and name == "c5a":    # every valid entry's time band, read and written
+                ret_b += 2.0 * n * H * dtb * esz
+                ret_ms += a.elapsed_time(b)
+        st = ms[steady]
+        r = {"chunks": w.n_chunks, "steady_chunks": len(steady),
+             "ms_per_chunk_mean": round(float(st.mean()), 4),
+             "ms_per_chunk_p10_p50_p90": [round(float(x), 4) for x in np.percentile(st, [10, 50, 90])],
+             "stream_total_ms": round(float(ms.sum()), 3),
+             "attend_tflops": round(att_flop / (att_ms * 1e-3) / 1e12, 2),
+             "attend_frac_bf16_peak": round(att_flop / (att_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "append_GBps_warm": round(app_b / (app_ms * 1e-3) / 1e9, 1),
+             "steady_op_ms_per_chunk": {op: round(t / len(steady), 4) for op, t in sorted(op_ms.items())}}
+        if ret_ms > 0:
+            r["retime_GBps_warm"] = round(ret_b / (ret_ms * 1e-3) / 1e9, 1)
+        if cpu and name in STREAM_ORACLE_CHUNK:
+            r["oracle_s_per_chunk"] = oracle_chunk_seconds(w, STREAM_ORACLE_CHUNK[name])
+        res[name] = r
+        del tc, drv, cache, pools
+        torch.cuda.empty_cache()
+    return res
+
+
+def oracle_chunk_seconds(w, i):
+    """Wall time of the oracle (untuned numpy) for chunk i of workload w on this host: chunks 0..i-1 are
+    replayed first with one query row attended (their cache operations in full), then chunk i runs in full."""
+    import numpy as np
+    from oracle import make_run
+    from workloads import chunk_inputs
+    run = make_run(w)
+    q_prev = None
+    for c in range(i + 1):
+        q, k, v = chunk_inputs(w, c % 4, frames=w.chunk_frames[c])
+        kw = {"q_prev": q_prev} if w.name.startswith("c5b") else {}
+        if c == i:
+            t0 = time.perf_counter()
+            run.step(c, q, k, v, **kw)
+            return round(time.perf_counter() - t0, 4)
+        run.step(c, q, k, v, rows=np.arange(1), **kw)
+        q_prev = q
 
 
 def ceilings(dev, stream, ev):
@@ -292,7 +429,7 @@ def ceilings(dev, stream, ev):
             torch.cuda.synchronize()
             ms = back_to_back_ms(stream, ev, f, n=3)
             best = max(best, nbytes / (ms * 1e-3) / 1e9)
-        out[f"hbm_{name}_GBps_measured"] = round(best, 1)
+        out[f"hbm_{name}_GBps_probe"] = round(best, 1)
     del a, b, sink
     return out
 
@@ -593,31 +730,26 @@ def vendor_context(dev, stream, H, N, Lk, D):
     return out
 
 
-def cpu_baseline(rows, w, cache):
-    """The oracle, untuned, on this host: fp32 BLAS attention of `rows` query rows (all heads) over a full
-    28080-entry cache, as TFLOP/s; the cache contents are the GPU cache's own export."""
+def cpu_baseline(w):
+    """The oracle, untuned, on this host: one full steady chunk of the bench workload (chunk 7: the
+    append that evicts 4680 entries, then the attention of all 4680 queries x 40 heads over the 28080
+    cached keys, fp32 numpy BLAS), after its chunks 0-6 were replayed with one query row attended; reported
+    as the chunk's attention flop over its wall time, like the GPU's value."""
     import numpy as np
-    import torch
-    from oracle import attention_f32, OracleCache
-    from workloads import chunk_inputs
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
-    st = cache.export()
-    K = st["K"].float().cpu().numpy()
-    V = st["V"].float().cpu().numpy()
-    q, _, _ = chunk_inputs(w, 0)
-    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, "bf16")
-    t0 = time.perf_counter()
-    qh = oc.rotate_queries(q, 3, 0)[:rows]
-    attention_f32(qh, K, V)
-    dt = time.perf_counter() - t0
-    flop = 4.0 * w.heads * rows * K.shape[0] * w.head_dim
-    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} query rows x {w.heads} heads over {K.shape[0]} keys (one 3-frame chunk's queries, "
-                      f"incl. their RoPE), fp32 numpy BLAS; {dt:.2f} s"}
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    sec = oracle_chunk_seconds(w, 7)
+    N = w.chunk_frames[7] * w.frame_seqlen
+    flop = 4.0 * w.heads * N * w.capacity * w.head_dim
+    return {"value": round(flop / sec / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": threads, "seconds": sec,
+            "sample": f"one full steady chunk of the c3 stream (chunk 7: append evicting {N} entries + attention "
+                      f"of {N} queries x {w.heads} heads over {w.capacity} keys, incl. the RoPE of keys and "
+                      f"queries), fp32 numpy BLAS; chunks 0-6 replayed first with one query row attended"}
 
 
 if __name__ == "__main__":

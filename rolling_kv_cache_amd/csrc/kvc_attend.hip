@@ -154,17 +154,36 @@ __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, in
   }
 }
 
+// Key of accumulator element i of S^T block kb for lane half hl: kb*32 +
+// perm_row((i/4)*8 + hl*4 + i%4), which is kkey(kb, i) + 8*hl with kkey a
+// compile-time constant (perm_row moves the hl bit from 2 to 3 and bit 3 of
+// (i/4)*8 to 2).  Masks compare kkey against one per-lane bound instead of
+// forming 32 key indices.
+__device__ __forceinline__ constexpr int kkey(int kb, int i) {
+  return kb * 32 + (i & 3) + 4 * ((i >> 2) & 1) + 16 * ((i >> 3) & 1);
+}
+
 // keys of the tile outside [lead, nv) get -inf (lead > 0 only in the first tile
 // of a range that starts inside a tile)
 __device__ __forceinline__ void mask_tile(f32x16_t* s, int lead, int nv, int hl) {
   if (nv >= kBN && lead <= 0) return;
+  const int nvh = nv - 8 * hl, leadh = lead - 8 * hl;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kb * 32 + perm_row((i >> 2) * 8 + hl * 4 + (i & 3));
-      if (key >= nv || key < lead) s[kb][i] = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (kkey(kb, i) >= nvh || kkey(kb, i) < leadh) s[kb][i] = -INFINITY;
+}
+
+// keys of the tile at or past nv get -inf
+__device__ __forceinline__ void mask_tile_end(f32x16_t* s, int nv, int hl) {
+  if (nv >= kBN) return;
+  const int nvh = nv - 8 * hl;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (kkey(kb, i) >= nvh) s[kb][i] = -INFINITY;
 }
 
 // a split-key part's rows: the unnormalised O, the reference m and the row sum
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     if (CAUSAL) {
       const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
       if (lb + kBN > lim_lo) {
-        mask_tile(s, 0, min(nv, lim - lb), hl);
+        mask_tile_end(s, min(nv, lim - lb), hl);
         return;
       }
     }
@@ -795,7 +814,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
     if (CAUSAL) {
       const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
       if (lb + kBN > lim_lo) {
-        mask_tile(s, 0, min(nv, lim - lb), hl);
+        mask_tile_end(s, min(nv, lim - lb), hl);
         return;
       }
     }
