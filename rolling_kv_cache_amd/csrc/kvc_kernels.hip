@@ -67,8 +67,11 @@ __device__ __forceinline__ SegW pick_seg_v(const AppendArgs& a, int b) {
 // Key blocks: KTB tokens x up to KHB heads.  Thread (token i, chunk c) owns
 // chunk c of token i for every head of its block: the token's frame, grid
 // position and the chunk's (cos, sin) pairs are computed once and reused for
-// each head, and the heads go eight at a time (eight 16-byte loads in flight).
-constexpr int KHB = 20;                     // heads per key block
+// each head, and all KHB 16-byte loads are in flight before the first store
+// (one round per thread: many blocks, no chain of dependent rounds).  KHB is
+// 8 for caches of 32 heads or more and 4 below (measured: 40 heads 8 > 4 > 20,
+// 12 heads 4 > 8).
+inline int append_khb(int heads) { return heads >= 32 ? 8 : 4; }
 
 template <typename T, int D>
 struct AppendShape {
@@ -78,10 +81,10 @@ struct AppendShape {
   static constexpr int HPB = 256 / (8 * CH);  // heads per value block
 };
 
-template <typename T, int D>
+template <typename T, int D, int KHB>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   using Sh = AppendShape<T, D>;
-  constexpr int E = Sh::E, CH = Sh::CH, KTB = Sh::KTB, HPB = Sh::HPB, HU = 8;
+  constexpr int E = Sh::E, CH = Sh::CH, KTB = Sh::KTB, HPB = Sh::HPB, HU = KHB;
   const Geo& g = a.geo;
   const int tid = threadIdx.x;
   int b = blockIdx.x;
@@ -215,10 +218,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // Blocks of the append grid for one segment list (host and kernel agree on
 // these counts through the same constants).
 template <typename T, int D>
-static void append_blocks(AppendArgs& a) {
+static void append_blocks(AppendArgs& a, int khb) {
   using Sh = AppendShape<T, D>;
   constexpr int KTB = Sh::KTB, HPB = Sh::HPB;
-  const int nhg = (a.geo.H + KHB - 1) / KHB;
+  const int nhg = (a.geo.H + khb - 1) / khb;
   int kb = 0, vb = 0;
   for (int i = 0; i < a.nseg; ++i) {
     SegW& s = a.seg[i];
@@ -234,11 +237,15 @@ static void append_blocks(AppendArgs& a) {
 
 template <typename T, int D>
 static hipError_t append_launch(AppendArgs a, hipStream_t s) {
-  append_blocks<T, D>(a);
+  const int khb = append_khb(a.geo.H);
+  append_blocks<T, D>(a, khb);
   const int blocks = a.nkb + a.nvb;
   if (blocks == 0) return hipSuccess;
   const unsigned layers = a.layers > 1 ? (unsigned)a.layers : 1u;
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3(blocks, layers), dim3(256), 0, s, a);
+  if (khb == 8)
+    hipLaunchKernelGGL((append_kernel<T, D, 8>), dim3(blocks, layers), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((append_kernel<T, D, 4>), dim3(blocks, layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -262,7 +269,7 @@ struct RetimeShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int DT = D - 4 * (D / 6);            // time band width
   static constexpr int CA = (DT + E - 1) / E;           // chunks per KA row (time band, padded)
-  static constexpr int THREADS = (32 * CA + 63) / 64 * 64;
+  static constexpr int THREADS = (kRetimeSlots * CA + 63) / 64 * 64;
 };
 
 template <typename T, int D>
@@ -275,11 +282,11 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
 #pragma unroll
   for (int i = 1; i < 4; ++i)
     if (i < a.nrng && b >= a.rng[i].blk0) rg = a.rng[i];
-  const int s0 = rg.lo + (b - rg.blk0) * 32;
-  const int ns = min(32, rg.lo + rg.n - s0);
+  const int s0 = rg.lo + (b - rg.blk0) * kRetimeSlots;
+  const int ns = min(kRetimeSlots, rg.lo + rg.n - s0);
   const RegionPtrs R = layer_region(rg.region == 0 ? a.reg[0] : a.reg[1], (int64_t)blockIdx.y * a.layer_stride);
-  __shared__ int s_dl[32];
-  __shared__ int s_tn[32];
+  __shared__ int s_dl[kRetimeSlots];
+  __shared__ int s_tn[kRetimeSlots];
   const int tid = threadIdx.x;
   const bool placed = a.out_ka[0] != nullptr;      // out of place, by each slot's absolute time
   if (tid < ns) {
@@ -349,15 +356,16 @@ hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
 // compact: destination slot j <- source slot idx[j] (the two window buffers;
 // idx unique, increasing except once where the kept logical entries cross the
 // window ring's wrap).  Two block kinds in one launch:
-//  * key blocks: KS destination slots x all heads; thread (slot, chunk) copies
-//    that 16-byte chunk of the slot's key row for every head (eight heads in
-//    flight) and, for chunk 0, the slot's t and g;
-//  * value blocks: one destination V^T tile (64 slots) of one head.  A slot's
-//    value is a column of a source V^T tile (one element in each 64-slot row),
-//    so lane l of every wave owns destination slot l of the tile and wave w
-//    the rows [w D/4, (w+1) D/4): the lanes of one load read the kept columns
-//    of one source row (a few 128-byte lines, as the kept slots rise), and the
-//    lanes of one store write a whole destination row.  All D/4 loads of a
+//  * key blocks: KS destination slots x KHC heads; thread (slot, chunk) copies
+//    that 16-byte chunk of the slot's key row for each of the block's heads
+//    (all in flight) and, in the first head group, for chunk 0, the slot's t
+//    and g;
+//  * value blocks: 4 VR rows of one destination V^T tile (64 slots) of one
+//    head.  A slot's value is a column of a source V^T tile (one element in
+//    each 64-slot row), so lane l of every wave owns destination slot l of the
+//    tile and each wave VR rows: the lanes of one load read the kept columns of
+//    one source row (a few 128-byte lines, as the kept slots rise), and the
+//    lanes of one store write a whole destination row.  All VR loads of a
 //    thread are in flight before its stores.  Slots past n in the last tile
 //    are written as zeros: attention reads whole tiles and weights those slots
 //    by exactly 0, which needs finite values.
@@ -366,13 +374,15 @@ struct CompactShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int CH = D / E;          // 16-byte chunks per key row
   static constexpr int KS = 256 / CH;       // destination slots per key block
-  static constexpr int VR = D / 4;          // value rows per wave
+  static constexpr int KHC = 2;             // heads per key block
+  static constexpr int VR = 8;              // value rows per wave
+  static constexpr int VP = D / (4 * VR);   // value blocks per destination tile and head
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   using Sh = CompactShape<T, D>;
-  constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, VR = Sh::VR, HU = 8;
+  constexpr int E = Sh::E, CH = Sh::CH, KS = Sh::KS, KHC = Sh::KHC, VR = Sh::VR, VP = Sh::VP;
   const Geo& g = a.geo;
   if (blockIdx.y > 0) {
     a.src = layer_region(a.src, (int64_t)blockIdx.y * a.layer_stride);
@@ -381,11 +391,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   const int tid = threadIdx.x;
   int b = blockIdx.x;
   if (b < a.nk) {
-    const int j = b * KS + tid / CH;
+    const int nhg = (g.H + KHC - 1) / KHC;
+    const int hg = b % nhg;
+    const int j = (b / nhg) * KS + tid / CH;
     const int c = tid % CH;
     if (j >= a.n) return;
     const int sj = a.idx[j];
-    if (c == 0) {
+    if (c == 0 && hg == 0) {
       a.dst.t[j] = a.src.t[sj];
       a.dst.g[j] = a.src.g[sj];
     }
@@ -406,22 +418,23 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     }
     // native 16-byte vectors (HIP's uint4 class would land in private memory here)
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    for (int h0 = 0; h0 < g.H; h0 += HU) {
-      v4u x[HU];
+    const int h0 = hg * KHC;
+    v4u x[KHC];
 #pragma unroll
-      for (int u = 0; u < HU; ++u)
-        if (h0 + u < g.H) x[u] = *reinterpret_cast<const v4u*>(sp + (h0 + u) * ss);
+    for (int u = 0; u < KHC; ++u)
+      if (h0 + u < g.H) x[u] = *reinterpret_cast<const v4u*>(sp + (h0 + u) * ss);
 #pragma unroll
-      for (int u = 0; u < HU; ++u)
-        if (h0 + u < g.H) *reinterpret_cast<v4u*>(dp + (h0 + u) * ds) = x[u];
-    }
+    for (int u = 0; u < KHC; ++u)
+      if (h0 + u < g.H) *reinterpret_cast<v4u*>(dp + (h0 + u) * ds) = x[u];
     return;
   }
   b -= (int)a.nk;
   const int NT = (a.n + kTile - 1) / kTile;
+  const int vp = b % VP;
+  b /= VP;
   const int h = b / NT, dt = b - (b / NT) * NT;
   constexpr int TE = D * kTile;                       // elements per V^T tile
-  const int lane = tid & (kTile - 1), w = tid / kTile;
+  const int lane = tid & (kTile - 1), w = vp * 4 + tid / kTile;
   const int j = dt * kTile + lane;
   const bool ok = j < a.n;
   const int sj = ok ? a.idx[j] : 0;
@@ -451,8 +464,9 @@ hipError_t launch_stage_idx(const int32_t* host_visible, int32_t* dst, int32_t n
 
 template <typename T, int D>
 static hipError_t compact_launch(CompactArgs a, hipStream_t s) {
-  a.nk = (a.n + CompactShape<T, D>::KS - 1) / CompactShape<T, D>::KS;
-  a.nv = (int64_t)a.geo.H * ((a.n + kTile - 1) / kTile);
+  using Sh = CompactShape<T, D>;
+  a.nk = (int64_t)((a.n + Sh::KS - 1) / Sh::KS) * ((a.geo.H + Sh::KHC - 1) / Sh::KHC);
+  a.nv = (int64_t)a.geo.H * ((a.n + kTile - 1) / kTile) * Sh::VP;
   a.nt = 0;
   const int64_t blocks = a.nk + a.nv;
   if (blocks == 0) return hipSuccess;

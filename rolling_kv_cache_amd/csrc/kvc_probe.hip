@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out, 
 
 // Streaming kernels over n16 16-byte elements, grid-stride, four elements in
 // flight per thread.  MODE 0: read (xor-reduce into a per-thread value),
-// 1: copy, 2: write, 3: copy with non-temporal stores.
+// 1: copy, 2: write, 3: copy with non-temporal stores, 4: copy with
+// non-temporal loads and stores.
 template <int MODE>
 __global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                         size_t n16, uint32_t* sink) {
@@ -58,7 +59,10 @@ __global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4_t* __restric
   const u32x4_t fill = {1u, 2u, 3u, (uint32_t)threadIdx.x};
   for (; i + 3 * stride < n16; i += 4 * stride) {
     u32x4_t x[4];
-    if (MODE != 2) {
+    if (MODE == 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+    } else if (MODE != 2) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) x[u] = src[i + u * stride];
     }
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4_t* __restric
       if (MODE == 0) acc ^= x[u];
       if (MODE == 1) dst[i + u * stride] = x[u];
       if (MODE == 2) dst[i + u * stride] = fill;
-      if (MODE == 3) __builtin_nontemporal_store(x[u], &dst[i + u * stride]);
+      if (MODE == 3 || MODE == 4) __builtin_nontemporal_store(x[u], &dst[i + u * stride]);
     }
   }
   for (; i < n16; i += stride) {
@@ -75,8 +79,20 @@ __global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4_t* __restric
     if (MODE == 1) dst[i] = src[i];
     if (MODE == 2) dst[i] = fill;
     if (MODE == 3) __builtin_nontemporal_store(src[i], &dst[i]);
+    if (MODE == 4) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
   }
   if (MODE == 0) sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// One 16-byte element per thread, no loop (a grid of n16 / 256 workgroups):
+// copy (MODE 5) or copy with non-temporal loads and stores (MODE 6).
+template <int MODE>
+__global__ __launch_bounds__(256) void hbm_flat_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                       size_t n16) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  if (MODE == 5) dst[i] = src[i];
+  if (MODE == 6) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
 }  // namespace
@@ -98,10 +114,13 @@ int kvc_probe_wall_clock_khz(int device, int* khz) {
 }
 
 // HBM probe over `bytes` (a multiple of 16): mode 0 read src, 1 copy src ->
-// dst, 2 write dst, 3 copy with non-temporal stores; `blocks` workgroups of
-// 256 threads; sink: device uint32[blocks * 256] (mode 0).
+// dst, 2 write dst, 3 copy with non-temporal stores, 4 copy with non-temporal
+// loads and stores (modes 0-4: `blocks` workgroups of 256 threads,
+// grid-stride), 5 copy and 6 copy with non-temporal loads and stores with one
+// 16-byte element per thread (`blocks` ignored); sink: device uint32[blocks *
+// 256] (mode 0).
 int kvc_probe_hbm(int mode, const void* src, void* dst, size_t bytes, int blocks, uint32_t* sink, void* stream) {
-  if (blocks < 1 || bytes % 16 != 0 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
+  if (blocks < 1 || bytes % 16 != 0 || mode < 0 || mode > 6) return (int)hipErrorInvalidValue;
   if ((mode != 2 && !src) || (mode != 0 && !dst) || (mode == 0 && !sink)) return (int)hipErrorInvalidValue;
   const size_t n16 = bytes / 16;
   const hipStream_t s = (hipStream_t)stream;
@@ -111,7 +130,17 @@ int kvc_probe_hbm(int mode, const void* src, void* dst, size_t bytes, int blocks
     case 0: hipLaunchKernelGGL(hbm_probe_kernel<0>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
     case 1: hipLaunchKernelGGL(hbm_probe_kernel<1>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
     case 2: hipLaunchKernelGGL(hbm_probe_kernel<2>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
-    default: hipLaunchKernelGGL(hbm_probe_kernel<3>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
+    case 3: hipLaunchKernelGGL(hbm_probe_kernel<3>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
+    case 4: hipLaunchKernelGGL(hbm_probe_kernel<4>, dim3(blocks), dim3(256), 0, s, sp, dp, n16, sink); break;
+    default: {
+      const size_t nb = (n16 + 255) / 256;
+      if (nb > 0x7FFFFFFFu) return (int)hipErrorInvalidValue;
+      if (mode == 5)
+        hipLaunchKernelGGL(hbm_flat_kernel<5>, dim3((unsigned)nb), dim3(256), 0, s, sp, dp, n16);
+      else
+        hipLaunchKernelGGL(hbm_flat_kernel<6>, dim3((unsigned)nb), dim3(256), 0, s, sp, dp, n16);
+      break;
+    }
   }
   return (int)hipGetLastError();
 }
