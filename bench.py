@@ -149,6 +149,8 @@ def main():
         torch.cuda.synchronize()
         if i >= 2:
             app_cold.append(a.elapsed_time(b))
+    dt_band = D - 4 * (D // 6)
+    ceil_app_us, ceil_ret_us = same_size_ceilings(dev, stream, ev, flush, N * H * D * 2 * 2, Lk * H * dt_band * 2)
     # attention-mass scores of this chunk's queries over the whole cache (the Deep-Forcing scoring pass)
     qwin = pool[0][0]
     sc_out = cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1])
@@ -231,6 +233,10 @@ def main():
             "retime_GBps_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9, 1),
             "append_hbm_frac_cold": round(app_bytes / (float(np.mean(app_cold)) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "retime_hbm_frac_cold": round(ret_bytes / (ret_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "append_same_size_copy_ceiling_us": round(ceil_app_us, 2),
+            "append_frac_of_copy_ceiling": round(ceil_app_us / (float(np.mean(app_cold)) * 1e3), 4),
+            "retime_same_size_inplace_ceiling_us": round(ceil_ret_us, 2),
+            "retime_frac_of_inplace_ceiling": round(ceil_ret_us / (ret_avg * 1e3), 4),
             "hbm_copy_torch_GBps_measured": round(copy_gbps, 1),
             "score_ms": round(score_ms, 4),
             "score_tflops": round(flop / (score_ms * 1e-3) / 1e12, 2),
@@ -421,17 +427,59 @@ def ceilings(dev, stream, ev):
     a.fill_(1)
     b.fill_(2)
     sink = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
-    for mode, name, nbytes in ((0, "read", n), (1, "copy", 2 * n), (2, "write", n), (3, "copy_nt", 2 * n)):
-        best = 0.0
-        for grid in (1024, 2048, 4096, 16384):
-            f = lambda: lib.kvc_probe_hbm(mode, vp(a.data_ptr()), vp(b.data_ptr()), n, grid, vp(sink.data_ptr()), sp)
-            assert f() == 0
-            torch.cuda.synchronize()
-            ms = back_to_back_ms(stream, ev, f, n=3)
-            best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    flat = {5: "flat", 6: "flat_nt", 7: "flat_inplace"}
+    for name, modes, factor in (("read", (0,), 1), ("write", (2,), 1), ("copy", (1, 3, 4, 5, 6), 2),
+                                ("inplace_rmw", (7,), 2)):
+        best, how = 0.0, None
+        for mode in modes:
+            for grid in ((1,) if mode in flat else (512, 1024, 2048, 4096, 16384)):
+                f = lambda: lib.kvc_probe_hbm(mode, vp(a.data_ptr()), vp(b.data_ptr()), n, grid, vp(sink.data_ptr()),
+                                              sp)
+                assert f() == 0
+                torch.cuda.synchronize()
+                gbps = factor * n / (back_to_back_ms(stream, ev, f, n=3) * 1e-3) / 1e9
+                if gbps > best:
+                    best, how = gbps, flat.get(mode, f"mode {mode}, {grid} workgroups")
         out[f"hbm_{name}_GBps_probe"] = round(best, 1)
+        out[f"hbm_{name}_probe_kernel"] = how
     del a, b, sink
     return out
+
+
+def same_size_ceilings(dev, stream, ev, flush, nbytes_copy, nbytes_inplace):
+    """The plain one-element-per-thread probe kernels on exactly a kernel's own traffic, MALL flushed before
+    each sample (median of 8): a copy of nbytes_copy (read once, written once: the append's pattern) and an
+    in-place read-modify-write of nbytes_inplace (the retime's pattern).  The time such a kernel needs is the
+    ceiling the HBM-bound kernels are set against, beside the 8 TB/s spec."""
+    import ctypes
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "rolling_kv_cache_amd", "libkvc_probe.so"))
+    vp = ctypes.c_void_p
+    lib.kvc_probe_hbm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    sp = vp(stream.cuda_stream)
+    nc = (int(nbytes_copy) + 15) // 16 * 16
+    ni = (int(nbytes_inplace) + 15) // 16 * 16
+    a = torch.ones(max(nc, ni), dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+
+    def cold(f, k=10):
+        ts = []
+        for i in range(k):
+            flush.sum()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            assert f() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+    cp = cold(lambda: lib.kvc_probe_hbm(5, vp(a.data_ptr()), vp(b.data_ptr()), nc, 1, None, sp))
+    ip = cold(lambda: lib.kvc_probe_hbm(7, None, vp(b.data_ptr()), ni, 1, None, sp))
+    del a, b
+    return cp, ip
+
 
 
 def sink_push_and_compact(dev, stream, flush, ev):

@@ -186,6 +186,17 @@ __device__ __forceinline__ void mask_tile_end(f32x16_t* s, int nv, int hl) {
       if (kkey(kb, i) >= nvh) s[kb][i] = -INFINITY;
 }
 
+constexpr float kPLimit = 281474976710656.f;   // 2^48
+
+__device__ __forceinline__ float tile_max(const f32x16_t* sp, float c2) {
+  float mt = sp[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sp[kb][i]);
+  return xhalf_max(mt) * c2;
+}
+
 // a split-key part's rows: the unnormalised O, the reference m and the row sum
 __device__ __forceinline__ void store_partial(const AttendArgs& a, const f32x16_t* o, float m, float lsum, int qrow,
                                               int h, int part, int hl) {
@@ -441,6 +452,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     }
   }
   mask(sa, 0);
+  __syncthreads();   // every wave has read K(0) before step 0 stores K(2) over it
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);
@@ -511,8 +523,11 @@ __global__ __launch_bounds__(256) void merge_split_kernel(AttendArgs a, int kpar
 // Rows pass: per (head, query) the softmax normaliser over every valid key,
 // folded into one log2-domain constant  M = m + log2(l)  with
 // m = max_j c2 s_j and l = sum_j exp2(c2 s_j - m), c2 = log2(e)/sqrt(D); the
-// probability of key j is then exp2(c2 s_j - M).  Workgroup = 4 waves x 32
-// queries, S^T = K.Q^T per 64-key tile as in attention, no P.V.
+// probability of key j is then exp2(c2 s_j - M).  It runs on the attention
+// kernel's 8-wave pipeline with a fixed per-row reference (m = the row's
+// maximum over its first key tile; blocks whose sums leave range are flagged
+// and redone by a 4-wave running-maximum kernel), S^T = K.Q^T per 64-key tile
+// as in attention, no P.V.
 //
 // Columns pass: per (head, key) the sum over queries of exp2(c2 s - M).
 // S = Q.K^T with the lane owning one key column: workgroup = 4 waves x 32
@@ -532,13 +547,17 @@ __device__ __forceinline__ void tile_store_k_padded(const TileRegs& tr, u32x4_t*
   for (int i = 0; i < 4; ++i) lk[((tid >> 4) + 16 * i) * kKSt + c] = tr.k[i];
 }
 
+// The running-maximum rows pass (4 waves x 32 rows).  It recomputes the rows
+// of the 256-row blocks the fixed-reference pass flagged: flags[h * mb256 +
+// mb / 2] for its 128-row block (h, mb).
 __global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a, const uint16_t* qbf, int mblocks,
-                                                                 int total, int ntile0, int ntiles) {
+                                                                 int total, int ntile0, int ntiles, int mb256) {
   __shared__ u32x4_t lks[2][kKTileP];
   const int lin = blockIdx.x;
   if (lin >= total) return;
   const int h = lin / mblocks;
   const int mb = lin - h * mblocks;
+  if (a.flags[h * mb256 + mb / 2] == 0) return;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int qrow = mb * kBM + wave * 32 + l32;
@@ -591,6 +610,132 @@ __global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a, co
   }
   const float lt = xhalf_sum(l);
   if (hl == 0 && qrow < a.Nq) a.m[(int64_t)h * a.Nq + qrow] = m + log2f(lt);
+}
+
+// Rows pass on the 8-wave pipeline (the fixed-reference attention kernel
+// without P.V): 256 query rows per workgroup, key tiles staged in LDS double
+// buffered, S^T(t+1) on the matrix cores interleaved with the exponentials of
+// S^T(t) against a fixed per-row reference (the row's maximum over tile 0), so
+// no tile needs a maximum.  M = ref + log2(sum); a workgroup whose partial sums
+// leave range (or turn non-finite) sets its flag, and the running-maximum pass
+// redoes its rows.
+__device__ __forceinline__ void qk_and_sum(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int kbase,
+                                           const f32x16_t* sp, float negm, float c2, float& psum) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+  float p0s = 0.f, p1s = 0.f;
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    const int kb = step >> 3, ks = step & 7;
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
+    const int e = step * 2;
+    const int pkb = e >> 4, pi = e & 15;
+    p0s += __builtin_amdgcn_exp2f(fmaf(sp[pkb][pi], c2, negm));
+    p1s += __builtin_amdgcn_exp2f(fmaf(sp[pkb][pi + 1], c2, negm));
+  }
+  psum = p0s + p1s;
+  asm volatile("" ::"v"(psum));
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // operand reads ahead
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next operand read
+    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // exp2 x2
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void score_rows_v5f_kernel(ScoreArgs a, const uint16_t* qbf, int mblocks,
+                                                                int total, int per_xcd, int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kKTileP];
+  __shared__ int s_flag;
+  const int wg = blockIdx.x;
+  const int lin = (wg & 7) * per_xcd + (wg >> 3);       // consecutive blocks of a head on one XCD
+  if (lin >= total) return;
+  const int h = lin / mblocks, mb = lin - (lin / mblocks) * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * 256 + wave * 32 + l32;
+  const TileSeq ts = tile_seq_edges_last(a.keys, ntile0, ntiles);
+  const int kbase = perm_row(l32) * kKSt + hl;
+  const int nt = ntiles, last = nt - 1;
+  const TilePtrs tp = tile_ptrs(a.keys, h, tid);
+  if (tid == 0) s_flag = 0;
+  const int c = tid & 15;
+  auto load_k = [&](u32x4_t* st, int r, int base) {
+    const uint16_t* kp = tp.k.get<uint16_t>(r) + base * tp.kstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[i] = *reinterpret_cast<const u32x4_t*>(kp + 32 * i * tp.kstride);
+  };
+  auto store_k = [&](const u32x4_t* st, u32x4_t* lk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lk[((tid >> 4) + 32 * i) * kKSt + c] = st[i];
+  };
+  u32x4_t st[2];
+  load_k(st, ts.region(0), ts.base(0));
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = qbf + ((int64_t)h * a.Nq + min(qrow, a.Nq - 1)) * 128 + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+  }
+  store_k(st, lks[0]);
+  {
+    const int t1 = min(1, last);
+    load_k(st, ts.region(t1), ts.base(t1));
+    store_k(st, lks[1]);
+  }
+  __syncthreads();
+  const float c2 = a.scale * 1.4426950408889634f;
+  f32x16_t sa[2], sb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kKSt + ks * 2]),
+                                                       qf[ks], sa[kb], 0, 0, 0);
+  }
+  mask_tile(sa, ts.lead(0), ts.valid(0), hl);
+  const float negm = -tile_max(sa, c2);       // tile 0 holds a valid key for every row
+  float lsum = 0.f, pmax = 0.f;
+  __syncthreads();                            // every wave has read K(0) before step 0 stores K(2) there
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext, auto masked) {
+    const int tk = min(t + 2, last);
+    constexpr bool any = decltype(masked)::value;
+    load_k(st, any ? ts.region(tk) : ts.region_w(tk), any ? ts.base(tk) : ts.base_w(tk));
+    float psum;
+    qk_and_sum(snext, lks[(t + 1) & 1], qf, kbase, scur, negm, c2, psum);
+    pmax = fmaxf(pmax, psum);
+    lsum += psum;
+    if constexpr (decltype(masked)::value) {
+      const int tn = min(t + 1, last);
+      mask_tile(snext, ts.lead(tn), ts.valid(tn), hl);
+    }
+    store_k(st, lks[t & 1]);
+    __syncthreads();
+  };
+  using Masked = std::integral_constant<bool, true>;
+  using Clean = std::integral_constant<bool, false>;
+  const int clean = max(0, ts.whole_prefix(nt) - 2);
+  int t = 0;
+  for (; t + 1 < clean; t += 2) {
+    step(t, sa, sb, Clean{});
+    step(t + 1, sb, sa, Clean{});
+  }
+  for (; t + 1 < nt; t += 2) {
+    step(t, sa, sb, Masked{});
+    step(t + 1, sb, sa, Masked{});
+  }
+  if (t < nt) step(t, sa, sb, Masked{});   // step t sums tile t (the last step's S^T(t + 1) is unused)
+  if (__ballot(!(pmax <= kPLimit)) != 0 && lane == 0) s_flag = 1;
+  __syncthreads();
+  if (tid == 0) a.flags[lin] = s_flag;
+  const float l = xhalf_sum(lsum);
+  if (hl == 0 && qrow < a.Nq) a.m[(int64_t)h * a.Nq + qrow] = -negm + log2f(l);
 }
 
 constexpr int kQT = 32;                          // query rows per columns-pass tile
@@ -683,8 +828,11 @@ __global__ __launch_bounds__(256, 2) void score_cols_mfma_kernel(ScoreArgs a, co
   }
 }
 
+// Rows pass: the fixed-reference 8-wave kernel, then the running-maximum kernel
+// on the flagged blocks only; then the columns pass.
 hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s) {
   const int mblocks = (a.Nq + kBM - 1) / kBM;
+  const int mb256 = (a.Nq + 255) / 256;
   const int ntile0 = range_tiles(a.keys, 0);
   const int ntile1 = range_tiles(a.keys, 1);
   ScoreArgs b = a;
@@ -703,10 +851,15 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
     nt = ntile1;
   }
   if (nt == 0 || a.Nq == 0) return hipSuccess;
-  const int total = mblocks * a.geo.H;
-  hipLaunchKernelGGL(score_rows_mfma_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt);
+  const int total256 = mb256 * a.geo.H, per_xcd = (total256 + 7) / 8;
+  hipLaunchKernelGGL(score_rows_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, qbf, mb256, total256, per_xcd, n0,
+                     nt);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  // columns: original region numbering (part is indexed by physical slot)
+  const int total = mblocks * a.geo.H;
+  hipLaunchKernelGGL(score_rows_mfma_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt, mb256);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // columns: original region numbering (part is indexed by physical slot).  The 4-wave kernel stays: an
+  // 8-wave version with 128-row query stages (201 VGPRs, one workgroup per CU) was 10 % slower.
   for (int r = 0; r < 2; ++r) {
     if (a.keys.n[r] == 0) continue;
     const int kblocks = (a.keys.n[r] + 127) / 128;
@@ -726,17 +879,6 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
 // scores exceed m so far that a 32-term partial sum of P passes 2^48 (or turns
 // inf/NaN) marks its block in a.flags, and the running-maximum v5 kernel then
 // recomputes exactly the marked blocks.
-constexpr float kPLimit = 281474976710656.f;   // 2^48
-
-__device__ __forceinline__ float tile_max(const f32x16_t* sp, float c2) {
-  float mt = sp[0][0];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sp[kb][i]);
-  return xhalf_max(mt) * c2;
-}
-
 // S^T(t+1) on the matrix cores, interleaved with P(t) = exp2(c2 S^T(t) - m)
 __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int kbase,
                                            const f32x16_t* sp, float negm, float c2, bf16x8_t pb[2][2],
@@ -858,6 +1000,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   mask(sa, 0);
   // tile 0 holds at least one valid key (for every row, also block-causal), so the reference is finite
   const float negm = -tile_max(sa, c2);
+  __syncthreads();   // every wave has read K(0) before step 0 stores K(2) over it
 
   auto step = [&](int t, f32x16_t* scur, f32x16_t* snext, auto masked) {
     const int tk = min(t + 2, last), tv = min(t + 1, last);

@@ -161,6 +161,7 @@ struct ScoreArgs {
   float* m;                               // scratch: row max [H][Nq]
   float* l;                               // scratch: row sum [H][Nq]
   float* part;                            // scratch: per-head column sums [H][cap0 + cap1]
+  int32_t* flags;                         // scratch: one recompute flag per 256-query rows-pass block
   float* scores;                          // out: [n_valid] logical order
   int32_t Nq;
   int32_t qt[32];                         // time of each query frame

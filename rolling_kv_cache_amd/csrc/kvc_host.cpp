@@ -748,7 +748,8 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames) {
   if (!h || q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return 0;
   const size_t Nq = (size_t)q_frames * h->S;
   return align_up((size_t)h->H * Nq * h->D * 4) + 2 * align_up((size_t)h->H * Nq * 4) +
-         align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4) + placed_ka_bytes(h);
+         align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4) + align_up((size_t)h->H * ((Nq + 255) / 256) * 4) +
+         placed_ka_bytes(h);
 }
 
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
@@ -774,6 +775,8 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   p += align_up((size_t)h->H * Nq * 4);
   a.part = (float*)p;
   p += align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4);
+  a.flags = (int32_t*)p;
+  p += align_up((size_t)h->H * ((Nq + 255) / 256) * 4);
   a.q = q_win;
   a.scores = scores;
   a.Nq = (int32_t)Nq;
