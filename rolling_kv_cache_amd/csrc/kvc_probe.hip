@@ -95,6 +95,15 @@ __global__ __launch_bounds__(256) void hbm_flat_kernel(const u32x4_t* __restrict
   if (MODE == 6) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
+// One 16-byte element per thread, read and written back in place (MODE 7).
+__global__ __launch_bounds__(256) void hbm_inplace_kernel(u32x4_t* __restrict__ p, size_t n16) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  u32x4_t x = p[i];
+  x[0] += 1u;
+  p[i] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,11 +126,12 @@ int kvc_probe_wall_clock_khz(int device, int* khz) {
 // dst, 2 write dst, 3 copy with non-temporal stores, 4 copy with non-temporal
 // loads and stores (modes 0-4: `blocks` workgroups of 256 threads,
 // grid-stride), 5 copy and 6 copy with non-temporal loads and stores with one
-// 16-byte element per thread (`blocks` ignored); sink: device uint32[blocks *
-// 256] (mode 0).
+// 16-byte element per thread, 7 read-modify-write of dst in place with one
+// element per thread (`blocks` ignored); sink: device uint32[blocks * 256]
+// (mode 0).
 int kvc_probe_hbm(int mode, const void* src, void* dst, size_t bytes, int blocks, uint32_t* sink, void* stream) {
-  if (blocks < 1 || bytes % 16 != 0 || mode < 0 || mode > 6) return (int)hipErrorInvalidValue;
-  if ((mode != 2 && !src) || (mode != 0 && !dst) || (mode == 0 && !sink)) return (int)hipErrorInvalidValue;
+  if (blocks < 1 || bytes % 16 != 0 || mode < 0 || mode > 7) return (int)hipErrorInvalidValue;
+  if ((mode != 2 && mode != 7 && !src) || (mode != 0 && !dst) || (mode == 0 && !sink)) return (int)hipErrorInvalidValue;
   const size_t n16 = bytes / 16;
   const hipStream_t s = (hipStream_t)stream;
   const u32x4_t* sp = (const u32x4_t*)src;
@@ -137,8 +147,10 @@ int kvc_probe_hbm(int mode, const void* src, void* dst, size_t bytes, int blocks
       if (nb > 0x7FFFFFFFu) return (int)hipErrorInvalidValue;
       if (mode == 5)
         hipLaunchKernelGGL(hbm_flat_kernel<5>, dim3((unsigned)nb), dim3(256), 0, s, sp, dp, n16);
-      else
+      else if (mode == 6)
         hipLaunchKernelGGL(hbm_flat_kernel<6>, dim3((unsigned)nb), dim3(256), 0, s, sp, dp, n16);
+      else
+        hipLaunchKernelGGL(hbm_inplace_kernel, dim3((unsigned)nb), dim3(256), 0, s, dp, n16);
       break;
     }
   }
