@@ -796,7 +796,9 @@ namespace kvc {
 // the tile-transposed values (consecutive p are consecutive slots).  Each
 // update is M = a*M + (1-a)*E with the products and the sum rounded
 // separately; the state is written back and the memory slots get it rounded to
-// the cache dtype.
+// the cache dtype.  The frames go kFoldBatch at a time: their loads (and the
+// state's) are issued together, then folded oldest first.
+constexpr int kFoldBatch = 4;
 template <typename T>
 __device__ __forceinline__ float ema(float m, float e, float a, float b) {
 #pragma clang fp contract(off)
@@ -819,26 +821,37 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
     const int p = (int)(hp % g.S), h = (int)(hp / g.S);
     const int d0 = c * E;
     float st[2][E];
-    for (int f = 0; f < a.n_frames; ++f) {
-      const int slot = (a.hw + f * g.S + p) % a.W_tok;
-      const T* src = d0 < g.DA ? (const T*)a.win.ka + ((int64_t)h * a.win.cap + slot) * g.DA + d0
-                               : (const T*)a.win.kb + ((int64_t)h * a.win.cap + slot) * g.DB + (d0 - g.DA);
-      Vec16<T> x;
-      x.u = *reinterpret_cast<const uint4*>(src);
+    if (!a.init) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if (f == 0) {
-          if (a.init) {
+        const float* sp = a.state_k + (((int64_t)m * g.H + h) * g.S + p) * D + d0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) st[m][e] = Elem<T>::ld(x.e[e]);
+        for (int e = 0; e < E; ++e) st[m][e] = sp[e];
+      }
+    }
+    for (int f0 = 0; f0 < a.n_frames; f0 += kFoldBatch) {
+      Vec16<T> x[kFoldBatch];
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u) {
+        if (f0 + u >= a.n_frames) break;
+        const int slot = (a.hw + (f0 + u) * g.S + p) % a.W_tok;
+        const T* src = d0 < g.DA ? (const T*)a.win.ka + ((int64_t)h * a.win.cap + slot) * g.DA + d0
+                                 : (const T*)a.win.kb + ((int64_t)h * a.win.cap + slot) * g.DB + (d0 - g.DA);
+        x[u].u = *reinterpret_cast<const uint4*>(src);
+      }
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u) {
+        if (f0 + u >= a.n_frames) break;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (f0 + u == 0 && a.init) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) st[m][e] = Elem<T>::ld(x[u].e[e]);
             continue;
           }
-          const float* sp = a.state_k + (((int64_t)m * g.H + h) * g.S + p) * D + d0;
 #pragma unroll
-          for (int e = 0; e < E; ++e) st[m][e] = sp[e];
+          for (int e = 0; e < E; ++e) st[m][e] = ema<T>(st[m][e], Elem<T>::ld(x[u].e[e]), al[m], be[m]);
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e) st[m][e] = ema<T>(st[m][e], Elem<T>::ld(x.e[e]), al[m], be[m]);
       }
     }
 #pragma unroll
@@ -863,19 +876,29 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
   if (hd >= (int64_t)g.H * D) return;
   const int d = (int)(hd % D), h = (int)(hd / D);
   float st[2];
-  for (int f = 0; f < a.n_frames; ++f) {
-    const int slot = (a.hw + f * g.S + p) % a.W_tok;
-    const float e = Elem<T>::ld(((const T*)a.win.v)[v_index(h, a.win.cap, D, slot, d)]);
+  if (!a.init) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (f == 0) {
-        if (a.init) {
-          st[m] = e;
+    for (int m = 0; m < 2; ++m) st[m] = a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p];
+  }
+  for (int f0 = 0; f0 < a.n_frames; f0 += kFoldBatch) {
+    float ev[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      if (f0 + u >= a.n_frames) break;
+      const int slot = (a.hw + (f0 + u) * g.S + p) % a.W_tok;
+      ev[u] = Elem<T>::ld(((const T*)a.win.v)[v_index(h, a.win.cap, D, slot, d)]);
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      if (f0 + u >= a.n_frames) break;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (f0 + u == 0 && a.init) {
+          st[m] = ev[u];
           continue;
         }
-        st[m] = a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p];
+        st[m] = ema<T>(st[m], ev[u], al[m], be[m]);
       }
-      st[m] = ema<T>(st[m], e, al[m], be[m]);
     }
   }
 #pragma unroll

@@ -161,6 +161,28 @@ def test_attend_score_jump(variant):
     check_attention(out, oc.attend(q, 2, 4), f"score jump {variant or 'default'}")
 
 
+def test_scores_score_jump():
+    """Attention-mass scores where the later keys' scores exceed every score of the first key tile by about
+    48 to 90 in exp2 units: the fixed-reference rows pass must flag those query blocks and the
+    running-maximum pass redo them (without it the row sums overflow).  Against the fp64 oracle, with the
+    sum over entries equal to heads x query rows."""
+    w = Workload("sjump", 243, 2, 128, "bf16", 9, 23, 1, 6, (2,) * 4)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(3):
+        _, k, v = chunk_inputs(w, i, frames=2)
+        k = (k * (4.0 if i == 2 else 1.0 / 64)).astype(np.float32)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    (q,) = chunk_inputs(w, 97, tensors=(0,), frames=2)
+    q = (q * 4.0).astype(np.float32)
+    got = gc.score(dev(q, w), [4, 5]).cpu().numpy().astype(np.float64)
+    ref = oc.score(q, 2, [4, 5], f64=True)
+    assert np.isfinite(got).all()
+    assert abs(got.sum() - w.heads * 2 * w.frame_seqlen) < 1e-3 * w.heads * 2 * w.frame_seqlen
+    assert np.max(np.abs(got - ref)) <= 1e-4 * max(1.0, ref.max())
+
+
 # ---------------------------------------------------------------- edge and error paths
 def test_error_paths_leave_state_unchanged():
     from rolling_kv_cache_amd import KVCError
@@ -195,6 +217,30 @@ def test_error_paths_leave_state_unchanged():
             y = gpu_bits(x) if x.dtype not in (torch.int32, torch.int64) else x.cpu().numpy()
             assert np.array_equal(y, before[n]), (j, n)
         assert gc.info() == info, j
+
+
+def test_set_stream_and_paths():
+    """kvc_set_stream makes the new stream wait for the work queued on the old one: appends queued on the
+    default stream, then attention on a second stream without any synchronization, matches the oracle.
+    kvc_set_paths refuses unknown bits."""
+    from rolling_kv_cache_amd import lib
+    w = SMALL_SW
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(6):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), w.chunk_start_frame(i))
+        oc.append(k, v, w.chunk_frames[i], w.chunk_start_frame(i))
+    qd = dev(q, w)
+    s2 = torch.cuda.Stream()
+    gc.set_stream(s2)
+    with torch.cuda.stream(s2):
+        out = gc.attend(qd, w.chunk_start_frame(5))
+    s2.synchronize()
+    check_attention(out.float().cpu().numpy(), oc.attend(q, w.chunk_frames[5], w.chunk_start_frame(5)), "stream")
+    assert lib.kvc_set_paths(gc._h, 8) == 1 and lib.kvc_set_paths(gc._h, 0xFFFF) == 1
+    gc.set_paths(running_max=True, no_split=True)
+    gc.set_paths()
 
 
 def test_compact_validation():
