@@ -353,7 +353,7 @@ def config_streams(dev, stream, ev, cpu):
              "ms_per_chunk_mean": round(float(st.mean()), 4),
              "ms_per_chunk_p10_p50_p90": [round(float(x), 4) for x in np.percentile(st, [10, 50, 90])],
              "stream_total_ms": round(float(ms.sum()), 3),
-             "attend_tflops": round(att_flop / (att_ms * 1e-3) / 1e12, 2),
+             "attend_tflops": round(att_flop / (att_ms * 1e-3) / 1e12, 4),
              "attend_frac_bf16_peak": round(att_flop / (att_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
              "append_GBps_warm": round(app_b / (app_ms * 1e-3) / 1e9, 1),
              "steady_op_ms_per_chunk": {op: round(t / len(steady), 4) for op, t in sorted(op_ms.items())}}
