@@ -306,10 +306,11 @@ __device__ __forceinline__ void qk_and_softmax(f32x16_t* s, const u32x4_t* lk, c
 }
 
 __device__ __forceinline__ void pv_padded(f32x16_t* o, const u32x4_t* lv, int vbase, bf16x8_t pb[2][2]) {
+  // the four accumulators in turn: no MFMA waits for the result of the one before it
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int db = 0; db < 4; ++db) {
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lv[vbase + db * 32 * kVSt + ks * 2]);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks >> 1][ks & 1], o[db], 0, 0, 0);
     }
@@ -628,7 +629,7 @@ __device__ __forceinline__ void qk_and_sum(f32x16_t* s, const u32x4_t* lk, const
   float p0s = 0.f, p1s = 0.f;
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
-    const int kb = step >> 3, ks = step & 7;
+    const int kb = step & 1, ks = step >> 1;      // the two accumulators alternate
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]);
     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
     const int e = step * 2;
@@ -891,7 +892,7 @@ __device__ __forceinline__ void qk_and_exp(f32x16_t* s, const u32x4_t* lk, const
   psum = 0.f;
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
-    const int kb = step >> 3, ks = step & 7;
+    const int kb = step & 1, ks = step >> 1;      // the two accumulators alternate
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kKSt + ks * 2]);
     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
     const int e = step * 2;

@@ -23,7 +23,7 @@ namespace kvc {
 
 constexpr int kTile = 64;        // slots per V tile / attention key tile
 constexpr int kMaxSegs = 4;
-constexpr int kRetimeSlots = 32;  // slots per retime workgroup
+constexpr int kRetimeSlots = 8;   // slots per retime workgroup
 
 // Kernel-path bits (kvc_set_paths): alternatives to the default kernels, for
 // comparisons and tests.

@@ -256,26 +256,79 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// retime: a block owns 32 consecutive slots of one physical range; it reads
-// their times, rotates the time band of every head's key by the slot's
-// actual change (t' - t) and finally writes t'.  Thread p owns chunk p % CA of
-// slot p / CA for every head: its (cos, sin) pairs depend only on the slot's
-// change and the chunk, so they are read from the table once and reused for
-// all heads, and for each head the block's threads cover the 32 contiguous KA
-// rows as one run of 16-byte chunks (fully coalesced).  Heads go eight at a
-// time, so eight chunks are in flight per thread.
+// retime: a block owns kRetimeSlots consecutive slots of one physical range
+// for every head; it reads their times, rotates the time band of every head's
+// key by the slot's actual change (t' - t) and finally writes t'.  Thread
+// (hq, p) owns chunk p % CA of slot p / CA in heads hq, hq + HL, hq + 2 HL, ...
+// (HL head lanes of kRetimeSlots * CA threads): its (cos, sin) pairs depend
+// only on the slot's change and the chunk, so they are read from the table once
+// and reused for all its heads; for each head the lane's threads cover the
+// block's contiguous KA rows as one run of 16-byte chunks.  With 8 slots a
+// block and up to 8 heads per thread, every thread issues all its loads in one
+// round (40 heads: 5 head lanes x 8), and the many small blocks keep enough
+// loads in flight on every CU; a loop over rounds per thread (32 slots a
+// block, 5 rounds of 8 heads) left the stream about a quarter slower.
 template <typename T, int D>
 struct RetimeShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int DT = D - 4 * (D / 6);            // time band width
   static constexpr int CA = (DT + E - 1) / E;           // chunks per KA row (time band, padded)
-  static constexpr int THREADS = (kRetimeSlots * CA + 63) / 64 * 64;
+  static constexpr int LANES = kRetimeSlots * CA;       // threads per head lane
+  static constexpr int HL = 256 / LANES;                // head lanes
+  static constexpr int THREADS = 256;
+  static_assert(HL >= 1, "one head lane fits a block");
 };
+
+// one thread's heads h0, h0 + HL, ..., HU of them, all loads issued before any is used (a head past the
+// last is clamped to it: a repeated load, never stored)
+template <typename T, int D, int HU>
+__device__ __forceinline__ void retime_heads(const RetimeArgs& a, const T* base, T* obase, int64_t hstride, int h0,
+                                             int H, int c, const int32_t* tslot, int tfix, bool fixed, bool placed) {
+  using Sh = RetimeShape<T, D>;
+  constexpr int E = Sh::E, DT = Sh::DT, HL = Sh::HL;
+  Vec16<T> x[HU];
+#pragma unroll
+  for (int u = 0; u < HU; ++u) x[u].u = *reinterpret_cast<const uint4*>(base + min(h0 + u * HL, H - 1) * hstride);
+  // this chunk's rotation, shared by every head: the table row of the common change (the shift itself) is
+  // fetched with the keys, and replaced only where a clamp or a placement makes the slot's change another
+  // (every load unconditional: a pad pair past the band reads the band's last pair and is not used)
+  auto rotation = [&](int dl, float (&cs)[E / 2][2]) {
+    const float* tp = a.tab.tcs + ((size_t)(dl + a.tab.maxpos) * (DT / 2)) * 2;
+#pragma unroll
+    for (int q = 0; q < E / 2; ++q) {
+      const int d = c * E + 2 * q;
+      const float2 v = *reinterpret_cast<const float2*>(tp + min(d, DT - 2));
+      cs[q][0] = d < DT ? v.x : 1.f;
+      cs[q][1] = d < DT ? v.y : 0.f;
+    }
+  };
+  float cs[E / 2][2];
+  rotation(placed ? 0 : a.delta, cs);
+  asm volatile("" ::: "memory");     // the slot's time is read after the key and table loads are issued
+  const int t = fixed ? tfix : *tslot;
+  const int tn = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
+  const int dl = placed ? t : tn - t;
+  if (placed || dl != a.delta) rotation(dl, cs);
+#pragma unroll
+  for (int u = 0; u < HU; ++u) {
+    float xf[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
+#pragma unroll
+    for (int q = 0; q < E / 2; ++q)
+      if (c * E + 2 * q < DT) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
+  }
+#pragma unroll
+  for (int u = 0; u < HU; ++u)
+    if (h0 + u * HL < H) *reinterpret_cast<uint4*>(obase + (h0 + u * HL) * hstride) = x[u].u;
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(RetimeArgs a) {
   using Sh = RetimeShape<T, D>;
-  constexpr int E = Sh::E, DT = Sh::DT, CA = Sh::CA, HU = 8;
+  constexpr int E = Sh::E, CA = Sh::CA, LANES = Sh::LANES, HL = Sh::HL;
   const Geo& g = a.geo;
   const int b = blockIdx.x;
   RangeW rg = a.rng[0];
@@ -285,54 +338,34 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
   const int s0 = rg.lo + (b - rg.blk0) * kRetimeSlots;
   const int ns = min(kRetimeSlots, rg.lo + rg.n - s0);
   const RegionPtrs R = layer_region(rg.region == 0 ? a.reg[0] : a.reg[1], (int64_t)blockIdx.y * a.layer_stride);
-  __shared__ int s_dl[kRetimeSlots];
-  __shared__ int s_tn[kRetimeSlots];
   const int tid = threadIdx.x;
   const bool placed = a.out_ka[0] != nullptr;      // out of place, by each slot's absolute time
-  if (tid < ns) {
-    const int t = (placed && rg.fixed) ? rg.tfix : R.t[s0 + tid];
-    const int tn = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
-    s_dl[tid] = placed ? t : tn - t;
-    s_tn[tid] = tn;
-  }
-  __syncthreads();
-  const int j = tid / CA, c = tid - (tid / CA) * CA;
-  if (j < ns && a.keys) {
-    // this chunk's rotation, shared by every head
-    float cs[E / 2][2];
-    const float* tp = a.tab.tcs + ((size_t)(s_dl[j] + a.tab.maxpos) * (DT / 2)) * 2;
-#pragma unroll
-    for (int q = 0; q < E / 2; ++q) {
-      const int d = c * E + 2 * q;
-      cs[q][0] = d < DT ? tp[d] : 1.f;
-      cs[q][1] = d < DT ? tp[d + 1] : 0.f;
-    }
-    T* base = (T*)R.ka + ((int64_t)s0 + j) * (CA * E) + c * E;
-    T* obase = placed ? (T*)a.out_ka[rg.region] + ((int64_t)s0 + j) * (CA * E) + c * E : base;
+  const int hq = tid / LANES, p = tid - (tid / LANES) * LANES;
+  const int j = p / CA, c = p - (p / CA) * CA;
+  if (hq < HL && j < ns && a.keys) {
+    const T* base = (const T*)R.ka + ((int64_t)s0 + j) * (CA * E) + c * E;
+    T* obase = placed ? (T*)a.out_ka[rg.region] + ((int64_t)s0 + j) * (CA * E) + c * E : (T*)base;
     const int64_t hstride = (int64_t)R.cap * (CA * E);
-    for (int h0 = 0; h0 < g.H; h0 += HU) {
-      Vec16<T> x[HU];
-#pragma unroll
-      for (int u = 0; u < HU; ++u)
-        if (h0 + u < g.H) x[u].u = *reinterpret_cast<const uint4*>(base + (h0 + u) * hstride);
-#pragma unroll
-      for (int u = 0; u < HU; ++u) {
-        if (h0 + u >= g.H) break;
-        float xf[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) xf[e] = Elem<T>::ld(x[u].e[e]);
-#pragma unroll
-        for (int q = 0; q < E / 2; ++q)
-          if (c * E + 2 * q < DT) rot_pair(xf[2 * q], xf[2 * q + 1], cs[q][0], cs[q][1]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[u].e[e] = Elem<T>::st(xf[e]);
-        *reinterpret_cast<uint4*>(obase + (h0 + u) * hstride) = x[u].u;
-      }
-    }
+    // the slot's own time is read by each of its threads (no barrier before the key loads)
+    const int32_t* ts = R.t + s0 + j;
+    const bool fx = placed && rg.fixed;
+    const int nh = (g.H + HL - 1) / HL;       // heads per thread (block-uniform)
+    if (nh <= 1)
+      retime_heads<T, D, 1>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
+    else if (nh <= 2)
+      retime_heads<T, D, 2>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
+    else if (nh <= 4)
+      retime_heads<T, D, 4>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
+    else
+      for (int h0 = hq; h0 < g.H; h0 += HL * 8)
+        retime_heads<T, D, 8>(a, base, obase, hstride, h0, g.H, c, ts, rg.tfix, fx, placed);
   }
   if (placed) return;
-  __syncthreads();
-  if (tid < ns) R.t[s0 + tid] = s_tn[tid];
+  __syncthreads();     // every thread has read its slot's old time
+  if (tid < ns) {
+    const int t = R.t[s0 + tid];
+    R.t[s0 + tid] = a.clamp0 ? max(0, t + a.delta) : t + a.delta;
+  }
 }
 
 hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
