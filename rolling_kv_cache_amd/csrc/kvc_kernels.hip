@@ -170,20 +170,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int h = hb * HPB + tid / (8 * CH);
   if (h >= g.H) return;
   const int slot0 = tile * kTile + grp * 8;
+  // all eight loads issued before any is used: a slot outside the segment reads the segment's nearest row
+  // (a valid address) and is zeroed after, instead of a load under a branch that would wait on its own
   Vec16<T> rows[8];
   bool full = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int src = sg.src + min(max(slot0 + j - sg.dst, 0), sg.n - 1);
+    rows[j].u =
+        *reinterpret_cast<const uint4*>((const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int slot = slot0 + j;
     const bool ok = slot >= sg.dst && slot < sg.dst + sg.n;
     full = full && ok;
-    if (ok) {
-      const int src = sg.src + (slot - sg.dst);
-      rows[j].u =
-          *reinterpret_cast<const uint4*>((const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
-    } else {
-      rows[j].u = make_uint4(0, 0, 0, 0);
-    }
+    if (!ok) rows[j].u = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -280,12 +282,13 @@ struct RetimeShape {
 };
 
 // one thread's heads h0, h0 + HL, ..., HU of them, all loads issued before any is used (a head past the
-// last is clamped to it: a repeated load, never stored)
+// last is clamped to it: a repeated load, never stored; HL is chosen so that this is rare)
 template <typename T, int D, int HU>
 __device__ __forceinline__ void retime_heads(const RetimeArgs& a, const T* base, T* obase, int64_t hstride, int h0,
-                                             int H, int c, const int32_t* tslot, int tfix, bool fixed, bool placed) {
+                                             int HL, int H, int c, const int32_t* tslot, int tfix, bool fixed,
+                                             bool placed) {
   using Sh = RetimeShape<T, D>;
-  constexpr int E = Sh::E, DT = Sh::DT, HL = Sh::HL;
+  constexpr int E = Sh::E, DT = Sh::DT;
   Vec16<T> x[HU];
 #pragma unroll
   for (int u = 0; u < HU; ++u) x[u].u = *reinterpret_cast<const uint4*>(base + min(h0 + u * HL, H - 1) * hstride);
@@ -349,16 +352,22 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
     // the slot's own time is read by each of its threads (no barrier before the key loads)
     const int32_t* ts = R.t + s0 + j;
     const bool fx = placed && rg.fixed;
-    const int nh = (g.H + HL - 1) / HL;       // heads per thread (block-uniform)
-    if (nh <= 1)
-      retime_heads<T, D, 1>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
-    else if (nh <= 2)
-      retime_heads<T, D, 2>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
-    else if (nh <= 4)
-      retime_heads<T, D, 4>(a, base, obase, hstride, hq, g.H, c, ts, rg.tfix, fx, placed);
-    else
-      for (int h0 = hq; h0 < g.H; h0 += HL * 8)
-        retime_heads<T, D, 8>(a, base, obase, hstride, h0, g.H, c, ts, rg.tfix, fx, placed);
+    // heads per thread nh (block-uniform), and the fewest head lanes hl that cover the heads in nh rounds
+    // (12 heads: 4 lanes x 3, not 5 x 3 with three repeated loads)
+    const int nh = (g.H + HL - 1) / HL, hl = (g.H + nh - 1) / nh;
+    if (hq < hl) {
+      if (nh <= 1)
+        retime_heads<T, D, 1>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+      else if (nh <= 2)
+        retime_heads<T, D, 2>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+      else if (nh <= 3)
+        retime_heads<T, D, 3>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+      else if (nh <= 4)
+        retime_heads<T, D, 4>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+      else
+        for (int h0 = hq; h0 < g.H; h0 += hl * 8)
+          retime_heads<T, D, 8>(a, base, obase, hstride, h0, hl, g.H, c, ts, rg.tfix, fx, placed);
+    }
   }
   if (placed) return;
   __syncthreads();     // every thread has read its slot's old time
@@ -825,12 +834,17 @@ namespace kvc {
 // chunk c of the key row) walks the evicted frames oldest first, reading the
 // chunk of the token at position p (consecutive threads read consecutive
 // chunks and rows), and keeps both memories' fp32 state for its E dims in
-// registers.  Value blocks: thread (head, dim d, position p) does the same on
-// the tile-transposed values (consecutive p are consecutive slots).  Each
-// update is M = a*M + (1-a)*E with the products and the sum rounded
-// separately; the state is written back and the memory slots get it rounded to
-// the cache dtype.  The frames go kFoldBatch at a time: their loads (and the
-// state's) are issued together, then folded oldest first.
+// registers.  Value blocks: thread (head, dim d, positions p .. p + VW - 1)
+// does the same on the tile-transposed values, where VW consecutive positions
+// are VW consecutive slots of one tile row: one 16-byte load per frame (when
+// the frame size, the ring head and size and the memory slots are multiples
+// of VW; otherwise one position per thread).  Each update is
+// M = a*M + (1-a)*E with the products and the sum rounded separately; the
+// state is written back and the memory slots get it rounded to the cache
+// dtype.  The frames go kFoldBatch at a time: their loads (and the state's)
+// are issued together, then folded oldest first; a batch's loads past the
+// last frame repeat the last frame's (valid addresses) and are not used, so no
+// load sits under a branch of its own.
 constexpr int kFoldBatch = 4;
 template <typename T>
 __device__ __forceinline__ float ema(float m, float e, float a, float b) {
@@ -840,8 +854,89 @@ __device__ __forceinline__ float ema(float m, float e, float a, float b) {
   return x + y;
 }
 
+template <typename T, int W>
+struct ValRun {       // W consecutive elements of type T
+  union {
+    uint4 u[(W * sizeof(T) + 15) / 16];
+    T e[W];
+  };
+};
+
+// value blocks: W positions per thread (W = 1: any geometry; W = 16 / sizeof(T): aligned runs)
+template <typename T, int D, int W>
+__device__ __forceinline__ void mem_fold_values(const MemFoldArgs& a, int64_t id) {
+  const Geo& g = a.geo;
+  const float al[2] = {a.alpha[0], a.alpha[1]};
+  const float be[2] = {1.f - a.alpha[0], 1.f - a.alpha[1]};
+  const int np = g.S / W;
+  const int p = (int)(id % np) * W;
+  const int64_t hd = id / np;
+  if (hd >= (int64_t)g.H * D) return;
+  const int d = (int)(hd % D), h = (int)(hd / D);
+  float st[2][W] = {};
+  if (!a.init) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float* sp = a.state_v + (((int64_t)m * g.H + h) * D + d) * g.S + p;
+#pragma unroll
+      for (int w = 0; w < W; ++w) st[m][w] = sp[w];
+    }
+  }
+  for (int f0 = 0; f0 < a.n_frames; f0 += kFoldBatch) {
+    ValRun<T, W> x[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int f = min(f0 + u, a.n_frames - 1);
+      const int slot = (a.hw + f * g.S + p) % a.W_tok;
+      const T* src = (const T*)a.win.v + v_index(h, a.win.cap, D, slot, d);
+      if (W * sizeof(T) >= 16) {
+#pragma unroll
+        for (int q = 0; q < (int)(W * sizeof(T) / 16); ++q) x[u].u[q] = reinterpret_cast<const uint4*>(src)[q];
+      } else {
+        x[u].e[0] = src[0];
+      }
+    }
+    // every loaded frame is folded and the result kept only for real frames (a branch here would let the
+    // compiler sink each load into it, one wait per frame)
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const bool real = f0 + u < a.n_frames, first = f0 + u == 0 && a.init;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const float e = Elem<T>::ld(x[u].e[w]);
+          const float nx = first ? e : ema<T>(st[m][w], e, al[m], be[m]);
+          st[m][w] = real ? nx : st[m][w];
+        }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    float* sp = a.state_v + (((int64_t)m * g.H + h) * D + d) * g.S + p;
+    ValRun<T, W> y;
+    if (W % 4 == 0) {
+#pragma unroll
+      for (int w = 0; w < W; w += 4)
+        *reinterpret_cast<float4*>(sp + w) = make_float4(st[m][w], st[m][w + 1], st[m][w + 2], st[m][w + 3]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < W; ++w) sp[w] = st[m][w];
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) y.e[w] = Elem<T>::st(st[m][w]);
+    T* dst = (T*)a.sink.v + v_index(h, a.sink.cap, D, a.mem_lo + m * g.S + p, d);
+    if (W * sizeof(T) >= 16) {
+#pragma unroll
+      for (int q = 0; q < (int)(W * sizeof(T) / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = y.u[q];
+    } else {
+      dst[0] = y.e[0];
+    }
+  }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
+__global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb, int vec) {
   constexpr int E = Elem<T>::E, CH = D / E;
   const Geo& g = a.geo;
   const float al[2] = {a.alpha[0], a.alpha[1]};
@@ -853,7 +948,7 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
     if (hp >= (int64_t)g.H * g.S) return;
     const int p = (int)(hp % g.S), h = (int)(hp / g.S);
     const int d0 = c * E;
-    float st[2][E];
+    float st[2][E] = {};
     if (!a.init) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -866,25 +961,22 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
       Vec16<T> x[kFoldBatch];
 #pragma unroll
       for (int u = 0; u < kFoldBatch; ++u) {
-        if (f0 + u >= a.n_frames) break;
-        const int slot = (a.hw + (f0 + u) * g.S + p) % a.W_tok;
+        const int slot = (a.hw + min(f0 + u, a.n_frames - 1) * g.S + p) % a.W_tok;
         const T* src = d0 < g.DA ? (const T*)a.win.ka + ((int64_t)h * a.win.cap + slot) * g.DA + d0
                                  : (const T*)a.win.kb + ((int64_t)h * a.win.cap + slot) * g.DB + (d0 - g.DA);
         x[u].u = *reinterpret_cast<const uint4*>(src);
       }
 #pragma unroll
       for (int u = 0; u < kFoldBatch; ++u) {
-        if (f0 + u >= a.n_frames) break;
+        const bool real = f0 + u < a.n_frames, first = f0 + u == 0 && a.init;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (f0 + u == 0 && a.init) {
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int e = 0; e < E; ++e) st[m][e] = Elem<T>::ld(x[u].e[e]);
-            continue;
+          for (int e = 0; e < E; ++e) {
+            const float v = Elem<T>::ld(x[u].e[e]);
+            const float nx = first ? v : ema<T>(st[m][e], v, al[m], be[m]);
+            st[m][e] = real ? nx : st[m][e];
           }
-#pragma unroll
-          for (int e = 0; e < E; ++e) st[m][e] = ema<T>(st[m][e], Elem<T>::ld(x[u].e[e]), al[m], be[m]);
-        }
       }
     }
 #pragma unroll
@@ -892,10 +984,10 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
       float* sp = a.state_k + (((int64_t)m * g.H + h) * g.S + p) * D + d0;
       Vec16<T> y;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        sp[e] = st[m][e];
-        y.e[e] = Elem<T>::st(st[m][e]);
-      }
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(sp + e) = make_float4(st[m][e], st[m][e + 1], st[m][e + 2], st[m][e + 3]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) y.e[e] = Elem<T>::st(st[m][e]);
       const int slot = a.mem_lo + m * g.S + p;
       T* dst = d0 < g.DA ? (T*)a.sink.ka + ((int64_t)h * a.sink.cap + slot) * g.DA + d0
                          : (T*)a.sink.kb + ((int64_t)h * a.sink.cap + slot) * g.DB + (d0 - g.DA);
@@ -904,42 +996,12 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb) {
     return;
   }
   const int64_t id = (int64_t)(blockIdx.x - nkb) * 256 + threadIdx.x;
-  const int p = (int)(id % g.S);
-  const int64_t hd = id / g.S;
-  if (hd >= (int64_t)g.H * D) return;
-  const int d = (int)(hd % D), h = (int)(hd / D);
-  float st[2];
-  if (!a.init) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) st[m] = a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p];
-  }
-  for (int f0 = 0; f0 < a.n_frames; f0 += kFoldBatch) {
-    float ev[kFoldBatch];
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      if (f0 + u >= a.n_frames) break;
-      const int slot = (a.hw + (f0 + u) * g.S + p) % a.W_tok;
-      ev[u] = Elem<T>::ld(((const T*)a.win.v)[v_index(h, a.win.cap, D, slot, d)]);
-    }
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      if (f0 + u >= a.n_frames) break;
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (f0 + u == 0 && a.init) {
-          st[m] = ev[u];
-          continue;
-        }
-        st[m] = ema<T>(st[m], ev[u], al[m], be[m]);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    a.state_v[(((int64_t)m * g.H + h) * D + d) * g.S + p] = st[m];
-    ((T*)a.sink.v)[v_index(h, a.sink.cap, D, a.mem_lo + m * g.S + p, d)] = Elem<T>::st(st[m]);
-  }
+  if (vec)
+    mem_fold_values<T, D, (int)(16 / sizeof(T))>(a, id);
+  else
+    mem_fold_values<T, D, 1>(a, id);
 }
+
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void mem_export_kernel(MemExportArgs a) {
@@ -958,10 +1020,13 @@ __global__ __launch_bounds__(256) void mem_export_kernel(MemExportArgs a) {
 
 template <typename T, int D>
 static hipError_t mem_fold_launch(const MemFoldArgs& a, hipStream_t s) {
-  constexpr int CH = D / Elem<T>::E;
-  const int64_t nk = (int64_t)a.geo.H * a.geo.S * CH, nv = (int64_t)a.geo.H * D * a.geo.S;
+  constexpr int CH = D / Elem<T>::E, VW = 16 / (int)sizeof(T);
+  // runs of VW positions are VW consecutive, aligned slots of one tile row in the window and the memory
+  const bool vec = a.geo.S % VW == 0 && a.hw % VW == 0 && a.W_tok % VW == 0 && a.mem_lo % VW == 0 &&
+                   kTile % VW == 0;
+  const int64_t nk = (int64_t)a.geo.H * a.geo.S * CH, nv = (int64_t)a.geo.H * D * a.geo.S / (vec ? VW : 1);
   const int nkb = (int)((nk + 255) / 256), nvb = (int)((nv + 255) / 256);
-  hipLaunchKernelGGL((mem_fold_kernel<T, D>), dim3(nkb + nvb), dim3(256), 0, s, a, nkb);
+  hipLaunchKernelGGL((mem_fold_kernel<T, D>), dim3(nkb + nvb), dim3(256), 0, s, a, nkb, vec ? 1 : 0);
   return hipGetLastError();
 }
 
