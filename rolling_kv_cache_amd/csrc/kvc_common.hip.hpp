@@ -39,11 +39,29 @@ struct Elem<float> {
   __device__ __forceinline__ static float st(float f) { return f; }
 };
 
+
+typedef uint32_t u32x4_stream __attribute__((ext_vector_type(4)));
+
 template <typename T>
 union Vec16 {
   uint4 u;
+  u32x4_stream n;       // the same 16 bytes as a native vector, for the non-temporal builtin
   T e[16 / sizeof(T)];
 };
+
+// 16-byte load into v, with the non-temporal hint when STREAM, for data a kernel streams through once.
+// Measured on MI355X (a ~100 MB copy, MALL flushed): with one to four 16-byte loads in flight per thread
+// the hint makes the copy about a third faster; with eight it makes it slower (and the hint on the stores
+// makes no difference).  The append and retime kernels follow that: streaming loads where a thread holds
+// four or fewer rows (12-head caches), plain loads where it holds eight (40-head caches), which is also
+// what those kernels measured best with.
+template <bool STREAM, typename V>
+__device__ __forceinline__ void ld16(V& v, const void* p) {
+  if constexpr (STREAM)
+    v.n = __builtin_nontemporal_load(reinterpret_cast<const u32x4_stream*>(p));
+  else
+    v.u = *reinterpret_cast<const uint4*>(p);
+}
 
 // One RoPE pair rotation with every product and sum rounded to fp32 (no fused
 // multiply-add):  x' = (x*c) - (y*s),  y' = (x*s) + (y*c).

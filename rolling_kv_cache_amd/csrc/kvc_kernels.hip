@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       Vec16<T> x[HU];
 #pragma unroll
       for (int u = 0; u < HU; ++u)
-        if (h0 + u < h_hi) x[u].u = *reinterpret_cast<const uint4*>(sp + (int64_t)(h0 + u) * a.k_head);
+        if (h0 + u < h_hi) ld16<KHB <= 4>(x[u], sp + (int64_t)(h0 + u) * a.k_head);
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
         const int h = h0 + u;
@@ -177,8 +177,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int src = sg.src + min(max(slot0 + j - sg.dst, 0), sg.n - 1);
-    rows[j].u =
-        *reinterpret_cast<const uint4*>((const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
+    ld16<KHB <= 4>(rows[j], (const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -291,7 +290,7 @@ __device__ __forceinline__ void retime_heads(const RetimeArgs& a, const T* base,
   constexpr int E = Sh::E, DT = Sh::DT;
   Vec16<T> x[HU];
 #pragma unroll
-  for (int u = 0; u < HU; ++u) x[u].u = *reinterpret_cast<const uint4*>(base + min(h0 + u * HL, H - 1) * hstride);
+  for (int u = 0; u < HU; ++u) ld16<HU <= 4>(x[u], base + min(h0 + u * HL, H - 1) * hstride);
   // this chunk's rotation, shared by every head: the table row of the common change (the shift itself) is
   // fetched with the keys, and replaced only where a clamp or a placement makes the slot's change another
   // (every load unconditional: a pad pair past the band reads the band's last pair and is not used)
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     v4u x[KHC];
 #pragma unroll
     for (int u = 0; u < KHC; ++u)
-      if (h0 + u < g.H) x[u] = *reinterpret_cast<const v4u*>(sp + (h0 + u) * ss);
+      if (h0 + u < g.H) x[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(sp + (h0 + u) * ss));
 #pragma unroll
     for (int u = 0; u < KHC; ++u)
       if (h0 + u < g.H) *reinterpret_cast<v4u*>(dp + (h0 + u) * ds) = x[u];
@@ -964,7 +963,7 @@ __global__ __launch_bounds__(256) void mem_fold_kernel(MemFoldArgs a, int nkb, i
         const int slot = (a.hw + min(f0 + u, a.n_frames - 1) * g.S + p) % a.W_tok;
         const T* src = d0 < g.DA ? (const T*)a.win.ka + ((int64_t)h * a.win.cap + slot) * g.DA + d0
                                  : (const T*)a.win.kb + ((int64_t)h * a.win.cap + slot) * g.DB + (d0 - g.DA);
-        x[u].u = *reinterpret_cast<const uint4*>(src);
+        ld16<true>(x[u], src);
       }
 #pragma unroll
       for (int u = 0; u < kFoldBatch; ++u) {
