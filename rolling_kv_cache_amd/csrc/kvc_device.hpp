@@ -23,7 +23,12 @@ namespace kvc {
 
 constexpr int kTile = 64;        // slots per V tile / attention key tile
 constexpr int kMaxSegs = 4;
-constexpr int kRetimeSlots = 8;   // slots per retime workgroup
+// slots per retime workgroup: 8 with 24 or more heads; with fewer, 32 (16 where the time band has more
+// than 8 chunks of 16 bytes), so that a workgroup still moves about as many bytes
+constexpr int retime_band_chunks(int D, int esz) { return (D - 4 * (D / 6) + 16 / esz - 1) / (16 / esz); }
+constexpr int retime_slots(int heads, int D, int esz) {
+  return heads >= 24 ? 8 : (32 * retime_band_chunks(D, esz) <= 256 ? 32 : 16);
+}
 
 // Kernel-path bits (kvc_set_paths): alternatives to the default kernels, for
 // comparisons and tests.

@@ -291,7 +291,7 @@ hipError_t launch_placed_ka(kvc_handle h, char* dst, kvc::KeyRegions* keys) {
     a.rng[a.nrng].lo = 0;
     a.rng[a.nrng].n = n[r];
     a.rng[a.nrng].blk0 = blocks;
-    blocks += (n[r] + kvc::kRetimeSlots - 1) / kvc::kRetimeSlots;
+    blocks += (n[r] + kvc::retime_slots(h->H, h->geo.D, h->geo.esz) - 1) / kvc::retime_slots(h->H, h->geo.D, h->geo.esz);
     ++a.nrng;
   }
   a.keys = 1;
@@ -326,7 +326,7 @@ hipError_t launch_placed_attend(kvc_handle h, kvc::AttendArgs& a) {
     g.blk0 = blocks;
     g.fixed = fixed;
     g.tfix = t;
-    blocks += (n + kvc::kRetimeSlots - 1) / kvc::kRetimeSlots;
+    blocks += (n + kvc::retime_slots(h->H, h->geo.D, h->geo.esz) - 1) / kvc::retime_slots(h->H, h->geo.D, h->geo.esz);
   };
   add(kvc::kSink, 0, h->st.ns, 0, 0);
   add(kvc::kWin, 0, h->st.nw, 0, 0);
@@ -722,7 +722,7 @@ static kvc_status retime_layers(const kvc_handle* hs, int32_t nl, int32_t delta,
     a.rng[i].lo = rs[i].lo;
     a.rng[i].n = rs[i].n;
     a.rng[i].blk0 = blocks;
-    blocks += (rs[i].n + kvc::kRetimeSlots - 1) / kvc::kRetimeSlots;
+    blocks += (rs[i].n + kvc::retime_slots(h->H, h->geo.D, h->geo.esz) - 1) / kvc::retime_slots(h->H, h->geo.D, h->geo.esz);
   }
   a.delta = delta;
   a.clamp0 = clamp0 != 0;

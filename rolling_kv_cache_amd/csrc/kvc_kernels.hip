@@ -257,36 +257,46 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// retime: a block owns kRetimeSlots consecutive slots of one physical range
-// for every head; it reads their times, rotates the time band of every head's
-// key by the slot's actual change (t' - t) and finally writes t'.  Thread
-// (hq, p) owns chunk p % CA of slot p / CA in heads hq, hq + HL, hq + 2 HL, ...
-// (HL head lanes of kRetimeSlots * CA threads): its (cos, sin) pairs depend
+// retime: a block owns SLOTS consecutive slots of one physical range for
+// every head; it reads their times, rotates the time band of every head's key
+// by the slot's actual change (t' - t) and finally writes t'.  Thread (hq, p)
+// owns chunk p % CA of slot p / CA in heads hq, hq + HL, hq + 2 HL, ... (HL
+// head lanes of SLOTS * CA threads): its (cos, sin) pairs depend
 // only on the slot's change and the chunk, so they are read from the table once
 // and reused for all its heads; for each head the lane's threads cover the
 // block's contiguous KA rows as one run of 16-byte chunks.  With 8 slots a
 // block and up to 8 heads per thread, every thread issues all its loads in one
 // round (40 heads: 5 head lanes x 8), and the many small blocks keep enough
 // loads in flight on every CU; a loop over rounds per thread (32 slots a
-// block, 5 rounds of 8 heads) left the stream about a quarter slower.
-template <typename T, int D>
+// block, 5 rounds of 8 heads) left the stream about a quarter slower.  The
+// block has as many head lanes as it needs: at least four heads per thread
+// (with 12 heads, 3 lanes x 4 heads rather than 4 x 3, which measured 7 %
+// slower), at most 256 threads.  With fewer than 24 heads a block takes 32
+// slots instead of 8, so that it still moves tens of kilobytes (12 heads: 8
+// slots a block measured 6 % slower than 32).
+template <typename T, int D, int SLOTS>
 struct RetimeShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int DT = D - 4 * (D / 6);            // time band width
   static constexpr int CA = (DT + E - 1) / E;           // chunks per KA row (time band, padded)
-  static constexpr int LANES = kRetimeSlots * CA;       // threads per head lane
-  static constexpr int HL = 256 / LANES;                // head lanes
-  static constexpr int THREADS = 256;
-  static_assert(HL >= 1, "one head lane fits a block");
+  static constexpr int LANES = SLOTS * CA;              // threads per head lane
+  static constexpr int HLMAX = 256 / LANES;             // head lanes of a 256-thread block
+  static_assert(HLMAX >= 1, "one head lane fits a block");
+  // heads per thread and head lanes for H heads (the block is lanes(H) * LANES threads)
+  static constexpr int heads_per_thread(int H) {
+    const int n = (H + HLMAX - 1) / HLMAX;
+    return n < 4 ? (H < 4 ? H : 4) : n;
+  }
+  static constexpr int lanes(int H) { return (H + heads_per_thread(H) - 1) / heads_per_thread(H); }
 };
 
 // one thread's heads h0, h0 + HL, ..., HU of them, all loads issued before any is used (a head past the
 // last is clamped to it: a repeated load, never stored; HL is chosen so that this is rare)
-template <typename T, int D, int HU>
+template <typename T, int D, int SLOTS, int HU>
 __device__ __forceinline__ void retime_heads(const RetimeArgs& a, const T* base, T* obase, int64_t hstride, int h0,
                                              int HL, int H, int c, const int32_t* tslot, int tfix, bool fixed,
                                              bool placed) {
-  using Sh = RetimeShape<T, D>;
+  using Sh = RetimeShape<T, D, SLOTS>;
   constexpr int E = Sh::E, DT = Sh::DT;
   Vec16<T> x[HU];
 #pragma unroll
@@ -327,45 +337,51 @@ __device__ __forceinline__ void retime_heads(const RetimeArgs& a, const T* base,
     if (h0 + u * HL < H) *reinterpret_cast<uint4*>(obase + (h0 + u * HL) * hstride) = x[u].u;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(RetimeArgs a) {
-  using Sh = RetimeShape<T, D>;
-  constexpr int E = Sh::E, CA = Sh::CA, LANES = Sh::LANES, HL = Sh::HL;
+template <typename T, int D, int SLOTS>
+__global__ __launch_bounds__(256) void retime_kernel(RetimeArgs a) {
+  using Sh = RetimeShape<T, D, SLOTS>;
+  constexpr int E = Sh::E, CA = Sh::CA, LANES = Sh::LANES;
   const Geo& g = a.geo;
   const int b = blockIdx.x;
   RangeW rg = a.rng[0];
 #pragma unroll
   for (int i = 1; i < 4; ++i)
     if (i < a.nrng && b >= a.rng[i].blk0) rg = a.rng[i];
-  const int s0 = rg.lo + (b - rg.blk0) * kRetimeSlots;
-  const int ns = min(kRetimeSlots, rg.lo + rg.n - s0);
+  const int s0 = rg.lo + (b - rg.blk0) * SLOTS;
+  const int ns = min(SLOTS, rg.lo + rg.n - s0);
   const RegionPtrs R = layer_region(rg.region == 0 ? a.reg[0] : a.reg[1], (int64_t)blockIdx.y * a.layer_stride);
   const int tid = threadIdx.x;
   const bool placed = a.out_ka[0] != nullptr;      // out of place, by each slot's absolute time
   const int hq = tid / LANES, p = tid - (tid / LANES) * LANES;
   const int j = p / CA, c = p - (p / CA) * CA;
-  if (hq < HL && j < ns && a.keys) {
+  if (j < ns && a.keys) {
     const T* base = (const T*)R.ka + ((int64_t)s0 + j) * (CA * E) + c * E;
     T* obase = placed ? (T*)a.out_ka[rg.region] + ((int64_t)s0 + j) * (CA * E) + c * E : (T*)base;
     const int64_t hstride = (int64_t)R.cap * (CA * E);
     // the slot's own time is read by each of its threads (no barrier before the key loads)
     const int32_t* ts = R.t + s0 + j;
     const bool fx = placed && rg.fixed;
-    // heads per thread nh (block-uniform), and the fewest head lanes hl that cover the heads in nh rounds
-    // (12 heads: 4 lanes x 3, not 5 x 3 with three repeated loads)
-    const int nh = (g.H + HL - 1) / HL, hl = (g.H + nh - 1) / nh;
+    // heads per thread nh and head lanes hl, as the launch sized the block (block-uniform)
+    const int nh = Sh::heads_per_thread(g.H), hl = Sh::lanes(g.H);
     if (hq < hl) {
       if (nh <= 1)
-        retime_heads<T, D, 1>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+        retime_heads<T, D, SLOTS, 1>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
       else if (nh <= 2)
-        retime_heads<T, D, 2>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+        retime_heads<T, D, SLOTS, 2>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
       else if (nh <= 3)
-        retime_heads<T, D, 3>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+        retime_heads<T, D, SLOTS, 3>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
       else if (nh <= 4)
-        retime_heads<T, D, 4>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
-      else
-        for (int h0 = hq; h0 < g.H; h0 += hl * 8)
-          retime_heads<T, D, 8>(a, base, obase, hstride, h0, hl, g.H, c, ts, rg.tfix, fx, placed);
+        retime_heads<T, D, SLOTS, 4>(a, base, obase, hstride, hq, hl, g.H, c, ts, rg.tfix, fx, placed);
+      else {     // rounds of 8 heads, then the rest (4 or fewer in a round of 4)
+        int h0 = hq;
+        for (; h0 + hl * 7 < g.H; h0 += hl * 8)
+          retime_heads<T, D, SLOTS, 8>(a, base, obase, hstride, h0, hl, g.H, c, ts, rg.tfix, fx, placed);
+        const int rest = h0 < g.H ? (g.H - h0 + hl - 1) / hl : 0;
+        if (rest > 4)
+          retime_heads<T, D, SLOTS, 8>(a, base, obase, hstride, h0, hl, g.H, c, ts, rg.tfix, fx, placed);
+        else if (rest > 0)
+          retime_heads<T, D, SLOTS, 4>(a, base, obase, hstride, h0, hl, g.H, c, ts, rg.tfix, fx, placed);
+      }
     }
   }
   if (placed) return;
@@ -376,19 +392,37 @@ __global__ __launch_bounds__((RetimeShape<T, D>::THREADS)) void retime_kernel(Re
   }
 }
 
+template <typename T, int D, int SLOTS>
+static void retime_launch(const RetimeArgs& a, dim3 grid, hipStream_t s) {
+  using Sh = RetimeShape<T, D, SLOTS>;
+  // at least SLOTS threads (they write the slots' times), at most 256
+  const unsigned threads = (unsigned)max(SLOTS, Sh::lanes(a.geo.H) * Sh::LANES);
+  hipLaunchKernelGGL((retime_kernel<T, D, SLOTS>), grid, dim3(threads), 0, s, a);
+}
+
+template <typename T, int D>
+static void retime_launch(const RetimeArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int FEW = retime_slots(1, D, (int)sizeof(T));     // the slot count with few heads
+  static_assert(FEW == 16 || FEW == 32, "slots per workgroup with few heads");
+  if (retime_slots(a.geo.H, D, (int)sizeof(T)) == 8)
+    retime_launch<T, D, 8>(a, grid, s);
+  else
+    retime_launch<T, D, FEW>(a, grid, s);
+}
+
 hipError_t launch_retime(const RetimeArgs& a, int32_t nblocks, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
   const dim3 grid(nblocks, a.layers > 1 ? (unsigned)a.layers : 1u);
   if (a.geo.esz == 2) {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 128>), grid, dim3(RetimeShape<uint16_t, 128>::THREADS), 0, s, a);
+      retime_launch<uint16_t, 128>(a, grid, s);
     else
-      hipLaunchKernelGGL((retime_kernel<uint16_t, 64>), grid, dim3(RetimeShape<uint16_t, 64>::THREADS), 0, s, a);
+      retime_launch<uint16_t, 64>(a, grid, s);
   } else {
     if (a.geo.D == 128)
-      hipLaunchKernelGGL((retime_kernel<float, 128>), grid, dim3(RetimeShape<float, 128>::THREADS), 0, s, a);
+      retime_launch<float, 128>(a, grid, s);
     else
-      hipLaunchKernelGGL((retime_kernel<float, 64>), grid, dim3(RetimeShape<float, 64>::THREADS), 0, s, a);
+      retime_launch<float, 64>(a, grid, s);
   }
   return hipGetLastError();
 }
