@@ -51,10 +51,10 @@ union Vec16 {
 
 // 16-byte load into v, with the non-temporal hint when STREAM, for data a kernel streams through once.
 // Measured on MI355X (a ~100 MB copy, MALL flushed): with one to four 16-byte loads in flight per thread
-// the hint makes the copy about a third faster; with eight it makes it slower (and the hint on the stores
-// makes no difference).  The append and retime kernels follow that: streaming loads where a thread holds
-// four or fewer rows (12-head caches), plain loads where it holds eight (40-head caches), which is also
-// what those kernels measured best with.
+// the hint makes the copy about a third faster, with eight it makes it slower, and on the stores it makes
+// no difference.  Each kernel uses it where its own measurement favoured it: the append (key blocks of
+// four heads and value blocks of eight tokens: 42.2 -> 37.8 us at 40 heads) and the memory fold take
+// it; the retime takes it only where a thread holds four or fewer rows.
 template <bool STREAM, typename V>
 __device__ __forceinline__ void ld16(V& v, const void* p) {
   if constexpr (STREAM)

@@ -69,16 +69,21 @@ __device__ __forceinline__ SegW pick_seg_v(const AppendArgs& a, int b) {
 // position and the chunk's (cos, sin) pairs are computed once and reused for
 // each head, and all KHB 16-byte loads are in flight before the first store
 // (one round per thread: many blocks, no chain of dependent rounds).  KHB is
-// 8 for caches of 32 heads or more and 4 below (measured: 40 heads 8 > 4 > 20,
-// 12 heads 4 > 8).
-inline int append_khb(int heads) { return heads >= 32 ? 8 : 4; }
+// 4, with non-temporal loads (measured at 40 heads: 4 with those loads beats 8
+// with plain ones by 4 %, and 8 with them is slower still).
+constexpr int kAppendKHB = 4;
 
 template <typename T, int D>
 struct AppendShape {
   static constexpr int E = Elem<T>::E;
   static constexpr int CH = D / E;          // 16-byte chunks per row
   static constexpr int KTB = 256 / CH;      // tokens per key block
-  static constexpr int HPB = 256 / (8 * CH);  // heads per value block
+  // value blocks: VT = 8 tokens per thread (one 16-byte store per dim for bf16; 4 tokens with 8-byte stores
+  // measured 4-12 % slower), VG token groups per tile, HPB heads per block
+  static constexpr int VT = 8;
+  static constexpr int VG = kTile / VT;
+  static constexpr int HPB = 256 / (VG * CH);
+  static_assert(HPB >= 1, "a value block holds a head's tile");
 };
 
 template <typename T, int D, int KHB>
@@ -165,50 +170,59 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int nhb = (g.H + HPB - 1) / HPB;
   const int hb = local % nhb;
   const int tile = local / nhb + sg.dst / kTile;
-  const int grp = tid & 7;
-  const int c = (tid >> 3) % CH;
-  const int h = hb * HPB + tid / (8 * CH);
+  constexpr int VT = Sh::VT, VG = Sh::VG;
+  const int grp = tid % VG;
+  const int c = (tid / VG) % CH;
+  const int h = hb * HPB + tid / (VG * CH);
   if (h >= g.H) return;
-  const int slot0 = tile * kTile + grp * 8;
-  // all eight loads issued before any is used: a slot outside the segment reads the segment's nearest row
+  const int slot0 = tile * kTile + grp * VT;
+  // all VT loads issued before any is used: a slot outside the segment reads the segment's nearest row
   // (a valid address) and is zeroed after, instead of a load under a branch that would wait on its own
-  Vec16<T> rows[8];
+  Vec16<T> rows[VT];
   bool full = true;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < VT; ++j) {
     const int src = sg.src + min(max(slot0 + j - sg.dst, 0), sg.n - 1);
-    ld16<KHB <= 4>(rows[j], (const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
+    ld16<true>(rows[j], (const T*)a.v + (int64_t)src * a.v_tok + (int64_t)h * a.v_head + c * E);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < VT; ++j) {
     const int slot = slot0 + j;
     const bool ok = slot >= sg.dst && slot < sg.dst + sg.n;
     full = full && ok;
     if (!ok) rows[j].u = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < VT; ++j) {
     const int slot = slot0 + j;
     const int src = sg.src + (slot - sg.dst);
     if (slot >= sg.dst && slot < sg.dst + sg.n && src >= a.bank_lo && src < a.bank_hi)
       *reinterpret_cast<uint4*>((T*)a.bank_v + ((int64_t)h * a.bank_tok + (a.g0 + src)) * D + c * E) = rows[j].u;
   }
+  // dim c*E + e of the VT tokens: VT consecutive keys of one V^T row (8 or 16 bytes for bf16, 16 or 32 for
+  // fp32), aligned to their size
   T* vb = (T*)R.v + v_index(h, R.cap, D, slot0, 0);
+  constexpr int SB = VT * (int)sizeof(T);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     T* dst = vb + (size_t)(c * E + e) * kTile;
     if (full) {
       union {
-        uint4 u[sizeof(T) * 8 / 16];
-        T v[8];
+        uint2 w2[SB / 8];
+        T v[VT];
       } o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o.v[j] = rows[j].e[e];
+      for (int j = 0; j < VT; ++j) o.v[j] = rows[j].e[e];
+      if constexpr (SB == 8) {
+        *reinterpret_cast<uint2*>(dst) = o.w2[0];
+      } else {
 #pragma unroll
-      for (int q = 0; q < (int)(sizeof(T) * 8 / 16); ++q) reinterpret_cast<uint4*>(dst)[q] = o.u[q];
+        for (int q = 0; q < SB / 16; ++q)
+          reinterpret_cast<uint4*>(dst)[q] = make_uint4(o.w2[2 * q].x, o.w2[2 * q].y, o.w2[2 * q + 1].x, o.w2[2 * q + 1].y);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < VT; ++j) {
         const int slot = slot0 + j;
         if (slot >= sg.dst && slot < sg.dst + sg.n) dst[j] = rows[j].e[e];
       }
@@ -238,15 +252,12 @@ static void append_blocks(AppendArgs& a, int khb) {
 
 template <typename T, int D>
 static hipError_t append_launch(AppendArgs a, hipStream_t s) {
-  const int khb = append_khb(a.geo.H);
+  constexpr int khb = kAppendKHB;
   append_blocks<T, D>(a, khb);
   const int blocks = a.nkb + a.nvb;
   if (blocks == 0) return hipSuccess;
   const unsigned layers = a.layers > 1 ? (unsigned)a.layers : 1u;
-  if (khb == 8)
-    hipLaunchKernelGGL((append_kernel<T, D, 8>), dim3(blocks, layers), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((append_kernel<T, D, 4>), dim3(blocks, layers), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((append_kernel<T, D, khb>), dim3(blocks, layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
