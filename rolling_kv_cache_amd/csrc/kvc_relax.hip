@@ -86,21 +86,31 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(RelaxArgs a) {
     // kTrip tokens per trip, their loads issued together (a missing token adds zeros); more per trip
     // costs occupancy (16 per trip was a third slower)
     constexpr int kTrip = 4;
+    // the regions' planes by plain selects (an index into the argument struct would be a memory load
+    // ahead of every key load)
+    const uint8_t* pl[2];
+    int cap[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      pl[r] = c < CA ? (const uint8_t*)a.keys.ka[r] + (int64_t)c * E * ESZ
+                     : (const uint8_t*)a.keys.kb[r] + (int64_t)(c - CA) * E * ESZ;
+      cap[r] = a.keys.cap[r];
+    }
+    const int64_t rstride = (c < CA ? g.DA : g.DB) * (int64_t)ESZ;
     for (int tk = s * kRelaxSlice + row; tk < tok1; tk += kTrip * TPI) {
       u32x4_r w[kTrip];
+      // every load issued before the first is used: a token past the slice reads the slice's last token
+      // (a valid address) and adds zeros
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
-        const int t = tk + u * TPI;
-        w[u] = u32x4_r{0u, 0u, 0u, 0u};
-        if (t < tok1) {
-          int r, slot;
-          relax_phys(a, (int)(l0 + t), r, slot);
-          const int64_t rowi = (int64_t)h * a.keys.cap[r] + slot;
-          const uint8_t* p = c < CA ? (const uint8_t*)a.keys.ka[r] + (rowi * g.DA + c * E) * ESZ
-                                    : (const uint8_t*)a.keys.kb[r] + (rowi * g.DB + (c - CA) * E) * ESZ;
-          w[u] = *reinterpret_cast<const u32x4_r*>(p);
-        }
+        int r, slot;
+        relax_phys(a, (int)(l0 + min(tk + u * TPI, tok1 - 1)), r, slot);
+        const int64_t rowi = (int64_t)h * (r ? cap[1] : cap[0]) + slot;
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_r*>((r ? pl[1] : pl[0]) + rowi * rstride));
       }
+#pragma unroll
+      for (int u = 0; u < kTrip; ++u)
+        if (tk + u * TPI >= tok1) w[u] = u32x4_r{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
         if (ESZ == 2) {
