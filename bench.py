@@ -55,7 +55,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard across GPUs "
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard across GPUs "
               "with no exchange on the attention path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -768,7 +768,7 @@ def vendor_context(dev, stream, H, N, Lk, D):
             ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
         out["torch_sdpa_flash_tflops"] = round(4.0 * H * N * Lk * D / (ms * 1e-3) / 1e12, 1)
         del q, k, v
-    except Exception as e:  # backend not available in this build
+    except Exception as e:  # flash backend not available in this torch
         out["torch_sdpa_flash_error"] = str(e)[:120]
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
