@@ -141,6 +141,28 @@ def test_uniform_retime_keeps_attention():
     check_attention(b, a, "uniform retime")
 
 
+@pytest.mark.parametrize("dtype,D,H", [("bf16", 128, 3), ("bf16", 128, 24), ("bf16", 128, 29), ("bf16", 128, 64),
+                                       ("f32", 128, 5), ("bf16", 64, 26), ("f32", 64, 7)])
+def test_retime_workgroup_shapes(dtype, D, H):
+    """Retime on caches whose head count and time-band width pick each workgroup shape (8 slots and up to
+    five head lanes with 24 or more heads, 32 or 16 slots below; a round of eight heads and a rest of more
+    or fewer than four) and whose 55-token frames end inside workgroups: the cache state stays bit-exact
+    with the oracle after plain, clamped and partial-range shifts."""
+    w = Workload(f"rt_{dtype}_{D}_{H}", 230, H, D, dtype, 5, 11, 1, 4, (2,) * 4)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(4):
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    n = gc.info()["n_valid"]
+    for d, cl, lo, hi in [(3, False, 0, None), (-5, True, 0, None), (2, False, 7, n - 13), (-1, True, 50, n)]:
+        log(f"  {w.name} retime {d} {cl} [{lo}, {hi})")
+        gc.retime(d, cl, lo, hi)
+        oc.retime(d, cl, lo, hi)
+        assert_state_equal(gc, oc, w, f"{w.name} after retime {d} {cl} [{lo}, {hi})")
+
+
 @pytest.mark.parametrize("variant", ["", "running_max"])
 def test_attend_score_jump(variant):
     """Keys of the oldest frames are tiny and a later chunk's keys and queries are 4x N(0,1): the later
