@@ -742,9 +742,9 @@ hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s) {
 // score: (1) rotate the query window, (2) per-row max and sum of exp, (3) per
 // (key, head) column sum of the normalized probabilities, (4) sum over heads
 // into logical order.
-// rotated queries to scratch as [H][Nq][D]: fp32 for the general passes, or
-// bf16 (exact: the values are already rounded) for the matrix-core passes
-template <typename T, int D, bool BF16OUT>
+// rotated queries to scratch as [H][Nq][D] in fp32, for the general passes (the
+// values are already rounded to the cache dtype)
+template <typename T, int D>
 __global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
   const Geo& g = a.geo;
   const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
@@ -753,15 +753,33 @@ __global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
   const int i = (int)(gid / g.H);
   float qv[D];
   load_rotated_query<T, D>((const T*)a.q, i, h, a.qt[i / g.S], g, a.tab, qv);
-  if (BF16OUT) {
-    uint16_t* dst = (uint16_t*)a.qh + ((int64_t)h * a.Nq + i) * D;
+  float* dst = a.qh + ((int64_t)h * a.Nq + i) * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) dst[d] = f2bf_rne(qv[d]);
-  } else {
-    float* dst = a.qh + ((int64_t)h * a.Nq + i) * D;
+  for (int d = 0; d < D; ++d) dst[d] = qv[d];
+}
+
+// The matrix-core passes' rotation, to bf16 (exact: the values are already rounded): one thread per
+// 16-byte chunk of a (row, head) query, so that the loads and stores of consecutive threads are
+// consecutive 16-byte pieces of one row (a thread per row writing it element by element, 64 rows apart
+// across a wave, took 57 us at the C3 window).
+__global__ __launch_bounds__(256) void score_rot_bf16_kernel(ScoreArgs a) {
+  constexpr int D = 128, E = Elem<uint16_t>::E, CH = D / E;
+  const Geo& g = a.geo;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)a.Nq * g.H * CH) return;
+  const int c = (int)(gid % CH);
+  const int64_t r = gid / CH;                 // destination row h * Nq + i
+  const int i = (int)(r % a.Nq), h = (int)(r / a.Nq);
+  const int tok = i % g.S;
+  Vec16<uint16_t> x;
+  x.u = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + ((int64_t)i * g.H + h) * D + c * E);
+  float xf[E];
 #pragma unroll
-    for (int d = 0; d < D; ++d) dst[d] = qv[d];
-  }
+  for (int e = 0; e < E; ++e) xf[e] = Elem<uint16_t>::ld(x.e[e]);
+  rotate_run<E>(xf, g, a.tab, c * E, a.qt[i / g.S], tok / g.grid_w, tok % g.grid_w);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x.e[e] = Elem<uint16_t>::st(xf[e]);
+  *reinterpret_cast<uint4*>((uint16_t*)a.qh + r * D + c * E) = x.u;
 }
 
 template <typename T, int D>
@@ -838,7 +856,7 @@ template <typename T, int D>
 static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.Nq * a.geo.H;
   const unsigned b1 = (unsigned)((rows + 63) / 64);
-  hipLaunchKernelGGL((score_rot_kernel<T, D, false>), dim3(b1), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((score_rot_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
   hipLaunchKernelGGL((score_rows_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
   const int64_t cols = (int64_t)(a.keys.cap[0] + a.keys.cap[1]) * a.geo.H;
   hipLaunchKernelGGL((score_cols_kernel<T, D>), dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, a);
@@ -849,7 +867,7 @@ static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
 hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s) {
   if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 128) {
     const int64_t rows = (int64_t)a.Nq * a.geo.H;
-    hipLaunchKernelGGL((score_rot_kernel<uint16_t, 128, true>), dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(score_rot_bf16_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, a);
     if (hipError_t e = launch_score_mfma(a, (const uint16_t*)a.qh, s); e != hipSuccess) return e;
     const int ncap = a.keys.cap[0] + a.keys.cap[1];
     hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
