@@ -127,15 +127,16 @@ struct TileRegs {
   u32x4_t v[4];
 };
 
-// Rotate this lane's 64 query elements (row qc, halves hl) and pack them as the
-// eight B operands of S^T = K . Q^T.
+// Rotate this lane's D/2 query elements (row qc, halves hl) and pack them as the
+// D/16 B operands of S^T = K . Q^T.
+template <int D = 128>
 __device__ __forceinline__ void load_query(bf16x8_t* qf, const AttendArgs& a, int h, int qc, int hl) {
   const Geo& g = a.geo;
   const int tok = qc % g.S;
   const int t = a.t0 + qc / g.S, hp = tok / g.grid_w, wp = tok % g.grid_w;
-  const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)qc * g.H + h) * 128;
+  const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)qc * g.H + h) * D;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < D / 16; ++ks) {
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + ks * 16 + hl * 8);
     const uint32_t xw[4] = {x[0], x[1], x[2], x[3]};
     float f[8];
@@ -217,12 +218,13 @@ __device__ __forceinline__ void store_partial(const AttendArgs& a, const f32x16_
   }
 }
 
+template <int D = 128>
 __device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o, float lsum, int qrow, int h, int hl) {
   const float inv = 1.f / xhalf_sum(lsum);
   if (qrow >= a.Lq) return;
-  uint16_t* op = (uint16_t*)a.out + ((int64_t)qrow * a.geo.H + h) * 128;
+  uint16_t* op = (uint16_t*)a.out + ((int64_t)qrow * a.geo.H + h) * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       union {
@@ -486,6 +488,225 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
     store_partial(a, o, m, lsum, qrow, h, part, hl);
   else
     store_out(a, o, lsum, qrow, h, hl);
+}
+
+// ---------------------------------------------------------------------------
+// bf16, head_dim 64: the running-maximum pipeline above at half the head
+// width.  A stored key is 8 chunks of 16 bytes (3 of the KA plane, dims 0..23,
+// then 5 of the KB plane) and a V^T tile 64 rows of 8 chunks, so each of the
+// 512 threads stages one chunk of each per 64-key tile; a lane holds 4 query
+// fragments and two O accumulators.  Per tile a wave issues 8 MFMAs for S^T
+// and 8 for P.V beside the 32 exponentials of the previous tile.  Keys must be
+// stored rotated (raw-key caches of this width take the general kernel).
+constexpr int kD64A = 24, kD64B = 40;          // key plane widths for head_dim 64
+constexpr int kK64St = 9;                      // K row stride in 16-byte chunks (8 + pad)
+constexpr int kV64St = 9;                      // V^T row stride in 16-byte chunks (8 + pad)
+constexpr int kV64Tile = 64 * kTile;           // elements of one V^T tile
+
+// Thread tid moves chunk (tid & 7) of K row (tid >> 3) and the 16-byte piece tid of the V^T tile.
+struct Tile64Ptrs {
+  RegionPtr k;
+  RegionPtr v;
+  int kstride;
+};
+
+__device__ __forceinline__ Tile64Ptrs tile64_ptrs(const KeyRegions& kr, int h, int tid) {
+  Tile64Ptrs p;
+  const int c = tid & 7;
+  p.kstride = c < 3 ? kD64A : kD64B;
+  const uint16_t* k[2];
+  const uint16_t* v[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint16_t* plane = c < 3 ? (const uint16_t*)kr.ka[r] + c * 8 : (const uint16_t*)kr.kb[r] + (c - 3) * 8;
+    k[r] = plane + ((int64_t)h * kr.cap[r] + (tid >> 3)) * p.kstride;
+    v[r] = (const uint16_t*)kr.v[r] + (int64_t)h * (kr.cap[r] / kTile) * kV64Tile + tid * 8;
+  }
+  p.k.set(k[0], k[1]);
+  p.v.set(v[0], v[1]);
+  return p;
+}
+
+struct Stage64 {
+  u32x4_t k, v;
+};
+
+__device__ __forceinline__ void load64(Stage64& st, const Tile64Ptrs& p, int rk, int bk, int rv, int bv) {
+  st.k = *reinterpret_cast<const u32x4_t*>(p.k.get<uint16_t>(rk) + bk * p.kstride);
+  st.v = *reinterpret_cast<const u32x4_t*>(p.v.get<uint16_t>(rv) + (bv / kTile) * kV64Tile);
+}
+
+__device__ __forceinline__ void store64(const Stage64& st, u32x4_t* lk, u32x4_t* lv, int tid, bool v) {
+  lk[(tid >> 3) * kK64St + (tid & 7)] = st.k;
+  if (v) lv[(tid >> 3) * kV64St + (tid & 7)] = st.v;
+}
+
+// S^T of one tile (8 MFMAs) with the running-maximum softmax of the previous tile woven in, four
+// elements per MFMA; P packed as in the head_dim-128 kernel.
+__device__ __forceinline__ void qk_and_softmax64(f32x16_t* s, const u32x4_t* lk, const bf16x8_t* qf, int kbase,
+                                                 const f32x16_t* sp, float& m, float c2, bf16x8_t pb[2][2],
+                                                 float& psum, float& alpha, bool& upd) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+  const float mt = tile_max(sp, c2);
+  upd = mt > m + 8.f;
+  const float mn = upd ? mt : m;
+  alpha = exp2f(m - mn);
+  m = mn;
+  const float negm = -m;
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  psum = 0.f;
+#pragma unroll
+  for (int step = 0; step < 8; ++step) {
+    const int kb = step >> 2, ks = step & 3;
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kK64St + ks * 2]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[kb], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const int e = step * 4 + j;
+      const int pkb = e >> 4, phf = (e >> 3) & 1, pj = e & 7;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj], c2, negm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sp[pkb][phf * 8 + pj + 1], c2, negm));
+      const bf16x2_t pr = {(__bf16)p0, (__bf16)p1};
+      pb[pkb][phf][pj] = pr[0];
+      pb[pkb][phf][pj + 1] = pr[1];
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
+    }
+  }
+  asm volatile("" ::"v"(psum));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[kb][hf])));
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // first operand reads (lookahead)
+#pragma unroll
+  for (int step = 0; step < 8; ++step) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next operand read
+    __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);   // exp2 x4
+  }
+}
+
+__device__ __forceinline__ void pv64(f32x16_t* o, const u32x4_t* lv, int vbase, bf16x8_t pb[2][2]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lv[vbase + db * 32 * kV64St + ks * 2]);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks >> 1][ks & 1], o[db], 0, 0, 0);
+    }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attend_d64_kernel(AttendArgs a, int mblocks, int total, int per_xcd,
+                                                            int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kBN * kK64St];
+  __shared__ u32x4_t lvs[2][64 * kV64St];
+  const int wg = blockIdx.x;
+  // unit order as in the head_dim-128 kernels (block-causal: longest first, round-robin over the XCDs)
+  const int lin = CAUSAL ? wg : (wg & 7) * per_xcd + (wg >> 3);
+  if (lin >= total) return;
+  const int h = CAUSAL ? lin % a.geo.H : lin / mblocks;
+  const int mb = CAUSAL ? mblocks - 1 - lin / a.geo.H : lin - h * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * 256 + wave * 32 + l32;
+  const TileSeq ts = CAUSAL ? tile_seq(a.keys, ntile0, ntiles) : tile_seq_edges_last(a.keys, ntile0, ntiles);
+  const int kbase = perm_row(l32) * kK64St + hl;
+  const int vbase = l32 * kV64St + hl;
+  int nt = ntiles, lim = 0, lim_lo = 0;
+  if (CAUSAL) {
+    const int cb = a.causal_block, nall = a.keys.n[0] + a.keys.n[1];
+    auto limit = [&](int r) { return min(nall, (r / cb + 1) * cb); };
+    const int r0 = mb * 256, r1 = min(a.Lq, r0 + 256) - 1;
+    lim_lo = limit(r0);
+    lim = limit(min(qrow, a.Lq - 1));
+    const int lim_hi = limit(r1), n0 = a.keys.n[0];
+    nt = lim_hi <= n0 ? (lim_hi + kBN - 1) / kBN : ntile0 + (lim_hi - n0 + kBN - 1) / kBN;
+  }
+  const int last = nt - 1;
+  auto mask = [&](f32x16_t* sv, int t) {
+    const int nv = CAUSAL ? ts.valid_w(t) : ts.valid(t);
+    if (CAUSAL) {
+      const int lb = t < ntile0 ? t * kBN : a.keys.n[0] + (t - ntile0) * kBN;
+      if (lb + kBN > lim_lo) {
+        mask_tile_end(sv, min(nv, lim - lb), hl);
+        return;
+      }
+    }
+    mask_tile(sv, CAUSAL ? ts.lead_w(t) : ts.lead(t), nv, hl);
+  };
+  auto reg = [&](int t) { return CAUSAL ? ts.region_w(t) : ts.region(t); };
+  auto bas = [&](int t) { return CAUSAL ? ts.base_w(t) : ts.base(t); };
+  const Tile64Ptrs tp = tile64_ptrs(a.keys, h, tid);
+
+  Stage64 st;
+  load64(st, tp, reg(0), bas(0), reg(0), bas(0));
+  bf16x8_t qf[4];
+  load_query<64>(qf, a, h, min(qrow, a.Lq - 1), hl);
+  store64(st, lks[0], lvs[0], tid, true);
+  {
+    const int t1 = min(1, last);
+    load64(st, tp, reg(t1), bas(t1), 0, 0);
+    store64(st, lks[1], lvs[1], tid, false);
+  }
+  f32x16_t o[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  const float c2 = a.scale * 1.4426950408889634f;
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, lks[0][kbase + kb * 32 * kK64St + ks * 2]);
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sa[kb], 0, 0, 0);
+    }
+  }
+  mask(sa, 0);
+  __syncthreads();   // every wave has read K(0) before step 0 stores K(2) over it
+
+  // step t: S^T(t+1) beside the softmax of tile t, then P(t).V(t); K(t+2) and V(t+1) staged meanwhile
+  auto step = [&](int t, f32x16_t* scur, f32x16_t* snext) {
+    const int tk = min(t + 2, last), tv = min(t + 1, last);
+    load64(st, tp, reg(tk), bas(tk), reg(tv), bas(tv));
+    bf16x8_t pb[2][2];
+    float psum, alpha;
+    bool upd;
+    qk_and_softmax64(snext, lks[(t + 1) & 1], qf, kbase, scur, m, c2, pb, psum, alpha, upd);
+    if (__ballot(upd) != 0) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+    lsum = lsum * alpha + psum;
+    pv64(o, lvs[t & 1], vbase, pb);
+    mask(snext, min(t + 1, last));
+    store64(st, lks[t & 1], lvs[(t + 1) & 1], tid, true);
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < nt) step(t, sa, sb);
+  store_out<64>(a, o, lsum, qrow, h, hl);
 }
 
 // out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s) over the key parts,
@@ -1051,16 +1272,15 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
 // Launch shapes of the matrix-core attention.
 enum class AttendPlan { kFixedRef, kRunningMax, kCausalFixedRef, kCausalRunningMax, kSplit };
 
-static hipError_t attend_launch(const AttendArgs& a, AttendPlan plan, hipStream_t s) {
-  const int mblocks = (a.Lq + 255) / 256;
-  const int total = mblocks * a.geo.H;
-  const int per_xcd = (total + 7) / 8;
+// b = a with region 0 non-empty (a region with no valid keys contributes no tiles), n0 / nt = region 0's
+// tiles and all tiles; false when there is no work
+static bool attend_regions(const AttendArgs& a, AttendArgs& b, int& n0, int& nt) {
   const int ntile0 = range_tiles(a.keys, 0);
   const int ntile1 = range_tiles(a.keys, 1);
-  if (total == 0 || ntile0 + ntile1 == 0) return hipSuccess;
-  AttendArgs b = a;
-  int n0 = ntile0, nt = ntile0 + ntile1;
-  // a region with no valid keys contributes no tiles; keep region 0 non-empty
+  b = a;
+  n0 = ntile0;
+  nt = ntile0 + ntile1;
+  if (a.Lq == 0 || a.geo.H == 0 || nt == 0) return false;
   if (ntile0 == 0) {
     b.keys.ka[0] = a.keys.ka[1];
     b.keys.kb[0] = a.keys.kb[1];
@@ -1074,6 +1294,16 @@ static hipError_t attend_launch(const AttendArgs& a, AttendPlan plan, hipStream_
     n0 = ntile1;
     nt = ntile1;
   }
+  return true;
+}
+
+static hipError_t attend_launch(const AttendArgs& a, AttendPlan plan, hipStream_t s) {
+  const int mblocks = (a.Lq + 255) / 256;
+  const int total = mblocks * a.geo.H;
+  const int per_xcd = (total + 7) / 8;
+  AttendArgs b;
+  int n0, nt;
+  if (!attend_regions(a, b, n0, nt)) return hipSuccess;
   const dim3 grid(8 * per_xcd), block(512);
   switch (plan) {
     case AttendPlan::kSplit: {   // fixed-reference partials, flagged parts again, then the merge
@@ -1129,6 +1359,25 @@ hipError_t launch_attend_mfma(const AttendArgs& a, uint32_t paths, hipStream_t s
   if (a.causal_block > 0)
     return attend_launch(a, running_max ? AttendPlan::kCausalRunningMax : AttendPlan::kCausalFixedRef, s);
   return attend_launch(a, running_max ? AttendPlan::kRunningMax : AttendPlan::kFixedRef, s);
+}
+
+// bf16, head_dim 64: the running-maximum kernel of that width (keys stored rotated; plain or block-causal)
+hipError_t launch_attend_mfma64(const AttendArgs& a, hipStream_t s) {
+  if (a.raw || a.geo.D != 64 || a.geo.esz != 2 || a.geo.DA != kD64A || a.geo.DB != kD64B)
+    return hipErrorInvalidValue;
+  const int mblocks = (a.Lq + 255) / 256;
+  const int total = mblocks * a.geo.H;
+  const int per_xcd = (total + 7) / 8;
+  AttendArgs b;
+  int n0, nt;
+  if (!attend_regions(a, b, n0, nt)) return hipSuccess;
+  if (a.causal_block > 0)
+    hipLaunchKernelGGL((attend_d64_kernel<true>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd, n0,
+                       nt);
+  else
+    hipLaunchKernelGGL((attend_d64_kernel<false>), dim3(8 * per_xcd), dim3(512), 0, s, b, mblocks, total, per_xcd,
+                       n0, nt);
+  return hipGetLastError();
 }
 
 }  // namespace kvc

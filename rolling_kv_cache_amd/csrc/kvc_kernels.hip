@@ -722,6 +722,7 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
 
 hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s) {
   if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 128) return launch_attend_mfma(a, paths, s);
+  if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 64 && !a.raw) return launch_attend_mfma64(a, s);
   const int64_t total = (int64_t)a.Lq * a.geo.H;
   const unsigned blocks = (unsigned)((total + 63) / 64);
   if (a.geo.esz == 2) {

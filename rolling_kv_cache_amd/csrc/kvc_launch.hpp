@@ -14,11 +14,13 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 // copy n int32 from pinned host memory (its device-visible address) to device memory
 hipError_t launch_stage_idx(const int32_t* host_visible, int32_t* dst, int32_t n, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s);
-// Attention: the matrix-core path for bf16 with head_dim 128, else the
-// general per-row path; `paths` holds kPath* bits (kPathGeneral selects the
-// general path for any cache).
+// Attention: the matrix-core path for bf16 with head_dim 128, and for bf16
+// with head_dim 64 on a cache of rotated keys, else the general per-row path;
+// `paths` holds kPath* bits (kPathGeneral selects the general path for any
+// cache).
 hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s);
 hipError_t launch_attend_mfma(const AttendArgs& a, uint32_t paths, hipStream_t s);
+hipError_t launch_attend_mfma64(const AttendArgs& a, hipStream_t s);
 // Scores: the matrix-core passes for bf16 with head_dim 128, else the general
 // per-row/per-column path (kPathGeneral in `paths` selects the latter).
 hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s);

@@ -75,6 +75,22 @@ def test_small_bf16_sliding_window_general_path():
     _drive(SMALL_SW, general=True)
 
 
+SMALL_SW64 = Workload("sw64_small", 221, 3, 64, "bf16", 6, 10, 2, 6, (1, 3, 3, 3, 2, 3, 3, 1, 3))
+
+
+@pytest.mark.parametrize("general", [False, True])
+def test_small_bf16_head_dim_64(general):
+    """bf16 head_dim 64 (key planes of 24 + 40 dims) through its matrix-core kernel and through the general
+    path: the same 60-token frames, straddling first chunk, ragged tiles and wrap-around as above."""
+    _drive(SMALL_SW64, general=general)
+
+
+def test_head_dim_64_many_query_blocks():
+    """bf16 head_dim 64 with 12 heads and 3-frame chunks of 552 tokens (1656 query rows: six full 256-row
+    blocks and a ragged seventh) over a sink and a window whose tiles end inside a tile."""
+    _drive(Workload("sw64_big", 222, 12, 64, "bf16", 23, 24, 2, 7, (3, 3, 3, 3)))
+
+
 def test_small_rolling_sink():
     base = WORKLOADS["c4"]
     _drive(Workload("c4_small", 203, 2, 128, "bf16", 4, 8, base.sink_frames, base.window_frames,
@@ -341,6 +357,18 @@ def test_block_causal_small(general, sink, block):
     check_attention(out, oc.attend_block_causal(q, 8, 0, block), f"block-causal sink {sink} block {block}")
     if block >= 8:
         check_attention(out, gc.attend(dev(q, w), 0).float().cpu().numpy(), "one block == attend")
+
+
+@pytest.mark.parametrize("general", [False, True])
+@pytest.mark.parametrize("sink,block", [(0, 2), (1, 3), (0, 1)])
+def test_block_causal_head_dim_64(general, sink, block):
+    """The block-causal clip of the test above at head_dim 64 (bf16): its own matrix-core kernel and the
+    general path against the oracle."""
+    w = Workload("bc64", 223, 2, 64, "bf16", 9, 23, sink, 8 - sink, (2,) * 4)
+    gc, oc, q = _clip(w, 8)
+    with paths(gc, general=general):
+        out = gc.attend_block_causal(dev(q, w), 0, block).float().cpu().numpy()
+    check_attention(out, oc.attend_block_causal(q, 8, 0, block), f"head_dim 64 block-causal sink {sink} block {block}")
 
 
 def test_block_causal_partial_cache_and_time_offset():
