@@ -75,7 +75,7 @@ typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
  * and the time band raw; kvc_attend rotates each key's time band at its slot's
  * current time, so every attended key equals a fresh rotation of the raw key
  * and kvc_retime only rewrites time indices.  For bf16 caches with head_dim
- * 128 the workspace holds a copy of the keys' time-band plane that each
+ * 128 or 64 the workspace holds a copy of the keys' time-band plane that each
  * kvc_attend first fills, in one pass, with every slot (and the memory
  * tokens) placed at its current time; the attention then reads it (other
  * caches rotate inside the attention kernel).  kvc_score and kvc_relax_scores
@@ -182,10 +182,9 @@ kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
  *  KVC_PATH_RUNNING_MAX  attention: the running-maximum kernel alone instead
  *                        of the fixed per-row reference with its recompute pass
  *  KVC_PATH_GENERAL      attention and scores: the general one-thread-per-row
- *                        passes (the only ones for fp32 caches, for scores of
- *                        head_dim 64 caches, and for attention of raw-key
- *                        head_dim 64 caches; bf16 head_dim 64 attention of
- *                        rotated keys otherwise runs on its own matrix-core
+ *                        passes (the only ones for fp32 caches and for
+ *                        scores of head_dim 64 caches; bf16 head_dim 64
+ *                        attention otherwise runs on its own matrix-core
  *                        kernel, with a running maximum)
  *  KVC_PATH_NO_SPLIT     attention: never split the keys (KVC_CREATE_SPLIT_ATTEND) */
 #define KVC_PATH_RUNNING_MAX 1u

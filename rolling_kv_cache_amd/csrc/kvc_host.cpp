@@ -106,9 +106,9 @@ Layout make_layout(int32_t sink_frames, int32_t window_frames, int32_t S, int32_
     L.mem_k = take((size_t)2 * H * S * D * 4);
     L.mem_v = take((size_t)2 * H * S * D * 4);
   }
-  // raw-key caches on the matrix-core path: KA planes with every slot's time band placed at its
-  // current time, written once per attend call and read by the plain attention kernels
-  if ((cflags & KVC_CREATE_RAW_KEYS) && L.esz == 2 && D == 128) {
+  // raw-key caches on the matrix-core paths (bf16, head_dim 128 or 64): KA planes with every slot's time
+  // band placed at its current time, written once per attend call and read by the plain attention kernels
+  if ((cflags & KVC_CREATE_RAW_KEYS) && L.esz == 2 && (D == 128 || D == 64)) {
     L.placed_sink = take((size_t)H * L.SP * L.DA * L.esz);
     L.placed_win = take((size_t)H * L.WP * L.DA * L.esz);
   }

@@ -468,10 +468,12 @@ from dataclasses import replace as _replace
 
 
 @pytest.mark.parametrize("general", [False, True])
-def test_raw_keys_sliding_window(general):
+@pytest.mark.parametrize("base", [SMALL_SW, SMALL_SW64], ids=["d128", "d64"])
+def test_raw_keys_sliding_window(general, base):
     """Stored keys (time band raw, height/width rotated) bit-exact, attention against the oracle's fresh
-    rotation, on the ragged sink/window workload."""
-    _drive(_replace(SMALL_SW, name="sw_raw", raw_keys=True), general=general)
+    rotation, on the ragged sink/window workload (head_dim 128 and 64: the time band placed, then the
+    matrix-core kernel of that width, or the general path)."""
+    _drive(_replace(base, name="sw_raw", raw_keys=True), general=general)
 
 
 def test_raw_keys_tiny_fp32():
@@ -549,10 +551,11 @@ MEM_SMALL = _replace(SMALL_SW, name="mem_small", raw_keys=True, memory=(0.9, 0.5
 
 
 @pytest.mark.parametrize("general", [False, True])
-def test_memory_tokens_small(general):
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_memory_tokens_small(general, head_dim):
     """Memory state bit-exact and attention (sink + memories + window) after every chunk, with 60-token
-    frames whose memory slots straddle 64-slot tiles."""
-    _drive_memory(MEM_SMALL, general=general)
+    frames whose memory slots straddle 64-slot tiles; head_dim 128 and 64."""
+    _drive_memory(MEM_SMALL if head_dim == 128 else _replace(MEM_SMALL, name="mem64", head_dim=64), general=general)
 
 
 def test_memory_tokens_tiny_fp32_and_extreme_rates():
