@@ -182,10 +182,9 @@ kvc_status kvc_set_stream(kvc_handle h, void* hip_stream);
  *  KVC_PATH_RUNNING_MAX  attention: the running-maximum kernel alone instead
  *                        of the fixed per-row reference with its recompute pass
  *  KVC_PATH_GENERAL      attention and scores: the general one-thread-per-row
- *                        passes (the only ones for fp32 caches and for
- *                        scores of head_dim 64 caches; bf16 head_dim 64
- *                        attention otherwise runs on its own matrix-core
- *                        kernel, with a running maximum)
+ *                        passes (the only ones for fp32 caches; bf16 head_dim
+ *                        64 caches otherwise run matrix-core kernels of their
+ *                        own width, with a running maximum)
  *  KVC_PATH_NO_SPLIT     attention: never split the keys (KVC_CREATE_SPLIT_ATTEND) */
 #define KVC_PATH_RUNNING_MAX 1u
 #define KVC_PATH_GENERAL 2u

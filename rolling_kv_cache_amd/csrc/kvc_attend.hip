@@ -1093,6 +1093,192 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
 }
 
 // ---------------------------------------------------------------------------
+// Scores for bf16 head_dim 64 (key rows of 8 chunks: 3 of the KA plane, 5 of
+// the KB plane).  Rows pass: 4 waves x 32 query rows, 64-key tiles double
+// buffered in LDS, running maximum, every block (no flags).  Columns pass: as
+// for head_dim 128, a lane's key column held in registers (4 fragments), query
+// tiles of 32 rows (one 16-byte chunk per thread) streamed through LDS.
+__global__ __launch_bounds__(256, 2) void score_rows_d64_kernel(ScoreArgs a, const uint16_t* qbf, int mblocks,
+                                                                int total, int ntile0, int ntiles) {
+  __shared__ u32x4_t lks[2][kBN * kK64St];
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int h = lin / mblocks;
+  const int mb = lin - h * mblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int qrow = mb * kBM + wave * 32 + l32;
+  const TileSeq ts = tile_seq(a.keys, ntile0, ntiles);
+  const int kbase = perm_row(l32) * kK64St + hl;
+  const Tile64Ptrs tp = tile64_ptrs(a.keys, h, tid);   // rows (tid >> 3) and (tid >> 3) + 32 of a tile
+  auto load_k = [&](u32x4_t* st, int r, int base) {
+    const uint16_t* kp = tp.k.get<uint16_t>(r) + base * tp.kstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[i] = *reinterpret_cast<const u32x4_t*>(kp + 32 * i * tp.kstride);
+  };
+  auto store_k = [&](const u32x4_t* st, u32x4_t* lk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lk[((tid >> 3) + 32 * i) * kK64St + (tid & 7)] = st[i];
+  };
+  u32x4_t st[2];
+  load_k(st, ts.region(0), ts.base(0));
+  bf16x8_t qf[4];
+  {
+    const uint16_t* qp = qbf + ((int64_t)h * a.Nq + min(qrow, a.Nq - 1)) * 64 + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+  }
+  store_k(st, lks[0]);
+  __syncthreads();
+  const float c2 = a.scale * 1.4426950408889634f;
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) load_k(st, ts.region(t + 1), ts.base(t + 1));
+    f32x16_t sc[2];
+    const u32x4_t* lk = lks[t & 1];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lk[kbase + kb * 32 * kK64St + ks * 2]),
+                                                         qf[ks], sc[kb], 0, 0, 0);
+    }
+    mask_tile(sc, ts.lead(t), ts.valid(t), hl);
+    // tile 0 (logical order) holds a valid key, so m is finite from the first tile on
+    const float mn = fmaxf(m, tile_max(sc, c2));
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c2, -mn));
+    l = l * __builtin_amdgcn_exp2f(m - mn) + ps;
+    m = mn;
+    if (more) store_k(st, lks[(t + 1) & 1]);
+    __syncthreads();
+  }
+  const float lt = xhalf_sum(l);
+  if (hl == 0 && qrow < a.Nq) a.m[(int64_t)h * a.Nq + qrow] = m + log2f(lt);
+}
+
+__global__ __launch_bounds__(256, 2) void score_cols_d64_kernel(ScoreArgs a, const uint16_t* qbf, int region,
+                                                                int kblocks, int total) {
+  constexpr int kQT64 = 32;                      // query rows per tile
+  __shared__ u32x4_t lq[2][kQT64 * kK64St];
+  __shared__ __attribute__((aligned(16))) float lm[2][kQT64];
+  const int lin = blockIdx.x;
+  if (lin >= total) return;
+  const int h = lin / kblocks;
+  const int kblk = lin - h * kblocks;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int nk = a.keys.n[region];
+  const int key = kblk * 128 + wave * 32 + l32;
+  bf16x8_t kf[4];
+  {
+    const int kk = min(key, nk - 1);
+    const int64_t row = (int64_t)h * a.keys.cap[region] + kk;
+    const uint16_t* ka = (const uint16_t*)a.keys.ka[region] + row * kD64A;
+    const uint16_t* kb = (const uint16_t*)a.keys.kb[region] + row * kD64B;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d = ks * 16 + hl * 8;
+      const uint16_t* src = d < kD64A ? ka + d : kb + (d - kD64A);
+      kf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src));
+    }
+  }
+  const int nqt = (a.Nq + kQT64 - 1) / kQT64;
+  const uint16_t* qh = qbf + (int64_t)h * a.Nq * 64;
+  const float* mrow = a.m + (int64_t)h * a.Nq;
+  // thread tid stages chunk (tid & 7) of tile row (tid >> 3), and threads 0..31 the rows' M
+  auto load_q = [&](int qt, u32x4_t& st, float& mv) {
+    const int r = min(qt * kQT64 + (tid >> 3), a.Nq - 1);
+    st = *reinterpret_cast<const u32x4_t*>(qh + (int64_t)r * 64 + (tid & 7) * 8);
+    if (tid < kQT64) {
+      const int rm = qt * kQT64 + tid;
+      mv = rm < a.Nq ? mrow[rm] : INFINITY;   // rows past the window contribute exp2(-inf) = 0
+    }
+  };
+  auto store_q = [&](int buf, const u32x4_t& st, float mv) {
+    lq[buf][(tid >> 3) * kK64St + (tid & 7)] = st;
+    if (tid < kQT64) lm[buf][tid] = mv;
+  };
+  u32x4_t st;
+  float mv = 0.f;
+  load_q(0, st, mv);
+  store_q(0, st, mv);
+  __syncthreads();
+  const float c2 = a.scale * 1.4426950408889634f;
+  const int qbase = l32 * kK64St + hl;
+  float acc = 0.f;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const bool more = qt + 1 < nqt;
+    if (more) load_q(qt + 1, st, mv);
+    const u32x4_t* q = lq[qt & 1];
+    f32x16_t c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q[qbase + ks * 2]), kf[ks], c, 0, 0, 0);
+    // accumulator i is query row (i/4)*8 + hl*4 + i%4 of the tile
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 mg = *reinterpret_cast<const float4*>(&lm[qt & 1][g4 * 8 + hl * 4]);
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 0], c2, -mg.x));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 1], c2, -mg.y));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 2], c2, -mg.z));
+      acc += __builtin_amdgcn_exp2f(fmaf(c[g4 * 4 + 3], c2, -mg.w));
+    }
+    if (more) store_q((qt + 1) & 1, st, mv);
+    __syncthreads();
+  }
+  const float tot = xhalf_sum(acc);
+  if (hl == 0 && key < nk) {
+    const int ncap = a.keys.cap[0] + a.keys.cap[1];
+    const int p = region == 0 ? key : a.keys.cap[0] + key;
+    a.part[(int64_t)h * ncap + p] = tot;
+  }
+}
+
+hipError_t launch_score_mfma64(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s) {
+  if (a.geo.D != 64 || a.geo.esz != 2 || a.geo.DA != kD64A || a.geo.DB != kD64B) return hipErrorInvalidValue;
+  const int ntile0 = range_tiles(a.keys, 0);
+  const int ntile1 = range_tiles(a.keys, 1);
+  ScoreArgs b = a;
+  int n0 = ntile0, nt = ntile0 + ntile1;
+  if (ntile0 == 0) {   // keep region 0 non-empty for the tile sequence
+    b.keys.ka[0] = a.keys.ka[1];
+    b.keys.kb[0] = a.keys.kb[1];
+    b.keys.v[0] = a.keys.v[1];
+    b.keys.t[0] = a.keys.t[1];
+    b.keys.cap[0] = a.keys.cap[1];
+    b.keys.lo[0] = a.keys.lo[1];
+    b.keys.n[0] = a.keys.n[1];
+    b.keys.lo[1] = 0;
+    b.keys.n[1] = 0;
+    n0 = ntile1;
+    nt = ntile1;
+  }
+  if (nt == 0 || a.Nq == 0) return hipSuccess;
+  const int mblocks = (a.Nq + kBM - 1) / kBM;
+  const int total = mblocks * a.geo.H;
+  hipLaunchKernelGGL(score_rows_d64_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // columns: original region numbering (part is indexed by physical slot)
+  for (int r = 0; r < 2; ++r) {
+    if (a.keys.n[r] == 0) continue;
+    const int kblocks = (a.keys.n[r] + 127) / 128;
+    const int tot = kblocks * a.geo.H;
+    hipLaunchKernelGGL(score_cols_d64_kernel, dim3(tot), dim3(256), 0, s, a, qbf, r, kblocks, tot);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // v5f: v5 with a fixed reference per row instead of a running maximum.  Every
 // row keeps m = max of its scores in tile 0 (log2 units) for all tiles, so a
 // tile needs no maximum, no rescale test and no O rescale: P = exp2(c2 s - m).

@@ -763,8 +763,9 @@ __global__ __launch_bounds__(64) void score_rot_kernel(ScoreArgs a) {
 // 16-byte chunk of a (row, head) query, so that the loads and stores of consecutive threads are
 // consecutive 16-byte pieces of one row (a thread per row writing it element by element, 64 rows apart
 // across a wave, took 57 us at the C3 window).
+template <int D>
 __global__ __launch_bounds__(256) void score_rot_bf16_kernel(ScoreArgs a) {
-  constexpr int D = 128, E = Elem<uint16_t>::E, CH = D / E;
+  constexpr int E = Elem<uint16_t>::E, CH = D / E;
   const Geo& g = a.geo;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (int64_t)a.Nq * g.H * CH) return;
@@ -866,10 +867,16 @@ static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s) {
-  if (!(paths & kPathGeneral) && a.geo.esz == 2 && a.geo.D == 128) {
+  if (!(paths & kPathGeneral) && a.geo.esz == 2 && (a.geo.D == 128 || a.geo.D == 64)) {
     const int64_t rows = (int64_t)a.Nq * a.geo.H;
-    hipLaunchKernelGGL(score_rot_bf16_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, a);
-    if (hipError_t e = launch_score_mfma(a, (const uint16_t*)a.qh, s); e != hipSuccess) return e;
+    const int ch = a.geo.D / 8;              // 16-byte chunks per query row
+    if (a.geo.D == 128)
+      hipLaunchKernelGGL(score_rot_bf16_kernel<128>, dim3((unsigned)((rows * ch + 255) / 256)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(score_rot_bf16_kernel<64>, dim3((unsigned)((rows * ch + 255) / 256)), dim3(256), 0, s, a);
+    const hipError_t e = a.geo.D == 128 ? launch_score_mfma(a, (const uint16_t*)a.qh, s)
+                                        : launch_score_mfma64(a, (const uint16_t*)a.qh, s);
+    if (e != hipSuccess) return e;
     const int ncap = a.keys.cap[0] + a.keys.cap[1];
     hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((ncap + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();

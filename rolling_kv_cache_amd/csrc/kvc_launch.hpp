@@ -35,5 +35,7 @@ hipError_t relax_noalloc_scratch(void** ptr);
 // rows + columns passes over a query window already rotated into qbf
 // ([H][Nq][128] bf16); writes a.m (log2 normaliser per row) and a.part
 hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s);
+// the same for bf16 head_dim 64 (qbf: [H][Nq][64])
+hipError_t launch_score_mfma64(const ScoreArgs& a, const uint16_t* qbf, hipStream_t s);
 
 }  // namespace kvc

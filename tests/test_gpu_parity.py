@@ -110,10 +110,11 @@ def test_small_deep_forcing():
 
 
 @pytest.mark.parametrize("general", [False, True])
-def test_scores_match_oracle(general):
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_scores_match_oracle(general, head_dim):
     """Attention-mass scores on the matrix-core passes and on the general path: 206-token frames give a
-    ragged sink region, ragged key tiles and a ragged last query tile."""
-    w = Workload("score_small", 206, 3, 128, "bf16", 4, 8, 1, 5, (2, 2, 2))
+    ragged sink region, ragged key tiles and a ragged last query tile; head_dim 128 and 64."""
+    w = Workload("score_small", 206, 3, head_dim, "bf16", 4, 8, 1, 5, (2, 2, 2))
     gc = new_cache(w)
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
     for i in range(3):
