@@ -160,6 +160,7 @@ def main():
     extras = ceilings(dev, stream, ev)
     extras.update(sink_push_and_compact(dev, stream, flush, ev))
     extras.update(per_gpu_share(dev, stream, ev, w))
+    extras.update(head_dim_64(dev, stream, ev, w))
     extras.update(block_causal_clip(dev, stream, ev, WORKLOADS["c2"]))
     extras.update(raw_keys_ab(dev, stream, ev, flush, w))
     extras.update(memrope_chunk(dev, stream, ev, flush, WORKLOADS["c6"]))
@@ -589,6 +590,31 @@ def per_gpu_share(dev, stream, ev, w):
         res[f"attend_5head_share{tag}_ms"] = round(ms, 4)
         res[f"attend_5head_share{tag}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
     return res
+
+
+def head_dim_64(dev, stream, ev, w):
+    """The C3 step's attention and a 3-frame score window at head_dim 64 (40 heads, 4680 queries over the
+    28080-key cache, bf16): the head_dim-64 matrix-core kernels."""
+    import torch
+    import rolling_kv_cache_amd as kvc
+    from workloads import Workload, chunk_inputs
+    w64 = Workload("c3_d64", 230, w.heads, 64, "bf16", w.grid_h, w.grid_w, w.sink_frames, w.window_frames, (3,) * 7)
+    S, H, D = w64.frame_seqlen, w64.heads, w64.head_dim
+    c = kvc.KVCache(w64.sink_frames, w64.window_frames, S, H, D, w64.grid_w, torch.bfloat16)
+    q = None
+    for i in range(7):
+        q_, k, v = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in chunk_inputs(w64, i % 3))
+        c.append(k, v, 3 * i)
+        q = q_
+    Lk = c.info()["n_valid"]
+    flop = 4.0 * H * q.shape[0] * Lk * D
+    out = c.attend(q, 18)
+    sc = c.score(q, [18, 19, 20])
+    torch.cuda.synchronize()
+    ms = back_to_back_ms(stream, ev, lambda: c.attend(q, 18, out=out))
+    sms = back_to_back_ms(stream, ev, lambda: c.score(q, [18, 19, 20], out=sc), n=6)
+    return {"attend_d64_ms": round(ms, 4), "attend_d64_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "score_d64_ms": round(sms, 4)}
 
 
 def block_causal_clip(dev, stream, ev, w, block_frames=3):
