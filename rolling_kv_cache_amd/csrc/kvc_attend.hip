@@ -1,6 +1,6 @@
 // kvc_attend.hip -- chunk attention over the bounded cache on gfx950 matrix cores.
 //
-// out[i] = sum_j softmax_j(q_hat_i . k_j / sqrt(128)) v_j over every valid
+// out[i] = sum_j softmax_j(q_hat_i . k_j / sqrt(D)) v_j over every valid
 // cached entry, no mask (Causal-Forcing article, section 3; LingBot-World 2.0
 // article, "how the window rolls when full": queries read the whole window,
 // which already holds the new block).
@@ -42,7 +42,10 @@
 //    block-causal units are dealt longest first, round-robin over the XCDs;
 //  * launches with fewer workgroups than CUs split the keys into parts (same
 //    kernels, a part index, partial O with its reference and row sum) and
-//    merge them in a second pass.
+//    merge them in a second pass;
+//  * bf16 head_dim 64 has kernels of its own on the same pattern (8-chunk key
+//    rows, 4 query fragments, 2 O accumulators, running maximum), and so do
+//    its attention-mass scores.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -739,7 +742,8 @@ __global__ __launch_bounds__(256) void merge_split_kernel(AttendArgs a, int kpar
 }
 
 // ---------------------------------------------------------------------------
-// Attention-mass scores on the matrix cores (bf16, head_dim 128).  The query
+// Attention-mass scores on the matrix cores (bf16, head_dim 128; head_dim 64
+// further below).  The query
 // window arrives already rotated and rounded (qbf: [H][Nq][128] bf16).
 //
 // Rows pass: per (head, query) the softmax normaliser over every valid key,

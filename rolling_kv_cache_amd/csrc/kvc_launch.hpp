@@ -21,8 +21,8 @@ hipError_t launch_export(const ExportArgs& a, int32_t n_valid, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s);
 hipError_t launch_attend_mfma(const AttendArgs& a, uint32_t paths, hipStream_t s);
 hipError_t launch_attend_mfma64(const AttendArgs& a, hipStream_t s);
-// Scores: the matrix-core passes for bf16 with head_dim 128, else the general
-// per-row/per-column path (kPathGeneral in `paths` selects the latter).
+// Scores: the matrix-core passes for bf16 with head_dim 128 or 64, else the
+// general per-row/per-column path (kPathGeneral in `paths` selects the latter).
 hipError_t launch_score(const ScoreArgs& a, uint32_t paths, hipStream_t s);
 // MemRoPE: fold evicted frames into the EMA memories; copy the memory slots out
 hipError_t launch_mem_fold(const MemFoldArgs& a, hipStream_t s);
