@@ -372,6 +372,37 @@ def test_block_causal_head_dim_64(general, sink, block):
     check_attention(out, oc.attend_block_causal(q, 8, 0, block), f"head_dim 64 block-causal sink {sink} block {block}")
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_maximum_query_frames_and_top_time_positions(head_dim):
+    """The largest legal calls: 32 query frames (KVC_MAX_Q_FRAMES) attending to, and scoring, a 34-frame
+    cache whose times reach the top of the time range (16383 = KVC_MAX_POS), and a 32-frame
+    block-causal clip, all against the oracle (head_dim 128 and 64, bf16)."""
+    from rolling_kv_cache_amd import KVC_MAX_POS, KVC_MAX_Q_FRAMES
+    F = KVC_MAX_Q_FRAMES
+    w = Workload("maxq", 224, 2, head_dim, "bf16", 6, 10, 2, F, (4,) * 9)
+    gc = new_cache(w)
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    t0 = KVC_MAX_POS - 35
+    for i in range(9):                      # 36 frames, the newest at KVC_MAX_POS: the first two evicted
+        _, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), t0 + 4 * i)
+        oc.append(k, v, 4, t0 + 4 * i)
+    assert_state_equal(gc, oc, w, "maxq cache")
+    (q,) = chunk_inputs(w, 97, tensors=(0,), frames=F)
+    tq = KVC_MAX_POS - F + 1
+    out = gc.attend(dev(q, w), tq).float().cpu().numpy()
+    check_attention(out, oc.attend(q, F, tq), f"{F}-frame attend at the top time positions")
+    tf = list(range(tq, tq + F))
+    s_gpu = gc.score(dev(q, w), tf).cpu().numpy().astype(np.float64)
+    s_ref = oc.score(q, F, tf, f64=True)
+    assert abs(s_gpu.sum() - w.heads * F * w.frame_seqlen) < 1e-2
+    assert np.max(np.abs(s_gpu - s_ref)) < 1e-4 * max(1.0, s_ref.max())
+    wc = Workload("maxq_bc", 225, 2, head_dim, "bf16", 6, 10, 0, F, (4,) * 8)
+    gcc, occ, qc = _clip(wc, F, chunk=4)
+    out = gcc.attend_block_causal(dev(qc, wc), 0, 3).float().cpu().numpy()
+    check_attention(out, occ.attend_block_causal(qc, F, 0, 3), f"{F}-frame block-causal clip")
+
+
 def test_block_causal_partial_cache_and_time_offset():
     """The clip's queries see only what the cache holds (6 of 8 frames cached), rotated from t0 = 5."""
     w = Workload("bcp", 211, 2, 128, "bf16", 9, 23, 0, 8, (2,) * 3)
