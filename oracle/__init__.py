@@ -34,7 +34,7 @@ from .bf16 import round_to_bf16, bf16_ulp
 from .rope import band_split, inv_freq, cos_sin_table, token_positions, rotate_f32, rotate_f64
 from .cache import OracleCache, OracleError
 from .attention import attention_f32, attention_f64, attention_loops_f64
-from .score import attention_mass_scores
+from .score import attention_mass_scores, row_normalisers
 from .policies import (SlidingWindowRun, RollingSinkRun, InfinityRopeRun, DeepForcingRun,
                        RelaxForcingRun, DenoiseLoopRun, roll_index, make_run)
 from .relax import relax_frame_scores, top_frames
@@ -42,7 +42,7 @@ from .relax import relax_frame_scores, top_frames
 __all__ = [
     "round_to_bf16", "bf16_ulp", "band_split", "inv_freq", "cos_sin_table", "token_positions",
     "rotate_f32", "rotate_f64", "OracleCache", "OracleError", "attention_f32", "attention_f64",
-    "attention_loops_f64", "attention_mass_scores", "SlidingWindowRun", "RollingSinkRun",
+    "attention_loops_f64", "attention_mass_scores", "row_normalisers", "SlidingWindowRun", "RollingSinkRun",
     "InfinityRopeRun", "DeepForcingRun", "RelaxForcingRun", "DenoiseLoopRun", "roll_index", "make_run",
     "relax_frame_scores", "top_frames",
 ]

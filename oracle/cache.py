@@ -35,7 +35,7 @@ import numpy as np
 from .bf16 import round_to_bf16
 from .rope import band_split, rotate_f32, token_positions
 from .attention import attention_f32, attention_f64
-from .score import attention_mass_scores
+from .score import attention_mass_scores, row_normalisers
 from .relax import relax_frame_scores
 
 
@@ -350,6 +350,11 @@ class OracleCache:
         tok = np.arange(N, dtype=np.int64) % self.S
         qh = self._rotate(np.asarray(q_win, np.float32), t, tok)
         return attention_mass_scores(qh, self.attention_keys(), np.float64 if f64 else np.float32)
+
+    def row_normalisers(self, q, frames, t0):
+        """Each row's log2 softmax normaliser [H, N] for queries of frames t0 .. t0+frames-1 over the entries
+        attention reads (score.row_normalisers on the rotated, storage-rounded queries)."""
+        return row_normalisers(self.rotate_queries(q, frames, t0), self.attention_keys())
 
     def state(self):
         return {"K": self.K, "V": self.V, "t": self.t, "g": self.g, "n_sink": self.n_sink,

@@ -6,7 +6,7 @@ import pytest
 
 from oracle import (DeepForcingRun, InfinityRopeRun, OracleCache, RollingSinkRun, SlidingWindowRun,
                     attention_f32, attention_f64, attention_loops_f64, attention_mass_scores, bf16_ulp,
-                    roll_index, rotate_f64, round_to_bf16)
+                    roll_index, rotate_f64, round_to_bf16, row_normalisers)
 from workloads import WORKLOADS, Workload, chunk_inputs
 
 
@@ -220,6 +220,28 @@ def test_scores_sum_and_brute_force():
             for j in range(19):
                 ref[j] += e[j] / z
     assert np.max(np.abs(s - ref)) < 1e-12
+
+
+def test_row_normalisers_brute_force_and_scores():
+    """log2 softmax normalisers against explicit sums of powers of two; with them, every row's
+    probabilities sum to one and their column sums are the attention-mass scores."""
+    rng = np.random.default_rng(5)
+    qh = rng.standard_normal((7, 2, 64)) * 3.0
+    K = rng.standard_normal((19, 2, 64)) * 3.0
+    M = row_normalisers(qh, K)
+    assert M.shape == (2, 7)
+    c = math.log2(math.e) / 8.0
+    for h in range(2):
+        for i in range(7):
+            z = sum(2.0 ** (c * float(np.dot(qh[i, h], K[j, h]))) for j in range(19))
+            assert abs(M[h, i] - math.log2(z)) < 1e-10
+    s = attention_mass_scores(qh, K)
+    cols = np.zeros(19)
+    for h in range(2):
+        e = np.exp2(c * (qh[:, h, :] @ K[:, h, :].T) - M[h][:, None])
+        assert np.allclose(e.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        cols += e.sum(axis=0)
+    assert np.max(np.abs(cols - s)) < 1e-12
 
 
 def _df_small(n=16):
