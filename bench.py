@@ -157,6 +157,19 @@ def main():
     torch.cuda.synchronize()
     score_ms = back_to_back_ms(stream, ev, lambda: cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1],
                                                               out=sc_out), n=6)
+    # the same scores from the attention's row statistics (Deep Forcing scores the queries the previous
+    # chunk attended with, over the cache that attention saw): the attend keeps each row's normaliser
+    # (kvc_attend_stats) and the scoring runs only its columns pass (kvc_score_with_stats)
+    row_stats = torch.empty(H * N, dtype=torch.float32, device=dev)
+    att_stats_ms = back_to_back_ms(stream, ev, lambda: cache.attend(qwin, t_frame - 3, out=out, row_stats=row_stats),
+                                   n=6)
+    att_plain_ms = back_to_back_ms(stream, ev, lambda: cache.attend(qwin, t_frame - 3, out=out), n=6)
+    cache.attend(qwin, t_frame - 3, out=out, row_stats=row_stats)
+    sc_stats = cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1], row_stats=row_stats)
+    torch.cuda.synchronize()
+    score_stats_diff = float((sc_stats - sc_out).abs().max() / sc_out.abs().max())
+    score_stats_ms = back_to_back_ms(stream, ev, lambda: cache.score(qwin, [t_frame - 3, t_frame - 2, t_frame - 1],
+                                                                    out=sc_stats, row_stats=row_stats), n=6)
     extras = ceilings(dev, stream, ev)
     extras.update(sink_push_and_compact(dev, stream, flush, ev))
     extras.update(per_gpu_share(dev, stream, ev, w))
@@ -241,6 +254,10 @@ def main():
             "hbm_copy_torch_GBps_measured": round(copy_gbps, 1),
             "score_ms": round(score_ms, 4),
             "score_tflops": round(flop / (score_ms * 1e-3) / 1e12, 2),
+            "score_with_attention_row_stats_ms": round(score_stats_ms, 4),
+            "score_with_row_stats_max_diff_rel_to_max": float("%.3g" % score_stats_diff),
+            "attend_with_row_stats_ms": round(att_stats_ms, 4),
+            "attend_without_row_stats_ms": round(att_plain_ms, 4),
             **extras,
         },
     }

@@ -266,6 +266,33 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames);
 kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
                      void* scratch, size_t scratch_bytes);
 
+/* Attention that also keeps each query row's softmax normaliser, so that a
+ * later score of the same queries over the same entries needs only its
+ * columns pass.  Deep Forcing (rCM length-extrapolation article, strategy 4)
+ * scores the entries by the attention the previous chunk's queries paid to
+ * them, and nothing changes the cache between that attention and the scoring.
+ * As kvc_attend, plus row_stats: device float[heads][q_frames *
+ * frame_seqlen], caller-owned; row_stats[h][i] = log2 sum_j exp2(c * q_hat_i .
+ * k_j) over the valid entries, c = log2(e) / sqrt(head_dim).  EINVAL if
+ * row_stats is NULL; EUNSUPPORTED when the attention would read other entries
+ * than a score does (a KVC_CREATE_MEMORY cache after its first fold, or an
+ * attention limit below the number of entries).  The handle remembers the
+ * latest such call (buffer, frames, times) until the next call that changes
+ * the entries. */
+kvc_status kvc_attend_stats(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out,
+                            float* row_stats);
+
+/* kvc_score with the rows pass replaced by row_stats from kvc_attend_stats:
+ * the same scores (up to rounding: the attention sums its probabilities as
+ * rounded to the cache dtype) at about half the work.  row_stats must be the
+ * buffer of the handle's latest kvc_attend_stats, made with the same query
+ * frames (q_t[f] = its time + f) over the current entries: no append, retime,
+ * compact, sink push or attention-limit change since (KVC_ESTATE otherwise).
+ * The query window q_win must hold the same queries; that is the caller's to
+ * keep.  Other arguments and errors as kvc_score. */
+kvc_status kvc_score_with_stats(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t,
+                                const float* row_stats, float* scores, void* scratch, size_t scratch_bytes);
+
 /* Limit what kvc_attend reads to the newest max_keys valid entries in logical
  * order (LingBot-World 2.0 article, max_attention_size: queries read only the
  * last max_attention_size positions of the cache buffer, sink first), i.e. the

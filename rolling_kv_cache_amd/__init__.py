@@ -32,8 +32,9 @@ KVC_MAX_Q_FRAMES = 32
 
 # Every symbol include/kvc.h declares.
 EXPORTED = ("kvc_workspace_bytes", "kvc_create", "kvc_destroy", "kvc_set_stream", "kvc_set_paths", "kvc_append",
-            "kvc_attend",
-            "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_relax_scratch_bytes",
+            "kvc_attend", "kvc_attend_stats",
+            "kvc_attend_blockcausal", "kvc_retime", "kvc_score_scratch_bytes", "kvc_score", "kvc_score_with_stats",
+            "kvc_relax_scratch_bytes",
             "kvc_relax_scores", "kvc_relax_scores_noalloc", "kvc_set_attention_limit", "kvc_set_memory_rates", "kvc_export_memory",
             "kvc_compact", "kvc_sink_push", "kvc_group_workspace_bytes", "kvc_create_group", "kvc_retime_layers",
             "kvc_compact_layers", "kvc_sink_push_layers",
@@ -77,10 +78,12 @@ def _load():
         "kvc_set_paths": (ctypes.c_int, [vp, u32]),
         "kvc_append": (ctypes.c_int, [vp, vp, vp, i32, i32, u32]),
         "kvc_attend": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+        "kvc_attend_stats": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "kvc_attend_blockcausal": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
         "kvc_retime": (ctypes.c_int, [vp, i32, i32, i32, i32]),
         "kvc_score_scratch_bytes": (sz, [vp, i32]),
         "kvc_score": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, sz]),
+        "kvc_score_with_stats": (ctypes.c_int, [vp, vp, i32, p32, vp, vp, vp, sz]),
         "kvc_relax_scratch_bytes": (sz, [vp]),
         "kvc_relax_scores": (ctypes.c_int, [vp, i32, ctypes.c_float, vp, vp, sz]),
         "kvc_relax_scores_noalloc": (ctypes.c_int, [vp, i32, ctypes.c_float, vp]),
@@ -208,13 +211,26 @@ class KVCache:
         _check(lib.kvc_append(self._h, self._tensor(k, F, "k"), self._tensor(v, F, "v"), F, int(t_index),
                               KVC_APPEND_REPLACE_NEWEST if replace_newest else 0))
 
-    def attend(self, q, t_index=None, out=None):
+    def attend(self, q, t_index=None, out=None, row_stats=None):
+        """row_stats: a contiguous float32 CUDA tensor of at least heads x query rows elements; the call then
+        also writes each row's log2 softmax normaliser there (kvc_attend_stats), for score(..., row_stats)."""
         F = self._frames_of(q)
         if out is None:
             out = torch.empty_like(q)
-        _check(lib.kvc_attend(self._h, self._tensor(q, F, "q"), F, KVC_T_NEWEST if t_index is None else int(t_index),
-                              self._tensor(out, F, "out")))
+        t = KVC_T_NEWEST if t_index is None else int(t_index)
+        if row_stats is None:
+            _check(lib.kvc_attend(self._h, self._tensor(q, F, "q"), F, t, self._tensor(out, F, "out")))
+        else:
+            self._check_f32(row_stats, self.H * F * self.S, "row_stats")
+            _check(lib.kvc_attend_stats(self._h, self._tensor(q, F, "q"), F, t, self._tensor(out, F, "out"),
+                                        ctypes.c_void_p(row_stats.data_ptr())))
         return out
+
+    @staticmethod
+    def _check_f32(x, n, name):
+        if (not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32
+                or not x.is_contiguous() or x.numel() < n):
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of at least {n} elements")
 
     def attend_block_causal(self, q, t_index, block_frames: int, out=None):
         """Block-causal attention of a whole clip held by this cache from its first frame."""
@@ -229,7 +245,9 @@ class KVCache:
         hi = self.info()["n_valid"] if hi is None else hi
         _check(lib.kvc_retime(self._h, int(delta), 1 if clamp0 else 0, int(lo), int(hi)))
 
-    def score(self, q_win, q_t, out=None):
+    def score(self, q_win, q_t, out=None, row_stats=None):
+        """row_stats: the tensor of the latest attend(..., row_stats=...) of these queries at these times over
+        the unchanged cache; only the columns pass then runs (kvc_score_with_stats)."""
         F = self._frames_of(q_win)
         q_t = np.ascontiguousarray(np.asarray(q_t, dtype=np.int32))
         if q_t.shape != (F,):
@@ -246,9 +264,16 @@ class KVCache:
         elif (out.device.type != "cuda" or out.dtype != torch.float32 or not out.is_contiguous()
               or out.numel() < n):
             raise ValueError("out must be a contiguous float32 CUDA tensor of at least n_valid elements")
-        _check(lib.kvc_score(self._h, self._tensor(q_win, F, "q_win"), F,
-                             q_t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.c_void_p(out.data_ptr()),
-                             ctypes.c_void_p(self._score_scratch.data_ptr() + off), need))
+        qt = q_t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        scratch = ctypes.c_void_p(self._score_scratch.data_ptr() + off)
+        if row_stats is None:
+            _check(lib.kvc_score(self._h, self._tensor(q_win, F, "q_win"), F, qt, ctypes.c_void_p(out.data_ptr()),
+                                 scratch, need))
+        else:
+            self._check_f32(row_stats, self.H * F * self.S, "row_stats")
+            _check(lib.kvc_score_with_stats(self._h, self._tensor(q_win, F, "q_win"), F, qt,
+                                            ctypes.c_void_p(row_stats.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                            scratch, need))
         return out
 
     def relax_scores(self, tail_frames: int, weight: float = 0.5, out=None):

@@ -221,10 +221,15 @@ __device__ __forceinline__ void store_partial(const AttendArgs& a, const f32x16_
   }
 }
 
+// the normalised output row; with a.row_m, also the row's normaliser mref + log2(row sum) (mref: the
+// reference P was taken against, in log2 units)
 template <int D = 128>
-__device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o, float lsum, int qrow, int h, int hl) {
-  const float inv = 1.f / xhalf_sum(lsum);
+__device__ __forceinline__ void store_out(const AttendArgs& a, const f32x16_t* o, float lsum, int qrow, int h, int hl,
+                                          float mref) {
+  const float l = xhalf_sum(lsum);
+  const float inv = 1.f / l;
   if (qrow >= a.Lq) return;
+  if (a.row_m != nullptr && hl == 0) a.row_m[(int64_t)h * a.Lq + qrow] = mref + log2f(l);
   uint16_t* op = (uint16_t*)a.out + ((int64_t)qrow * a.geo.H + h) * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5_kernel(AttendArgs a, int mbl
   if (kparts > 1)
     store_partial(a, o, m, lsum, qrow, h, part, hl);
   else
-    store_out(a, o, lsum, qrow, h, hl);
+    store_out(a, o, lsum, qrow, h, hl, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(512, 1) void attend_d64_kernel(AttendArgs a, int mb
     step(t + 1, sb, sa);
   }
   if (t < nt) step(t, sa, sb);
-  store_out<64>(a, o, lsum, qrow, h, hl);
+  store_out<64>(a, o, lsum, qrow, h, hl, m);
 }
 
 // out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s) over the key parts,
@@ -732,6 +737,7 @@ __global__ __launch_bounds__(256) void merge_split_kernel(AttendArgs a, int kpar
     acc += w * x;
   }
   const float inv = 1.f / l;
+  if (a.row_m != nullptr && c == 0) a.row_m[(int64_t)h * a.Lq + row] = M + log2f(l);
   union {
     uint2 u;
     __bf16 b[4];
@@ -1077,13 +1083,15 @@ hipError_t launch_score_mfma(const ScoreArgs& a, const uint16_t* qbf, hipStream_
     nt = ntile1;
   }
   if (nt == 0 || a.Nq == 0) return hipSuccess;
-  const int total256 = mb256 * a.geo.H, per_xcd = (total256 + 7) / 8;
-  hipLaunchKernelGGL(score_rows_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, qbf, mb256, total256, per_xcd, n0,
-                     nt);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int total = mblocks * a.geo.H;
-  hipLaunchKernelGGL(score_rows_mfma_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt, mb256);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (!a.rows_given) {   // else a.m holds the attention's row normalisers
+    const int total256 = mb256 * a.geo.H, per_xcd = (total256 + 7) / 8;
+    hipLaunchKernelGGL(score_rows_v5f_kernel, dim3(8 * per_xcd), dim3(512), 0, s, b, qbf, mb256, total256, per_xcd,
+                       n0, nt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int total = mblocks * a.geo.H;
+    hipLaunchKernelGGL(score_rows_mfma_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt, mb256);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
   // columns: original region numbering (part is indexed by physical slot).  The 4-wave kernel stays: an
   // 8-wave version with 128-row query stages (201 VGPRs, one workgroup per CU) was 10 % slower.
   for (int r = 0; r < 2; ++r) {
@@ -1267,10 +1275,12 @@ hipError_t launch_score_mfma64(const ScoreArgs& a, const uint16_t* qbf, hipStrea
     nt = ntile1;
   }
   if (nt == 0 || a.Nq == 0) return hipSuccess;
-  const int mblocks = (a.Nq + kBM - 1) / kBM;
-  const int total = mblocks * a.geo.H;
-  hipLaunchKernelGGL(score_rows_d64_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (!a.rows_given) {   // else a.m holds the attention's row normalisers
+    const int mblocks = (a.Nq + kBM - 1) / kBM;
+    const int total = mblocks * a.geo.H;
+    hipLaunchKernelGGL(score_rows_d64_kernel, dim3(total), dim3(256), 0, s, b, qbf, mblocks, total, n0, nt);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
   // columns: original region numbering (part is indexed by physical slot)
   for (int r = 0; r < 2; ++r) {
     if (a.keys.n[r] == 0) continue;
@@ -1456,7 +1466,7 @@ __global__ __launch_bounds__(512, 1) void attend_v5f_kernel(AttendArgs a, int mb
   if (kparts > 1)
     store_partial(a, o, -negm, lsum, qrow, h, part, hl);   // the fixed reference, log2 units like v5's max
   else
-    store_out(a, o, lsum, qrow, h, hl);
+    store_out(a, o, lsum, qrow, h, hl, -negm);
 }
 
 // Launch shapes of the matrix-core attention.

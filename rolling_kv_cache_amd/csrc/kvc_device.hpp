@@ -156,6 +156,8 @@ struct AttendArgs {
   int32_t mem_t[2];                       // ... placed at times mem_t[0] (first S) and mem_t[1] (next S)
   float* split_o;                         // workspace (KVC_CREATE_SPLIT_ATTEND): per key part, head and row,
   float* split_ml;                        // the unnormalised O [128] and (reference, row sum); else null
+  float* row_m;                           // optional out [H][Lq]: each row's softmax normaliser in log2 units,
+                                          // M = log2 sum_j exp2(c2 s_j) with c2 = log2(e)/sqrt(D), s_j = q.k_j
 };
 
 constexpr int kSplitRows = 512 * 256;     // part x head x query rows the split-key buffers hold
@@ -168,6 +170,8 @@ struct ScoreArgs {
   float* part;                            // scratch: per-head column sums [H][cap0 + cap1]
   int32_t* flags;                         // scratch: one recompute flag per 256-query rows-pass block
   float* scores;                          // out: [n_valid] logical order
+  int32_t rows_given;                     // 1: m already holds each row's log2 normaliser (attention row
+                                          // statistics), so the rows passes are skipped
   int32_t Nq;
   int32_t qt[32];                         // time of each query frame
   KeyRegions keys;

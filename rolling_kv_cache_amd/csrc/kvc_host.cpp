@@ -148,6 +148,13 @@ struct kvc_cache {
   const void* group;        // layer group (kvc_create_group): shared tag, layer index, stride
   int32_t layer;
   int64_t layer_stride;
+  // row statistics (kvc_attend_stats -> kvc_score_with_stats): epoch counts the calls that changed the
+  // entries or what attention reads; the latest statistics are valid only while it stays where it was
+  uint64_t epoch;
+  bool stats_valid;
+  uint64_t stats_epoch;
+  const float* stats_buf;
+  int32_t stats_frames, stats_t0;
 };
 
 namespace {
@@ -594,11 +601,14 @@ kvc_status kvc_append(kvc_handle h, const void* k, const void* v, int32_t n_fram
   if (kvc_status s = device_result(h, e, "append")) return s;
   if (h->cflags & KVC_CREATE_MEMORY) h->mem_frames += evicted / h->S;
   h->st = std::move(nx);
+  ++h->epoch;
   return KVC_OK;
 }
 
+// row_m (optional): also write each query row's log2 softmax normaliser, [heads][q_frames * S]; *t0_out
+// receives the time query frame 0 was rotated at
 static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out,
-                              int32_t causal_block) {
+                              int32_t causal_block, float* row_m = nullptr, int32_t* t0_out = nullptr) {
   if (!q || !out) return fail(KVC_EINVAL, "q/out null");
   if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
   if (h->st.n_valid() == 0) return fail(KVC_ESTATE, "attend on an empty cache");
@@ -609,9 +619,18 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
     t0 = h->st.t_at(s0.region, s0.dst) - s0.src / h->S;
   }
   if (t0 < -KVC_MAX_POS || (int64_t)t0 + q_frames - 1 > KVC_MAX_POS) return fail(KVC_EINVAL, "q time out of range");
+  if (row_m != nullptr) {
+    // the statistics stand in for the rows pass of a score over the valid entries: attention must read
+    // exactly those (no memory tokens, no attention limit)
+    if ((h->cflags & KVC_CREATE_MEMORY) && h->mem_frames > 0)
+      return fail(KVC_EUNSUPPORTED, "row statistics with memory tokens");
+    if (h->max_keys > 0 && h->max_keys < h->st.n_valid())
+      return fail(KVC_EUNSUPPORTED, "row statistics with an attention limit");
+  }
   kvc::AttendArgs a{};
   a.q = q;
   a.out = out;
+  a.row_m = row_m;
   a.Lq = q_frames * h->S;
   a.t0 = t0;
   a.keys = key_regions(h);
@@ -683,12 +702,28 @@ static kvc_status attend_impl(kvc_handle h, const void* q, int32_t q_frames, int
   // raw keys on the matrix-core path: the time band placed once, then the plain kernels
   if (a.raw && h->L.placed_win != 0 && !(h->paths & KVC_PATH_GENERAL)) e = launch_placed_attend(h, a);
   if (e == hipSuccess) e = kvc::launch_attend(a, h->paths, h->stream);
+  if (t0_out != nullptr) *t0_out = t0;
   return device_result(h, e, "attend");
 }
 
 kvc_status kvc_attend(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out) {
   if (kvc_status s = check(h)) return s;
   return attend_impl(h, q, q_frames, q_t_index, out, 0);
+}
+
+kvc_status kvc_attend_stats(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index, void* out,
+                            float* row_stats) {
+  if (kvc_status s = check(h)) return s;
+  if (!row_stats) return fail(KVC_EINVAL, "row_stats null");
+  h->stats_valid = false;
+  int32_t t0 = 0;
+  if (kvc_status s = attend_impl(h, q, q_frames, q_t_index, out, 0, row_stats, &t0)) return s;
+  h->stats_valid = true;
+  h->stats_epoch = h->epoch;
+  h->stats_buf = row_stats;
+  h->stats_frames = q_frames;
+  h->stats_t0 = t0;
+  return KVC_OK;
 }
 
 kvc_status kvc_attend_blockcausal(kvc_handle h, const void* q, int32_t q_frames, int32_t q_t_index,
@@ -731,7 +766,10 @@ static kvc_status retime_layers(const kvc_handle* hs, int32_t nl, int32_t delta,
   a.tab = h->tab;
   hipError_t e = kvc::launch_retime(a, blocks, h->stream);
   if (kvc_status s = device_result_layers(hs, nl, e, "retime")) return s;
-  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
+  for (int32_t i = 0; i < nl; ++i) {
+    hs[i]->st = nx;
+    ++hs[i]->epoch;
+  }
   return KVC_OK;
 }
 
@@ -752,8 +790,9 @@ size_t kvc_score_scratch_bytes(kvc_handle h, int32_t q_frames) {
          placed_ka_bytes(h);
 }
 
-kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
-                     void* scratch, size_t scratch_bytes) {
+// row_stats (optional): the rows pass's normalisers, from the latest kvc_attend_stats of these queries
+static kvc_status score_impl(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
+                             void* scratch, size_t scratch_bytes, const float* row_stats) {
   if (kvc_status s = check(h)) return s;
   if (!q_win || !q_t || !scores || !scratch) return fail(KVC_EINVAL, "null argument");
   if (q_frames < 1 || q_frames > KVC_MAX_Q_FRAMES) return fail(KVC_EINVAL, "q_frames out of range");
@@ -764,6 +803,14 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   for (int32_t f = 0; f < q_frames; ++f) {
     if (q_t[f] < -KVC_MAX_POS || q_t[f] > KVC_MAX_POS) return fail(KVC_EINVAL, "q_t out of range");
     a.qt[f] = q_t[f];
+  }
+  if (row_stats != nullptr) {
+    bool same = h->stats_valid && h->stats_epoch == h->epoch && h->stats_buf == row_stats &&
+                h->stats_frames == q_frames;
+    for (int32_t f = 0; same && f < q_frames; ++f) same = q_t[f] == h->stats_t0 + f;
+    if (!same)
+      return fail(KVC_ESTATE, "row_stats are not the latest kvc_attend_stats of these query frames and times over "
+                              "the current cache");
   }
   const size_t Nq = (size_t)q_frames * h->S;
   char* p = (char*)scratch;
@@ -777,6 +824,10 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   p += align_up((size_t)h->H * (h->L.SP + h->L.WP) * 4);
   a.flags = (int32_t*)p;
   p += align_up((size_t)h->H * ((Nq + 255) / 256) * 4);
+  if (row_stats != nullptr) {   // the columns pass reads the attention's normalisers in place
+    a.m = const_cast<float*>(row_stats);
+    a.rows_given = 1;
+  }
   a.q = q_win;
   a.scores = scores;
   a.Nq = (int32_t)Nq;
@@ -794,6 +845,18 @@ kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const in
   if (h->cflags & KVC_CREATE_RAW_KEYS) e = launch_placed_ka(h, p, &a.keys);
   if (e == hipSuccess) e = kvc::launch_score(a, h->paths, h->stream);
   return device_result(h, e, "score");
+}
+
+kvc_status kvc_score(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t, float* scores,
+                     void* scratch, size_t scratch_bytes) {
+  return score_impl(h, q_win, q_frames, q_t, scores, scratch, scratch_bytes, nullptr);
+}
+
+kvc_status kvc_score_with_stats(kvc_handle h, const void* q_win, int32_t q_frames, const int32_t* q_t,
+                                const float* row_stats, float* scores, void* scratch, size_t scratch_bytes) {
+  if (kvc_status s = check(h)) return s;
+  if (!row_stats) return fail(KVC_EINVAL, "row_stats null");
+  return score_impl(h, q_win, q_frames, q_t, scores, scratch, scratch_bytes, row_stats);
 }
 
 static int32_t relax_slices(kvc_handle h) { return (h->S + kvc::kRelaxSlice - 1) / kvc::kRelaxSlice; }
@@ -873,6 +936,7 @@ kvc_status kvc_relax_scores_noalloc(kvc_handle h, int32_t tail_frames, float wei
 kvc_status kvc_set_attention_limit(kvc_handle h, int32_t max_keys) {
   if (kvc_status s = check(h)) return s;
   if (max_keys < 0) return fail(KVC_EINVAL, "max_keys must be >= 0");
+  if (h->max_keys != max_keys) ++h->epoch;
   h->max_keys = max_keys;
   return KVC_OK;
 }
@@ -948,7 +1012,10 @@ static kvc_status compact_layers(const kvc_handle* hs, int32_t nl, const int32_t
     }
   }
   if (kvc_status s = device_result_layers(hs, nl, e, "compact")) return s;
-  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
+  for (int32_t i = 0; i < nl; ++i) {
+    hs[i]->st = nx;
+    ++hs[i]->epoch;
+  }
   return KVC_OK;
 }
 
@@ -983,7 +1050,10 @@ static kvc_status sink_push_layers(const kvc_handle* hs, int32_t nl, int32_t ban
   hipError_t e = launch_segments(h, segs, bk, bv, D, head, D, head, t_index, b0, 0, 0, nl, h->layer_stride,
                                  h->layer_stride);
   if (kvc_status s = device_result_layers(hs, nl, e, "sink_push")) return s;
-  for (int32_t i = 0; i < nl; ++i) hs[i]->st = nx;
+  for (int32_t i = 0; i < nl; ++i) {
+    hs[i]->st = nx;
+    ++hs[i]->epoch;
+  }
   return KVC_OK;
 }
 

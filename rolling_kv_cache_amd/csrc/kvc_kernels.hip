@@ -718,6 +718,8 @@ __global__ __launch_bounds__(64) void attend_general_kernel(AttendArgs a) {
   const float inv = 1.f / l;
 #pragma unroll
   for (int d = 0; d < D; ++d) out[d] = Elem<T>::st(o[d] * inv);
+  // the row's normaliser in log2 units of q.k: m is a maximum of the scaled scores (natural units)
+  if (a.row_m != nullptr) a.row_m[(int64_t)h * a.Lq + i] = m * 1.4426950408889634f + log2f(l);
 }
 
 hipError_t launch_attend(const AttendArgs& a, uint32_t paths, hipStream_t s) {
@@ -832,7 +834,9 @@ __global__ __launch_bounds__(64) void score_cols_kernel(ScoreArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) s = fmaf(qv[d], kv[d], s);
     s *= a.scale;
-    acc += (double)(expf(s - a.m[(int64_t)h * a.Nq + i]) / a.l[(int64_t)h * a.Nq + i]);
+    // rows_given: a.m is the attention's log2 normaliser of the row (no separate row sum)
+    acc += a.rows_given ? (double)exp2f(fmaf(s, 1.4426950408889634f, -a.m[(int64_t)h * a.Nq + i]))
+                        : (double)(expf(s - a.m[(int64_t)h * a.Nq + i]) / a.l[(int64_t)h * a.Nq + i]);
   }
   a.part[(int64_t)h * ncap + p] = (float)acc;
 }
@@ -859,7 +863,7 @@ static void score_launch_all(const ScoreArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.Nq * a.geo.H;
   const unsigned b1 = (unsigned)((rows + 63) / 64);
   hipLaunchKernelGGL((score_rot_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
-  hipLaunchKernelGGL((score_rows_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
+  if (!a.rows_given) hipLaunchKernelGGL((score_rows_kernel<T, D>), dim3(b1), dim3(64), 0, s, a);
   const int64_t cols = (int64_t)(a.keys.cap[0] + a.keys.cap[1]) * a.geo.H;
   hipLaunchKernelGGL((score_cols_kernel<T, D>), dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, a);
   const int ncap = a.keys.cap[0] + a.keys.cap[1];

@@ -30,6 +30,7 @@ A schedule object needs ``chunk_frames`` (frames per chunk, in stream order),
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 
 def roll_block(n: int, K: int) -> int:
@@ -97,11 +98,19 @@ class InfinityRope:
 
 
 class DeepForcing:
-    def __init__(self, cache, sched, top_frames=4, recent_frames=2):
+    """Every attend keeps its rows' softmax normalisers (kvc_attend_stats); the scoring of the previous
+    chunk's queries, which sees the cache that attention saw, then runs only its columns pass
+    (kvc_score_with_stats).  use_row_stats=False scores with both passes (kvc_score)."""
+
+    def __init__(self, cache, sched, top_frames=4, recent_frames=2, use_row_stats=True):
         self.cache, self.sched = cache, sched
         self.C = top_frames * sched.frame_seqlen
         self.R = recent_frames * sched.frame_seqlen
         self.last = {}
+        self.row_stats = None
+        if use_row_stats:
+            rows = max(sched.chunk_frames) * sched.frame_seqlen
+            self.row_stats = torch.empty(cache.H * rows, dtype=torch.float32, device=cache.device)
 
     def keep_set(self, scores: np.ndarray, n: int, sink: int) -> np.ndarray:
         cand = np.arange(sink, n - self.R)
@@ -119,7 +128,8 @@ class DeepForcing:
         if info["n_valid"] + F * S > info["capacity"]:
             Fp = self.sched.chunk_frames[i - 1]
             tp = _start_frame(self.sched, i - 1)
-            scores = c.score(q_prev, [tp + f for f in range(Fp)]).cpu().numpy().astype(np.float64)
+            scores = c.score(q_prev, [tp + f for f in range(Fp)], row_stats=self.row_stats)
+            scores = scores.cpu().numpy().astype(np.float64)
             sink = info["sink_tokens"]
             keep = self.keep_set(scores, info["n_valid"], sink)
             self.last = {"scores": scores, "keep": keep}
@@ -128,7 +138,7 @@ class DeepForcing:
             self.last.update({"d_c": d_c, "d_s": d_s})
         t0 = _start_frame(self.sched, i)
         c.append(k, v, t0)
-        return c.attend(q, t0)
+        return c.attend(q, t0, row_stats=self.row_stats)
 
 
 class RelaxForcing:

@@ -129,6 +129,97 @@ def test_scores_match_oracle(general, head_dim):
     assert np.max(np.abs(s_gpu - s_ref)) < 1e-4 * max(1.0, s_ref.max())
 
 
+# log2 normalisers: the attention sums its probabilities as rounded to bf16 for the P.V product (relative
+# error at most 2^-8 each, so at most 2^-8 in the sum), i.e. log2(1 + 2^-8) = 5.6e-3, plus fp32 slack
+ROW_M_TOL = 6e-3
+
+
+@pytest.mark.parametrize("variant", ["", "general", "running_max", "split"])
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_score_with_attention_row_stats(variant, head_dim):
+    """kvc_attend_stats writes each row's log2 softmax normaliser (against the oracle's, on every attention
+    path: fixed reference + recompute, general, running maximum, split keys + merge; head_dim 128 and 64),
+    and kvc_score_with_stats, which runs only the columns pass on them, gives the scores of kvc_score
+    (against the oracle and the two-pass scores).  Ragged frames, a sink region and several key tiles."""
+    from rolling_kv_cache_amd import KVCError, KVC_ESTATE
+    w = Workload("score_stats", 206, 3, head_dim, "bf16", 4, 8, 1, 5, (2, 2, 2))
+    gc = new_cache(w, split=variant == "split")
+    oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
+    for i in range(3):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+        oc.append(k, v, 2, 2 * i)
+    qw, _, _ = chunk_inputs(w, 7, frames=2)
+    qd = dev(qw, w)
+    N = 2 * w.frame_seqlen
+    rs = torch.full((w.heads * N + 5,), float("nan"), dtype=torch.float32, device="cuda")
+    with paths(gc, general=variant == "general", running_max=variant == "running_max"):
+        out = gc.attend(qd, 3, row_stats=rs).float().cpu().numpy()
+        s_two = gc.score(qd, [3, 4]).cpu().numpy().astype(np.float64)
+        s_one = gc.score(qd, [3, 4], row_stats=rs).cpu().numpy().astype(np.float64)
+    check_attention(out, oc.attend(qw, 2, 3), f"attend with row statistics {variant}")
+    m_gpu = rs[:w.heads * N].view(w.heads, N).cpu().numpy().astype(np.float64)
+    m_ref = oc.row_normalisers(qw, 2, 3)
+    assert np.isnan(rs[w.heads * N:].cpu().numpy()).all(), "row statistics written past heads x rows"
+    assert np.max(np.abs(m_gpu - m_ref)) <= ROW_M_TOL, np.max(np.abs(m_gpu - m_ref))
+    s_ref = oc.score(qw, 2, [3, 4], f64=True)
+    tol = 1e-4 * max(1.0, s_ref.max())
+    assert abs(s_one.sum() - w.heads * N) < 1e-3 * w.heads * N
+    assert np.max(np.abs(s_one - s_ref)) < tol
+    assert np.max(np.abs(s_one - s_two)) < tol
+    # every term p_ij / l_i carries its row normaliser's relative error (at most 2^-8), so does each score
+    assert np.all(np.abs(s_one - s_two) <= (2.0 ** -8 + 1e-5) * s_two + 1e-7)
+    # stale statistics are refused: other times, another buffer, and any call that changes the entries
+    with pytest.raises(KVCError) as e:
+        gc.score(qd, [4, 5], row_stats=rs)
+    assert e.value.code == KVC_ESTATE
+    with pytest.raises(KVCError) as e:
+        gc.score(qd, [3, 4], row_stats=torch.empty_like(rs))
+    assert e.value.code == KVC_ESTATE
+    gc.retime(1)
+    with pytest.raises(KVCError) as e:
+        gc.score(qd, [3, 4], row_stats=rs)
+    assert e.value.code == KVC_ESTATE
+    gc.attend(qd, 3, row_stats=rs)
+    gc.score(qd, [3, 4], row_stats=rs)
+    _, k, v = chunk_inputs(w, 3, frames=2)
+    gc.append(dev(k, w), dev(v, w), 6)
+    with pytest.raises(KVCError) as e:
+        gc.score(qd, [3, 4], row_stats=rs)
+    assert e.value.code == KVC_ESTATE
+
+
+def test_attend_row_stats_refused_where_attention_reads_other_entries():
+    """With an attention limit below the entries, or memory tokens after the first fold, attention reads
+    other entries than a score: kvc_attend_stats returns EUNSUPPORTED and leaves no usable statistics."""
+    from rolling_kv_cache_amd import KVCError, KVC_EUNSUPPORTED, KVC_ESTATE
+    w = Workload("stats_refused", 208, 2, 128, "bf16", 4, 8, 1, 3, (2,) * 3)
+    gc = new_cache(w)
+    for i in range(3):
+        q, k, v = chunk_inputs(w, i)
+        gc.append(dev(k, w), dev(v, w), 2 * i)
+    qd = dev(q, w)
+    rs = torch.empty(w.heads * 2 * w.frame_seqlen, dtype=torch.float32, device="cuda")
+    gc.attend(qd, 4, row_stats=rs)
+    gc.set_attention_limit(3 * w.frame_seqlen)
+    with pytest.raises(KVCError) as e:
+        gc.attend(qd, 4, row_stats=rs)
+    assert e.value.code == KVC_EUNSUPPORTED
+    with pytest.raises(KVCError) as e:
+        gc.score(qd, [4, 5], row_stats=rs)
+    assert e.value.code == KVC_ESTATE
+    gc.set_attention_limit(0)
+    wm = MEM_SMALL
+    gm = new_cache(wm)
+    for i in range(wm.n_chunks):
+        q, k, v = chunk_inputs(wm, i)
+        gm.append(dev(k, wm), dev(v, wm), wm.chunk_start_frame(i))
+    rm = torch.empty(wm.heads * wm.chunk_frames[-1] * wm.frame_seqlen, dtype=torch.float32, device="cuda")
+    with pytest.raises(KVCError) as e:
+        gm.attend(dev(q, wm), wm.chunk_start_frame(wm.n_chunks - 1), row_stats=rm)
+    assert e.value.code == KVC_EUNSUPPORTED
+
+
 def test_replace_newest_denoise_steps():
     """Four denoising re-writes of the newest chunk, then the clean commit, before each new chunk."""
     w = Workload("replace", 207, 2, 128, "bf16", 4, 8, 1, 4, (2,) * 6)
@@ -180,12 +271,15 @@ def test_retime_workgroup_shapes(dtype, D, H):
         assert_state_equal(gc, oc, w, f"{w.name} after retime {d} {cl} [{lo}, {hi})")
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
 @pytest.mark.parametrize("variant", ["", "running_max"])
-def test_attend_score_jump(variant):
+def test_attend_score_jump(variant, head_dim):
     """Keys of the oldest frames are tiny and a later chunk's keys and queries are 4x N(0,1): the later
-    scores exceed every score of the first key tile by about 48 to 90 in exp2 units, so the kernels must
-    raise their running maximum mid-row and rescale O (without it P overflows to inf)."""
-    w = Workload("jump", 207, 2, 128, "bf16", 9, 23, 1, 6, (2,) * 4)
+    scores exceed every score of the first key tile by about 42 to 110 in exp2 units (at both head dims), so
+    the head_dim-128 fixed-reference kernel must flag its blocks, and the running-maximum kernels (the
+    recompute pass, or the only kernel at head_dim 64) raise their maximum mid-row and rescale O (without
+    it P overflows to inf)."""
+    w = Workload("jump", 207, 2, head_dim, "bf16", 9, 23, 1, 6, (2,) * 4)
     gc = new_cache(w)
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
     for i in range(3):
@@ -195,9 +289,15 @@ def test_attend_score_jump(variant):
         gc.append(dev(k, w), dev(v, w), 2 * i)
         oc.append(k, v, 2, 2 * i)
     q = (q * 4.0).astype(np.float32)
+    rs = torch.empty(w.heads * 2 * w.frame_seqlen, dtype=torch.float32, device="cuda")
     with paths(gc, running_max=variant == "running_max"):
         out = gc.attend(dev(q, w), 4).float().cpu().numpy()
+        out_rs = gc.attend(dev(q, w), 4, row_stats=rs).float().cpu().numpy()
     check_attention(out, oc.attend(q, 2, 4), f"score jump {variant or 'default'}")
+    assert np.array_equal(out, out_rs)
+    # the rows the recompute pass redid carry its (running-maximum) normalisers
+    m_gpu = rs.view(w.heads, -1).cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(m_gpu - oc.row_normalisers(q, 2, 4))) <= ROW_M_TOL
 
 
 def test_scores_score_jump():
@@ -794,11 +894,13 @@ def test_compact_across_the_ring_wrap():
     assert_state_equal(gc, oc, w, "compaction across the wrap")
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
 @pytest.mark.parametrize("variant", ["", "running_max"])
-def test_block_causal_score_jump(variant):
-    """Block-causal attention where the later blocks' scores exceed the first key tile's by 48-90 in exp2
-    units: the fixed-reference kernel must flag those blocks and the running-maximum pass redo them."""
-    w = Workload("bcjump", 223, 2, 128, "bf16", 9, 23, 0, 6, (2,) * 3)
+def test_block_causal_score_jump(variant, head_dim):
+    """Block-causal attention where the later blocks' scores exceed the first key tile's by tens of exp2
+    units: at head_dim 128 the fixed-reference kernel must flag those blocks and the running-maximum pass
+    redo them; at head_dim 64 the running-maximum kernel alone must rescale mid-row."""
+    w = Workload("bcjump", 223, 2, head_dim, "bf16", 9, 23, 0, 6, (2,) * 3)
     gc = new_cache(w)
     oc = OracleCache(w.sink_frames, w.window_frames, w.frame_seqlen, w.heads, w.head_dim, w.grid_w, w.dtype)
     for i in range(3):
