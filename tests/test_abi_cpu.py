@@ -68,6 +68,8 @@ def test_create_validates_before_any_device_work(kvc):
     # null handles
     assert lib.kvc_append(None, None, None, 1, 0, 0) == kvc.KVC_EINVAL
     assert lib.kvc_attend(None, None, 1, 0, None) == kvc.KVC_EINVAL
+    assert lib.kvc_attend_stats(None, None, 1, 0, None, None) == kvc.KVC_EINVAL
+    assert lib.kvc_score_with_stats(None, None, 1, None, None, None, None, 0) == kvc.KVC_EINVAL
     assert lib.kvc_destroy(None) == kvc.KVC_EINVAL
     assert lib.kvc_score_scratch_bytes(None, 1) == 0
     assert b"null" in lib.kvc_last_error()
